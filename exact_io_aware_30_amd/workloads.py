@@ -1,0 +1,140 @@
+"""Seeded synthetic attention inputs, and the FLOP / byte counts of a workload.
+
+This module holds no attention arithmetic: it draws inputs and counts work.
+Both the HIP path's tests and the CPU oracle's tests take their inputs from
+here, so the two sides see the same bits.
+
+Inputs: one CPU ``torch.Generator`` per workload, seeded, drawing float32
+N(0, 1) tensors in the order Q, K, V, dO, each [B, H, N, d]; Q is multiplied
+by ``q_scale`` (exact for a power of two) and every tensor is then rounded to
+the workload dtype (round-to-nearest-even).
+
+Counting conventions (the pages give "TFLOP/s" without a formula):
+  forward  = 4 B H N^2 d      (QK^T and PV, 2 N^2 d each)
+  backward = 10 B H N^2 d     (QK^T recompute, dO V^T, P^T dO, dS K, dS^T Q)
+  both halved exactly under the causal mask.
+Algorithmic bytes read or written once each, with T = B H N d elements of
+e bytes: forward 4Te + 4BHN, preprocess 2Te + 4BHN, dK/dV 6Te + 8BHN,
+dQ 5Te + 8BHN.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import torch
+
+DTYPES = {"fp16": torch.float16, "bf16": torch.bfloat16}
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: str          # "fp16" | "bf16"
+    B: int
+    H: int
+    N: int
+    d: int
+    causal: bool
+    q_scale: float = 1.0
+    seed: int = 0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def torch_dtype(self):
+        return DTYPES[self.dtype]
+
+    @property
+    def elems(self) -> int:
+        return self.B * self.H * self.N * self.d
+
+    def describe(self) -> str:
+        mask = "causal" if self.causal else "full"
+        return (f"{self.name}: {self.dtype} [B={self.B},H={self.H},N={self.N},d={self.d}] "
+                f"{mask} q_scale={self.q_scale:g} seed={self.seed}")
+
+
+# The five workloads the method is checked and measured on.
+WORKLOADS = {
+    "tiny": Workload("tiny", "fp16", 1, 2, 256, 64, False, 1.0, 1001),
+    "gpt2_medium": Workload("gpt2_medium", "bf16", 8, 16, 1024, 64, True, 1.0, 1002),
+    "ragged": Workload("ragged", "fp16", 3, 12, 2000, 32, False, 4.0, 1003),
+    "long": Workload("long", "bf16", 2, 16, 8192, 128, True, 1.0, 1004),
+    "batch1_64k": Workload("batch1_64k", "bf16", 1, 8, 65536, 64, True, 1.0, 1005),
+}
+
+
+def make_inputs(w: Workload, device="cpu"):
+    """(q, k, v, do) for workload ``w``: seeded N(0,1) fp32 draws, rounded."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed)
+    shape = (w.B, w.H, w.N, w.d)
+    out = []
+    for name in ("q", "k", "v", "do"):
+        x = torch.randn(shape, generator=g, dtype=torch.float32)
+        if name == "q" and w.q_scale != 1.0:
+            x = x * w.q_scale
+        out.append(x.to(w.torch_dtype).to(device))
+    return tuple(out)
+
+
+def make_tensor(shape, dtype: str, seed: int, device="cpu", scale: float = 1.0):
+    """One seeded N(0,1)*scale fp32 draw rounded to ``dtype``."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    x = torch.randn(tuple(shape), generator=g, dtype=torch.float32) * scale
+    return x.to(DTYPES[dtype]).to(device)
+
+
+def flops(w: Workload):
+    """(forward, backward, forward+backward) counted FLOPs."""
+    base = w.B * w.H * w.N * w.N * w.d
+    f, b = 4 * base, 10 * base
+    if w.causal:
+        f, b = f / 2, b / 2
+    return float(f), float(b), float(f + b)
+
+
+def kernel_flops(w: Workload):
+    """Counted FLOPs attributed to each kernel (causal halved).
+
+    The dK/dV kernel carries the QK^T recompute, dO V^T, P^T dO and dS^T Q
+    (8 B H N^2 d); the dQ kernel carries dS K (2 B H N^2 d).  The dQ
+    kernel's own recomputation of S and dP is work the deterministic layout
+    adds, not counted.
+    """
+    base = w.B * w.H * w.N * w.N * w.d * (0.5 if w.causal else 1.0)
+    return {"fwd": 4 * base, "bwd_dkdv": 8 * base, "bwd_dq": 2 * base, "bwd_preprocess": 0.0}
+
+
+def algorithmic_bytes(w: Workload):
+    """Bytes each kernel must move at least once (inputs read, outputs written)."""
+    e = torch.finfo(w.torch_dtype).bits // 8
+    T = w.elems
+    rows = w.B * w.H * w.N
+    return {
+        "fwd": 4 * T * e + 4 * rows,
+        "bwd_preprocess": 2 * T * e + 4 * rows,
+        "bwd_dkdv": 6 * T * e + 8 * rows,
+        "bwd_dq": 5 * T * e + 8 * rows,
+    }
+
+
+def footprint(B: int, H: int, N: int, d: int, elem_bytes: int, capacity_bytes: float | None = None):
+    """The footprint calculator: score matrix versus what the tiled kernel holds.
+
+    score   -- B*H*N*N elements of the score matrix, in bytes
+    linear  -- Q, K, V, O (B*H*N*d each) plus one fp32 L per row, in bytes
+    ratio   -- score / linear
+    n_max   -- largest N whose score matrix alone fits ``capacity_bytes``
+    """
+    score = B * H * N * N * elem_bytes
+    linear = 4 * B * H * N * d * elem_bytes + 4 * B * H * N
+    res = {"score": score, "linear": linear, "ratio": score / linear}
+    if capacity_bytes is not None:
+        res["n_max"] = int(math.isqrt(int(capacity_bytes // (B * H * elem_bytes))))
+    return res
