@@ -1,0 +1,200 @@
+"""Throughput of exact attention forward + backward on one MI355X.
+
+One step = the whole hot path on one batch of synthetic input already resident
+in device memory: fa_fwd, fa_bwd_preprocess, fa_bwd_dkdv, fa_bwd_dq (the last
+two are what fa_bwd enqueues).  The workload is bf16 [B=2, H=16, N=8192,
+d=128] with the causal mask.  FLOPs: forward 4 B H N^2 d, backward 10 B H N^2 d,
+both halved under the causal mask.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Prints one JSON line.  Besides the contract fields it carries
+  roofline      the dominant kernel (longest average launch, timed with HIP
+                events on the launch stream over the timed region) against
+                the dense bf16 MFMA peak, plus its HBM traffic per launch
+                from the committed rocprofv3 counter summary when that was
+                taken on the current kernel sources (else null);
+  cpu_baseline  the CPU fp64 oracle timed on one head of the same workload
+                (a bounded sample), in the same unit;
+  kernels       average duration, TFLOP/s and fraction of peak per kernel.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
+METRIC = "attention fwd+bwd TFLOP/s (bf16 causal N=8192 d=128) + % of MFMA peak"
+WORKLOAD = "long"
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_traffic_long.txt")
+KERNEL_SOURCES = ("fa_device.h", "fa_launch.h", "fa_fwd.hip", "fa_bwd.hip")
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "exact_io_aware_30_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_summary(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, if
+    it was measured on the current kernel sources."""
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+    except OSError:
+        return None
+    m = re.search(r"^source_hash:\s*(\S+)", text, re.M)
+    if not m or m.group(1) != source_hash():
+        return None
+    m = re.search(rf"^traffic_bytes\s+{re.escape(kernel)}:\s*([0-9.eE+]+)", text, re.M)
+    return float(m.group(1)) if m else None
+
+
+def cpu_baseline(w, heads: int = 4):
+    """The oracle, as it stands, on the first `heads` heads of batch 0."""
+    import numpy as np
+
+    import oracle
+    from exact_io_aware_30_amd import workloads
+
+    q, k, v, do = workloads.make_inputs(w)
+    one = [x[:1, :heads].to("cpu").double().numpy() for x in (q, k, v, do)]
+    cores = os.cpu_count() or 1
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=cores)
+    except Exception:
+        pass
+    t0 = time.perf_counter()
+    oracle.attention_backward(*one, w.scale, w.causal, row_block=1024)
+    dt = time.perf_counter() - t0
+    sample = workloads.Workload("sample", w.dtype, 1, heads, w.N, w.d, w.causal, w.q_scale, w.seed)
+    fb = workloads.flops(sample)[2]
+    return {"value": fb / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"heads (b=0, h=0..{heads - 1}) of {w.describe()}: fwd+bwd, {dt:.1f} s wall, numpy fp64",
+            "seconds": round(dt, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default=WORKLOAD)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from exact_io_aware_30_amd import binding, workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    q, k, v, do = (x.to(dev) for x in workloads.make_inputs(w))
+    o = torch.empty_like(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    delta = torch.empty_like(lse)
+    torch.cuda.synchronize()
+
+    phases = ("fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq")
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        binding.fa_fwd(q, k, v, o, lse, w.scale, w.causal)
+        if ev is not None:
+            ev[1].record()
+        binding.fa_bwd_preprocess(o, do, delta)
+        if ev is not None:
+            ev[2].record()
+        binding.fa_bwd_dkdv(q, k, v, do, lse, delta, dk, dv, w.scale, w.causal)
+        if ev is not None:
+            ev[3].record()
+        binding.fa_bwd_dq(q, k, v, do, lse, delta, dq, w.scale, w.causal)
+        if ev is not None:
+            ev[4].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {p: sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / args.steps for j, p in enumerate(phases)}
+    assert torch.isfinite(o).all() and torch.isfinite(dq).all(), "non-finite output"
+
+    f, b, fb = workloads.flops(w)
+    ms = wall * 1e3 / args.steps
+    kf = workloads.kernel_flops(w)
+    kb = workloads.algorithmic_bytes(w)
+    kernels = {}
+    for p in phases:
+        t = per[p] * 1e-3
+        ent = {"ms": round(per[p], 4)}
+        if kf[p] > 0:
+            ent["tflops"] = round(kf[p] / t / 1e12, 1)
+            ent["frac_mfma_peak"] = round(kf[p] / t / 1e12 / PEAK_BF16_TFLOPS, 4)
+        ent["gbs_algorithmic"] = round(kb[p] / t / 1e9, 1)
+        kernels[p] = ent
+    dom = max(("fwd", "bwd_dkdv", "bwd_dq"), key=lambda p: per[p])
+    achieved = kf[dom] / (per[dom] * 1e-3) / 1e12
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic_from_summary(dom), "algorithmic_bytes": kb[dom],
+                "algorithmic_flops": kf[dom]}
+    t_fwd = per["fwd"] * 1e-3
+    t_bwd = (per["bwd_preprocess"] + per["bwd_dkdv"] + per["bwd_dq"]) * 1e-3
+    value = fb / (ms * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "fp16",
+        "data": "synthetic: seeded i.i.d. N(0,1) Q, K, V, dO",
+        "config": {"workload": f"{w.name}: {w.dtype} [B={w.B},H={w.H},N={w.N},d={w.d}] "
+                               f"{'causal' if w.causal else 'full'}",
+                   "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal},
+        "frac_mfma_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "fwd_tflops": round(f / t_fwd / 1e12, 1),
+        "bwd_tflops": round(b / t_bwd / 1e12, 1),
+        "fwd_plus_bwd_tflops_from_events": round(fb / (t_fwd + t_bwd) / 1e12, 1),
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": None,
+        "kernel_source_hash": source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

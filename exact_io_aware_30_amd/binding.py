@@ -1,0 +1,155 @@
+"""ctypes binding of ``libfa_mi355x.so`` (C ABI in include/fa.h).
+
+Argument marshalling only: each function checks that the torch tensors are
+contiguous GPU tensors of the expected shape and dtype, then passes their
+``data_ptr()``, the sizes and torch's current HIP stream to the C function of
+the same name.  All arithmetic runs in the library's HIP kernels; there is no
+fallback path, and importing this module fails if the library is not built.
+
+``attention_forward`` / ``attention_backward`` allocate the outputs with
+torch and call the C functions.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from .build import LIB_PATH
+
+FA_F16, FA_BF16 = 0, 1
+FA_OK = 0
+_DT = {torch.float16: FA_F16, torch.bfloat16: FA_BF16}
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run `python -m exact_io_aware_30_amd.build` "
+        "(hipcc, gfx950) first -- there is no non-HIP fallback")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_p, _i, _f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+_SIG = {
+    "fa_fwd": [_p, _p, _p, _p, _p, _i, _i, _i, _i, _f, _i, _i, _p],
+    "fa_bwd_preprocess": [_p, _p, _p, _i, _i, _i, _i, _i, _p],
+    "fa_bwd": [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _f, _i, _i, _p],
+    "fa_bwd_dkdv": [_p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _f, _i, _i, _p],
+    "fa_bwd_dq": [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _f, _i, _i, _p],
+    "fa_status_string": [_i],
+    "fa_version": [],
+}
+for _name, _args in _SIG.items():
+    _fn = getattr(_lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = ctypes.c_char_p if _name == "fa_status_string" else _i
+
+EXPORTED = tuple(_SIG)
+
+
+class FAError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where}: {fa_status_string(code)} (status {code})")
+        self.code = code
+
+
+def fa_status_string(status: int) -> str:
+    return _lib.fa_status_string(int(status)).decode()
+
+
+def fa_version() -> int:
+    return _lib.fa_version()
+
+
+def _check(code: int, where: str):
+    if code != FA_OK:
+        raise FAError(code, where)
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _bhnd(t: torch.Tensor, name: str):
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be [B, H, N, d]")
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if t.dtype not in _DT:
+        raise ValueError(f"{name} must be float16 or bfloat16")
+    return t.shape
+
+
+def _same(ref: torch.Tensor, *pairs):
+    for t, name in pairs:
+        if t.shape != ref.shape or t.dtype != ref.dtype or not t.is_cuda or not t.is_contiguous() \
+                or t.device != ref.device:
+            raise ValueError(f"{name} must match q in shape, dtype and device and be contiguous")
+
+
+def _rows(ref: torch.Tensor, *pairs):
+    B, H, N, _ = ref.shape
+    for t, name in pairs:
+        if t.shape != (B, H, N) or t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 [B, H, N] GPU tensor")
+
+
+def fa_fwd(q, k, v, o, lse, scale: float, causal: bool) -> None:
+    B, H, N, d = _bhnd(q, "q")
+    _same(q, (k, "k"), (v, "v"), (o, "o"))
+    _rows(q, (lse, "lse"))
+    _check(_lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                       B, H, N, d, float(scale), int(bool(causal)), _DT[q.dtype], _stream(q)), "fa_fwd")
+
+
+def fa_bwd_preprocess(o, do, delta) -> None:
+    B, H, N, d = _bhnd(o, "o")
+    _same(o, (do, "do"))
+    _rows(o, (delta, "delta"))
+    _check(_lib.fa_bwd_preprocess(o.data_ptr(), do.data_ptr(), delta.data_ptr(), B, H, N, d,
+                                  _DT[o.dtype], _stream(o)), "fa_bwd_preprocess")
+
+
+def fa_bwd(q, k, v, do, lse, delta, dq, dk, dv, scale: float, causal: bool) -> None:
+    B, H, N, d = _bhnd(q, "q")
+    _same(q, (k, "k"), (v, "v"), (do, "do"), (dq, "dq"), (dk, "dk"), (dv, "dv"))
+    _rows(q, (lse, "lse"), (delta, "delta"))
+    _check(_lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                       delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
+                       float(scale), int(bool(causal)), _DT[q.dtype], _stream(q)), "fa_bwd")
+
+
+def fa_bwd_dkdv(q, k, v, do, lse, delta, dk, dv, scale: float, causal: bool) -> None:
+    B, H, N, d = _bhnd(q, "q")
+    _same(q, (k, "k"), (v, "v"), (do, "do"), (dk, "dk"), (dv, "dv"))
+    _rows(q, (lse, "lse"), (delta, "delta"))
+    _check(_lib.fa_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                            delta.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, float(scale),
+                            int(bool(causal)), _DT[q.dtype], _stream(q)), "fa_bwd_dkdv")
+
+
+def fa_bwd_dq(q, k, v, do, lse, delta, dq, scale: float, causal: bool) -> None:
+    B, H, N, d = _bhnd(q, "q")
+    _same(q, (k, "k"), (v, "v"), (do, "do"), (dq, "dq"))
+    _rows(q, (lse, "lse"), (delta, "delta"))
+    _check(_lib.fa_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                          delta.data_ptr(), dq.data_ptr(), B, H, N, d, float(scale), int(bool(causal)),
+                          _DT[q.dtype], _stream(q)), "fa_bwd_dq")
+
+
+def attention_forward(q, k, v, scale: float, causal: bool):
+    """(o, lse) with o like q and lse float32 [B, H, N]."""
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    fa_fwd(q, k, v, o, lse, scale, causal)
+    return o, lse
+
+
+def attention_backward(q, k, v, o, do, lse, scale: float, causal: bool):
+    """(dq, dk, dv, delta): the pre-pass then the two backward kernels."""
+    delta = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    fa_bwd_preprocess(o, do, delta)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    fa_bwd(q, k, v, do, lse, delta, dq, dk, dv, scale, causal)
+    return dq, dk, dv, delta

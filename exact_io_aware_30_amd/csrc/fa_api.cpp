@@ -1,0 +1,166 @@
+// C ABI of the attention library: argument checks, then kernel launches on
+// the caller's stream.  Every check runs before anything is enqueued, so a
+// rejected call has no effect.  See include/fa.h for the contract.
+#include "../../include/fa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "fa_launch.h"
+
+namespace {
+
+// One head slice is addressed with 32-bit byte offsets; the margin keeps the
+// offsets of the zero-filled rows past N (at most 255 rows) below 2^31 too.
+constexpr long long kMaxHeadBytes = (1LL << 31) - (1LL << 20);
+constexpr long long kMaxBlocks = 1LL << 24;           // workgroups of 256 lanes per launch
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+Range range_of(const void* p, long long bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return {lo, lo + static_cast<uintptr_t>(bytes)};
+}
+
+int check_common(int B, int H, int N, int d, fa_dtype dt) {
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_INVALID_ARG;
+  if (dt != FA_F16 && dt != FA_BF16) return FA_ERR_INVALID_ARG;
+  if (d != 32 && d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (static_cast<long long>(N) * d * 2 > kMaxHeadBytes) return FA_ERR_UNSUPPORTED;
+  const long long bh = static_cast<long long>(B) * H;
+  if (bh * ((N + 63) / 64) >= kMaxBlocks) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+int check_scale_mask(float scale, int causal) {
+  if (!(std::isfinite(scale) && scale > 0.f)) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+// outs must not overlap each other or any of ins.
+int check_alias(const Range* outs, int nout, const Range* ins, int nin) {
+  for (int i = 0; i < nout; ++i) {
+    for (int j = 0; j < nin; ++j)
+      if (overlap(outs[i], ins[j])) return FA_ERR_ALIAS;
+    for (int j = i + 1; j < nout; ++j)
+      if (overlap(outs[i], outs[j])) return FA_ERR_ALIAS;
+  }
+  return FA_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+int check_bwd(const void* q, const void* k, const void* v, const void* dO, const float* lse, const float* delta,
+              const void* dq, const void* dk, const void* dv, int B, int H, int N, int d, float scale, int causal,
+              fa_dtype dt, bool want_dq, bool want_dkdv) {
+  if (!q || !k || !v || !dO || !lse || !delta) return FA_ERR_INVALID_ARG;
+  if ((want_dq && !dq) || (want_dkdv && (!dk || !dv))) return FA_ERR_INVALID_ARG;
+  int rc = check_common(B, H, N, d, dt);
+  if (rc) return rc;
+  if ((rc = check_scale_mask(scale, causal))) return rc;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) || !aligned16(lse) || !aligned16(delta))
+    return FA_ERR_ALIGNMENT;
+  if ((want_dq && !aligned16(dq)) || (want_dkdv && (!aligned16(dk) || !aligned16(dv)))) return FA_ERR_ALIGNMENT;
+  const long long tb = static_cast<long long>(B) * H * N * d * 2, rb = static_cast<long long>(B) * H * N * 4;
+  const Range ins[6] = {range_of(q, tb), range_of(k, tb), range_of(v, tb), range_of(dO, tb), range_of(lse, rb),
+                        range_of(delta, rb)};
+  Range outs[3];
+  int n = 0;
+  if (want_dq) outs[n++] = range_of(dq, tb);
+  if (want_dkdv) {
+    outs[n++] = range_of(dk, tb);
+    outs[n++] = range_of(dv, tb);
+  }
+  return check_alias(outs, n, ins, 6);
+}
+
+fa::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                     const float* delta, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                     int causal, fa_dtype dt) {
+  return fa::BwdArgs{q, k, v, dO, lse, delta, dq, dk, dv, B, H, N, d, scale, causal == 1, dt == FA_BF16};
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+           float scale, int causal, fa_dtype dt, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  int rc = check_common(B, H, N, d, dt);
+  if (rc) return rc;
+  if ((rc = check_scale_mask(scale, causal))) return rc;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGNMENT;
+  const long long tb = static_cast<long long>(B) * H * N * d * 2, rb = static_cast<long long>(B) * H * N * 4;
+  const Range ins[3] = {range_of(q, tb), range_of(k, tb), range_of(v, tb)};
+  const Range outs[2] = {range_of(o, tb), range_of(lse, rb)};
+  if ((rc = check_alias(outs, 2, ins, 3))) return rc;
+  const fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, causal == 1, dt == FA_BF16};
+  return hip_status(fa::launch_fwd(a, static_cast<hipStream_t>(stream)));
+}
+
+int fa_bwd_preprocess(const void* o, const void* dO, float* delta, int B, int H, int N, int d, fa_dtype dt,
+                      void* stream) {
+  if (!o || !dO || !delta) return FA_ERR_INVALID_ARG;
+  int rc = check_common(B, H, N, d, dt);
+  if (rc) return rc;
+  if (!aligned16(o) || !aligned16(dO) || !aligned16(delta)) return FA_ERR_ALIGNMENT;
+  const long long tb = static_cast<long long>(B) * H * N * d * 2, rb = static_cast<long long>(B) * H * N * 4;
+  const Range ins[2] = {range_of(o, tb), range_of(dO, tb)};
+  const Range outs[1] = {range_of(delta, rb)};
+  if ((rc = check_alias(outs, 1, ins, 2))) return rc;
+  const fa::PreArgs a{o, dO, delta, B, H, N, d, dt == FA_BF16};
+  return hip_status(fa::launch_preprocess(a, static_cast<hipStream_t>(stream)));
+}
+
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse, const float* delta,
+                void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, fa_dtype dt, void* stream) {
+  const int rc = check_bwd(q, k, v, dO, lse, delta, nullptr, dk, dv, B, H, N, d, scale, causal, dt, false, true);
+  if (rc) return rc;
+  const fa::BwdArgs a = bwd_args(q, k, v, dO, lse, delta, nullptr, dk, dv, B, H, N, d, scale, causal, dt);
+  return hip_status(fa::launch_bwd_dkdv(a, static_cast<hipStream_t>(stream)));
+}
+
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse, const float* delta,
+              void* dq, int B, int H, int N, int d, float scale, int causal, fa_dtype dt, void* stream) {
+  const int rc = check_bwd(q, k, v, dO, lse, delta, dq, nullptr, nullptr, B, H, N, d, scale, causal, dt, true, false);
+  if (rc) return rc;
+  const fa::BwdArgs a = bwd_args(q, k, v, dO, lse, delta, dq, nullptr, nullptr, B, H, N, d, scale, causal, dt);
+  return hip_status(fa::launch_bwd_dq(a, static_cast<hipStream_t>(stream)));
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* dO, const float* lse, const float* delta,
+           void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, fa_dtype dt,
+           void* stream) {
+  int rc = check_bwd(q, k, v, dO, lse, delta, dq, dk, dv, B, H, N, d, scale, causal, dt, true, true);
+  if (rc) return rc;
+  const fa::BwdArgs a = bwd_args(q, k, v, dO, lse, delta, dq, dk, dv, B, H, N, d, scale, causal, dt);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((rc = hip_status(fa::launch_bwd_dkdv(a, st)))) return rc;
+  return hip_status(fa::launch_bwd_dq(a, st));
+}
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_INVALID_ARG: return "invalid argument (null pointer, size < 1, bad dtype, mask or scale)";
+    case FA_ERR_UNSUPPORTED: return "unsupported (head dim not 32/64/128, or sizes beyond the library limits)";
+    case FA_ERR_ALIGNMENT: return "a pointer is not 16-byte aligned";
+    case FA_ERR_HIP: return "the HIP runtime refused a kernel launch";
+    case FA_ERR_ALIAS: return "an output overlaps an input or another output";
+    default: return "unknown status";
+  }
+}
+
+int fa_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,348 @@
+// Backward kernels: the delta pre-pass, then dK/dV with key blocks in the
+// outer loop, then dQ with query blocks in the outer loop ("flash-attn-triton"
+// docs, "Where things live" and "Scope": backward kernels rebuild P from the
+// saved L instead of reading it back; "flash attention" note, "Key
+// Mechanisms": backward recomputation).  The gradient formulas are those of
+// the softmax-attention definition:
+//   P = 2^(S c - L log2 e)  (S = Q K^T, c = scale log2 e, masked entries 0)
+//   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),  dQ = scale dS K,
+//   dK = scale dS^T Q,  with D_i = sum_k dO_ik O_ik from the pre-pass.
+// No atomics: every output element is written by exactly one lane.
+#include "fa_device.h"
+#include "fa_launch.h"
+
+#include <algorithm>
+
+namespace fa {
+
+// ---------------------------------------------------------------------------
+// D_i = sum_k dO_ik O_ik.  D/8 lanes per row, 16 bytes per lane, fp32 sum.
+// ---------------------------------------------------------------------------
+template <class T, int D>
+__global__ __launch_bounds__(256) void preprocess_kernel(const void* __restrict__ op, const void* __restrict__ dop,
+                                                         float* __restrict__ delta, long rows) {
+  constexpr int CPR = D / 8, RPB = 256 / CPR;
+  const int tid = threadIdx.x;
+  const int ch = tid % CPR;
+  for (long row0 = (long)blockIdx.x * RPB; row0 < rows; row0 += (long)gridDim.x * RPB) {
+    const long row = row0 + tid / CPR;
+    float s = 0.f;
+    if (row < rows) {
+      const u32x4 a = *((const u32x4*)op + row * CPR + ch);
+      const u32x4 b = *((const u32x4*)dop + row * CPR + ch);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s = __builtin_fmaf(Elem<T>::lo(a[i]), Elem<T>::lo(b[i]), s);
+        s = __builtin_fmaf(Elem<T>::hi(a[i]), Elem<T>::hi(b[i]), s);
+      }
+    }
+#pragma unroll
+    for (int m = CPR / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m);
+    if (ch == 0 && row < rows) delta[row] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV.  Workgroup = 128 keys of one head (wave w owns keys k0 + 32w ..
+// k0 + 32w + 31, with its K and V rows resident as MFMA B operands), looping
+// over query tiles of 64 rows: Q and dO tiles plus their L and D staged
+// through swizzled LDS, double buffered.  Per tile and wave:
+//   S = Q K^T, dP = dO V^T          (lane = key, registers = queries)
+//   P = 2^(S c - L2), dS = P (dP - D)
+//   dV^T += dO^T P, dK^T += Q^T dS  (A operands by transposed LDS reads)
+// Under the causal mask query tiles start at the block's first key, and only
+// tiles that cross the diagonal are masked.
+// ---------------------------------------------------------------------------
+template <class T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void dkdv_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
+                                                   const void* __restrict__ vp, const void* __restrict__ dop,
+                                                   const float* __restrict__ lsep, const float* __restrict__ deltap,
+                                                   void* __restrict__ dkp, void* __restrict__ dvp, int N, int BH,
+                                                   float c, float scale) {
+  constexpr int BNK = 128, BMQ = 64, NT = 256, NKK = D / 16, NB = D / 32;
+  constexpr int TILE = BMQ * D * 2;
+  constexpr int BUF = 2 * TILE + 2 * BMQ * 4;
+  __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
+  lds_char* lds = (lds_char*)smem;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5;
+  const int x = blockIdx.x;
+  const int kb = x / BH, bh = x % BH;
+  const int k0 = kb * BNK;
+  const size_t head = (size_t)bh * N * D * 2;
+  const uint32_t bytes = (uint32_t)N * D * 2;
+  const auto rq = make_rsrc((const char*)qp + head, bytes);
+  const auto rk = make_rsrc((const char*)kp + head, bytes);
+  const auto rv = make_rsrc((const char*)vp + head, bytes);
+  const auto rdo = make_rsrc((const char*)dop + head, bytes);
+  const auto rdk = make_rsrc((char*)dkp + head, bytes);
+  const auto rdv = make_rsrc((char*)dvp + head, bytes);
+  const float* lse = lsep + (size_t)bh * N;
+  const float* dlt = deltap + (size_t)bh * N;
+
+  const int wk0 = k0 + 32 * w;
+  const int krow = wk0 + (lane & 31);
+  u32x4 kf[NKK], vf[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    kf[kk] = bload16(rk, (uint32_t)((krow * D + 16 * kk + 8 * h) * 2));
+    vf[kk] = bload16(rv, (uint32_t)((krow * D + 16 * kk + 8 * h) * 2));
+  }
+
+  const int i_start = CAUSAL ? k0 : 0;
+  const int nt = (N - i_start + BMQ - 1) / BMQ;
+
+  Stage<BMQ, D, NT> sq, sdo;
+  float ld = 0.f;  // this thread's L (tid < 64) or D (64 <= tid < 128) for the next tile
+  auto load_rowstats = [&](int i0) {
+    const int r = i0 + (tid & 63);
+    if (tid < 64) ld = r < N ? lse[r] * kLog2e : INFINITY;
+    else if (tid < 128) ld = r < N ? dlt[r] : 0.f;
+  };
+  sq.load(rq, i_start, tid);
+  sdo.load(rdo, i_start, tid);
+  load_rowstats(i_start);
+
+  f32x16 dka[NB], dva[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) dka[b] = dva[b] = (f32x16){};
+
+  for (int t = 0; t < nt; ++t) {
+    lds_char* qt = lds + (t & 1) * BUF;
+    lds_char* dot = qt + TILE;
+    float* st = (float*)(dot + TILE);  // [0, 64): L * log2 e, [64, 128): D
+    sq.store(qt, tid);
+    sdo.store(dot, tid);
+    if (tid < 128) st[tid] = ld;
+    __syncthreads();
+    const int i0 = i_start + t * BMQ;
+    if (t + 1 < nt) {
+      sq.load(rq, i0 + BMQ, tid);
+      sdo.load(rdo, i0 + BMQ, tid);
+      load_rowstats(i0 + BMQ);
+    }
+    if (CAUSAL && i0 + BMQ - 1 < wk0) continue;  // every query of the tile precedes every key of the wave
+
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      s[a] = (f32x16){};
+      dp[a] = (f32x16){};
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        s[a] = Elem<T>::mma(lds_rows_operand<D>(qt, 32 * a, kk, lane), kf[kk], s[a]);
+        dp[a] = Elem<T>::mma(lds_rows_operand<D>(dot, 32 * a, kk, lane), vf[kk], dp[a]);
+      }
+    }
+    const bool edge = CAUSAL && (i0 < wk0 + 31);
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int qi = 32 * a + 8 * g + 4 * h;
+        const f32x4 l2 = *(const f32x4*)(st + qi);
+        const f32x4 dd = *(const f32x4*)(st + 64 + qi);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          float p = exp2_fast(__builtin_fmaf(s[a][r], c, -l2[e]));
+          if (edge && krow > i0 + qi + e) p = 0.f;
+          s[a][r] = p;
+          dp[a][r] = p * (dp[a][r] - dd[e]);
+        }
+      }
+    u32x4 pf[4], dsf[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      pf[j] = pack8<T>(s[j >> 1], j & 1);
+      dsf[j] = pack8<T>(dp[j >> 1], j & 1);
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        dva[b] = Elem<T>::mma(lds_cols_operand<D>(dot, j, 32 * b, lane), pf[j], dva[b]);
+        dka[b] = Elem<T>::mma(lds_cols_operand<D>(qt, j, 32 * b, lane), dsf[j], dka[b]);
+      }
+  }
+  store_rows<T, D>(rdk, krow, dka, scale, lane);
+  store_rows<T, D>(rdv, krow, dva, 1.0f, lane);
+}
+
+// ---------------------------------------------------------------------------
+// dQ.  Workgroup = 128 queries of one head (wave w owns 32, with its Q and dO
+// rows resident as MFMA B operands and its L and D in registers), looping
+// over key tiles of 64 rows (K and V staged through swizzled LDS):
+//   S^T = K Q^T, dP^T = V dO^T   (lane = query, registers = keys)
+//   P = 2^(S c - L2), dS = P (dP - D)
+//   dQ^T += K^T dS^T             (A operand by transposed LDS reads)
+// ---------------------------------------------------------------------------
+template <class T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void dq_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
+                                                 const void* __restrict__ vp, const void* __restrict__ dop,
+                                                 const float* __restrict__ lsep, const float* __restrict__ deltap,
+                                                 void* __restrict__ dqp, int N, int BH, int nqb, float c,
+                                                 float scale) {
+  constexpr int BM = 128, BN = 64, NT = 256, NKK = D / 16, NB = D / 32;
+  constexpr int TILE = BN * D * 2;
+  __shared__ __attribute__((aligned(16))) char smem[4 * TILE];
+  lds_char* lds = (lds_char*)smem;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5;
+  const int x = blockIdx.x;
+  const int qb = CAUSAL ? (nqb - 1 - x / BH) : (x / BH);
+  const int bh = x % BH;
+  const int q0 = qb * BM;
+  const size_t head = (size_t)bh * N * D * 2;
+  const uint32_t bytes = (uint32_t)N * D * 2;
+  const auto rq = make_rsrc((const char*)qp + head, bytes);
+  const auto rk = make_rsrc((const char*)kp + head, bytes);
+  const auto rv = make_rsrc((const char*)vp + head, bytes);
+  const auto rdo = make_rsrc((const char*)dop + head, bytes);
+  const auto rdq = make_rsrc((char*)dqp + head, bytes);
+
+  const int wq0 = q0 + 32 * w;
+  const int qrow = wq0 + (lane & 31);
+  u32x4 qf[NKK], dof[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    qf[kk] = bload16(rq, (uint32_t)((qrow * D + 16 * kk + 8 * h) * 2));
+    dof[kk] = bload16(rdo, (uint32_t)((qrow * D + 16 * kk + 8 * h) * 2));
+  }
+  const float l2 = qrow < N ? lsep[(size_t)bh * N + qrow] * kLog2e : INFINITY;
+  const float dd = qrow < N ? deltap[(size_t)bh * N + qrow] : 0.f;
+
+  const int kend = CAUSAL ? min(N, q0 + BM) : N;
+  const int nt = (kend + BN - 1) / BN;
+  Stage<BN, D, NT> sk, sv;
+  sk.load(rk, 0, tid);
+  sv.load(rv, 0, tid);
+
+  f32x16 dqa[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) dqa[b] = (f32x16){};
+
+  for (int t = 0; t < nt; ++t) {
+    lds_char* kt = lds + (t & 1) * 2 * TILE;
+    lds_char* vt = kt + TILE;
+    sk.store(kt, tid);
+    sv.store(vt, tid);
+    __syncthreads();
+    if (t + 1 < nt) {
+      sk.load(rk, (t + 1) * BN, tid);
+      sv.load(rv, (t + 1) * BN, tid);
+    }
+    const int j0 = t * BN;
+    if (CAUSAL && j0 > wq0 + 31) continue;  // every key of the tile follows every query of the wave
+
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      s[a] = (f32x16){};
+      dp[a] = (f32x16){};
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        s[a] = Elem<T>::mma(lds_rows_operand<D>(kt, 32 * a, kk, lane), qf[kk], s[a]);
+        dp[a] = Elem<T>::mma(lds_rows_operand<D>(vt, 32 * a, kk, lane), dof[kk], dp[a]);
+      }
+    }
+    const bool edge = (j0 + BN > N) || (CAUSAL && j0 + BN - 1 > wq0);
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = exp2_fast(__builtin_fmaf(s[a][r], c, -l2));
+        if (edge) {
+          const int key = j0 + 32 * a + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (key >= N || (CAUSAL && key > qrow)) p = 0.f;
+        }
+        dp[a][r] = p * (dp[a][r] - dd);
+      }
+    u32x4 dsf[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dsf[j] = pack8<T>(dp[j >> 1], j & 1);
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dqa[b] = Elem<T>::mma(lds_cols_operand<D>(kt, j, 32 * b, lane), dsf[j], dqa[b]);
+  }
+  store_rows<T, D>(rdq, qrow, dqa, scale, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+template <class T, int D>
+static hipError_t launch_pre_t(const PreArgs& a, hipStream_t st) {
+  const long rows = (long)a.B * a.H * a.N;
+  const int rpb = 256 / (D / 8);
+  const long grid = std::min<long>((rows + rpb - 1) / rpb, 1L << 20);
+  hipLaunchKernelGGL((preprocess_kernel<T, D>), dim3((unsigned)grid), dim3(256), 0, st, a.o, a.dO, a.delta, rows);
+  return hipGetLastError();
+}
+
+template <class T>
+static hipError_t launch_pre_e(const PreArgs& a, hipStream_t st) {
+  switch (a.d) {
+    case 32: return launch_pre_t<T, 32>(a, st);
+    case 64: return launch_pre_t<T, 64>(a, st);
+    default: return launch_pre_t<T, 128>(a, st);
+  }
+}
+
+hipError_t launch_preprocess(const PreArgs& a, hipStream_t st) {
+  return a.bf16 ? launch_pre_e<bf16_tag>(a, st) : launch_pre_e<f16_tag>(a, st);
+}
+
+template <class T, int D, bool CAUSAL>
+static hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t st) {
+  const int BH = a.B * a.H;
+  const int nkb = (a.N + 127) / 128;
+  hipLaunchKernelGGL((dkdv_kernel<T, D, CAUSAL>), dim3(nkb * BH), dim3(256), 0, st, a.q, a.k, a.v, a.dO, a.lse,
+                     a.delta, a.dk, a.dv, a.N, BH, a.scale * kLog2e, a.scale);
+  return hipGetLastError();
+}
+
+template <class T, int D, bool CAUSAL>
+static hipError_t launch_dq_t(const BwdArgs& a, hipStream_t st) {
+  const int BH = a.B * a.H;
+  const int nqb = (a.N + 127) / 128;
+  hipLaunchKernelGGL((dq_kernel<T, D, CAUSAL>), dim3(nqb * BH), dim3(256), 0, st, a.q, a.k, a.v, a.dO, a.lse,
+                     a.delta, a.dq, a.N, BH, nqb, a.scale * kLog2e, a.scale);
+  return hipGetLastError();
+}
+
+template <class T, int D>
+static hipError_t launch_dkdv_d(const BwdArgs& a, hipStream_t st) {
+  return a.causal ? launch_dkdv_t<T, D, true>(a, st) : launch_dkdv_t<T, D, false>(a, st);
+}
+template <class T, int D>
+static hipError_t launch_dq_d(const BwdArgs& a, hipStream_t st) {
+  return a.causal ? launch_dq_t<T, D, true>(a, st) : launch_dq_t<T, D, false>(a, st);
+}
+
+template <class T>
+static hipError_t launch_dkdv_e(const BwdArgs& a, hipStream_t st) {
+  switch (a.d) {
+    case 32: return launch_dkdv_d<T, 32>(a, st);
+    case 64: return launch_dkdv_d<T, 64>(a, st);
+    default: return launch_dkdv_d<T, 128>(a, st);
+  }
+}
+template <class T>
+static hipError_t launch_dq_e(const BwdArgs& a, hipStream_t st) {
+  switch (a.d) {
+    case 32: return launch_dq_d<T, 32>(a, st);
+    case 64: return launch_dq_d<T, 64>(a, st);
+    default: return launch_dq_d<T, 128>(a, st);
+  }
+}
+
+hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t st) {
+  return a.bf16 ? launch_dkdv_e<bf16_tag>(a, st) : launch_dkdv_e<f16_tag>(a, st);
+}
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t st) {
+  return a.bf16 ? launch_dq_e<bf16_tag>(a, st) : launch_dq_e<f16_tag>(a, st);
+}
+
+}  // namespace fa

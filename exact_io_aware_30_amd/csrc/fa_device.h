@@ -1,0 +1,210 @@
+// Device building blocks shared by the gfx950 attention kernels.
+//
+// MFMA: v_mfma_f32_32x32x16_{bf16,f16}.  Lane layouts (checked on the device):
+//   A (32 x 16): lane l holds A[l % 32][8 * (l / 32) + e], e = 0..7
+//   B (16 x 32): lane l holds B[8 * (l / 32) + e][l % 32]
+//   C (32 x 32): register r of lane l holds C[8 * (r / 4) + 4 * (l / 32) + r % 4][l % 32]
+// The reduction index k of one MFMA may be any permutation shared by A and
+// B.  The kernels use the permutation that makes a C tile, converted to
+// 16-bit, directly usable as an A or B operand: within a 16-wide chunk, lane
+// half h and element e stand for position 8 * (e / 4) + 4 * h + e % 4.
+//
+// LDS tiles are [rows][D] 16-bit, rows of D*2 bytes with no padding; the
+// 16-byte chunk c of row r lives at chunk (c ^ swz(r)).  swz() is chosen so
+// that both ways the kernels read a tile hit 64 distinct banks per 256 bytes:
+//   * ds_read_b128 of 16 consecutive rows at one chunk (operand rows), and
+//   * ds_read_b64_tr_b16 of 4 consecutive rows x 64 bytes per 32 lanes
+//     (operands whose reduction index runs along the rows).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) char lds_char;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit format, gfx9
+
+struct bf16_tag {};
+struct f16_tag {};
+
+template <class T>
+struct Elem;
+
+template <>
+struct Elem<bf16_tag> {
+  static __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  // Two floats to two round-to-nearest-even bf16 in one dword (x low).
+  static __device__ __forceinline__ unsigned pack2(float x, float y) {
+    return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){x, y}, bf16x2));
+  }
+  static __device__ __forceinline__ float lo(unsigned u) { return __uint_as_float(u << 16); }
+  static __device__ __forceinline__ float hi(unsigned u) { return __uint_as_float(u & 0xffff0000u); }
+};
+
+template <>
+struct Elem<f16_tag> {
+  static __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ unsigned pack2(float x, float y) {
+    return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){x, y}, f16x2));
+  }
+  static __device__ __forceinline__ float lo(unsigned u) {
+    return (float)__builtin_bit_cast(f16x2, u)[0];
+  }
+  static __device__ __forceinline__ float hi(unsigned u) {
+    return (float)__builtin_bit_cast(f16x2, u)[1];
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Buffer resources: a head slice [N, D] addressed with byte offsets.  Loads
+// past num_records return zero and stores past it are dropped, which is how
+// the ragged tail (rows >= N) is zero-filled on load and never written.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kRsrcWord3);
+}
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ void bstore8(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Swizzled LDS tile of ROWS x D 16-bit elements.
+// ---------------------------------------------------------------------------
+template <int D>
+struct Swz {
+  static constexpr int CPR = D / 8;  // 16-byte chunks per row
+  static_assert(CPR == 4 || CPR == 8 || CPR == 16, "D must be 32, 64 or 128");
+  static __device__ __forceinline__ int f(int r) {
+    if constexpr (CPR == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else if constexpr (CPR == 8) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+    else return (r >> 2) & 3;
+  }
+  // Byte offset of 16-byte chunk c of row r.
+  static __device__ __forceinline__ int chunk(int r, int c) { return (r * CPR + (c ^ f(r))) << 4; }
+  // Byte offset of element column col (multiple of 4) of row r, for 8-byte reads.
+  static __device__ __forceinline__ int elem4(int r, int col) {
+    return chunk(r, col >> 3) + ((col & 4) << 1);
+  }
+};
+
+// Operand with rows along the MFMA M/N index: lane l reads row (row0 + l % 32),
+// 8 elements starting at column 16 * kk + 8 * (l / 32).
+template <int D>
+__device__ __forceinline__ u32x4 lds_rows_operand(const lds_char* tile, int row0, int kk, int lane) {
+  const int r = row0 + (lane & 31);
+  const int c = 2 * kk + (lane >> 5);
+  return *(const u32x4*)(tile + Swz<D>::chunk(r, c));
+}
+
+__device__ __forceinline__ u32x2 ds_read_tr16(const lds_char* p) {
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Operand whose reduction index runs along the tile rows: lane l gets column
+// (col0 + l % 32) and the 8 rows of 16-row chunk kc in the permuted order
+// (rows 16kc + 4h + 0..3, then 16kc + 8 + 4h + 0..3, h = l / 32).
+// ds_read_b64_tr_b16 works on 16-lane groups: lane t of a group names row
+// (base + t / 4) and 4 columns starting at 4 * (t % 4); after the transpose
+// lane i of the group holds column i of those 4 rows.
+template <int D>
+__device__ __forceinline__ u32x4 lds_cols_operand(const lds_char* tile, int kc, int col0, int lane) {
+  const int g = lane >> 4, t = lane & 15, h = lane >> 5;
+  const int col = col0 + 16 * (g & 1) + 4 * (t & 3);
+  const int r0 = 16 * kc + 4 * h + (t >> 2);
+  u32x2 a = ds_read_tr16(tile + Swz<D>::elem4(r0, col));
+  u32x2 b = ds_read_tr16(tile + Swz<D>::elem4(r0 + 8, col));
+  return (u32x4){a.x, a.y, b.x, b.y};
+}
+
+// ---------------------------------------------------------------------------
+// Global -> register -> LDS staging of a ROWS x D tile by NT threads.
+// ---------------------------------------------------------------------------
+template <int ROWS, int D, int NT>
+struct Stage {
+  static constexpr int CPR = D / 8;
+  static constexpr int PER = ROWS * CPR / NT;
+  static_assert(ROWS * CPR % NT == 0, "tile must split evenly over the threads");
+  u32x4 r[PER];
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t src, int row0, int tid) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = tid + i * NT;
+      const int row = c / CPR, col = c % CPR;
+      r[i] = bload16(src, (uint32_t)(((row0 + row) * D + col * 8) * 2));
+    }
+  }
+  __device__ __forceinline__ void store(lds_char* tile, int tid) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = tid + i * NT;
+      const int row = c / CPR, col = c % CPR;
+      *(u32x4*)(tile + Swz<D>::chunk(row, col)) = r[i];
+    }
+  }
+};
+
+// Value of x in lane l ^ 32, combined with x: returns {x_own, x_partner} as
+// the two halves of v_permlane32_swap (order depends on the lane half).
+__device__ __forceinline__ float max_with_partner(float x) {
+  auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float sum_with_partner(float x) {
+  auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+
+// Pack the 8 C-registers c[8*j .. 8*j+7] into an A/B operand (see header).
+template <class T>
+__device__ __forceinline__ u32x4 pack8(const f32x16& c, int j) {
+  return (u32x4){Elem<T>::pack2(c[8 * j + 0], c[8 * j + 1]), Elem<T>::pack2(c[8 * j + 2], c[8 * j + 3]),
+                 Elem<T>::pack2(c[8 * j + 4], c[8 * j + 5]), Elem<T>::pack2(c[8 * j + 6], c[8 * j + 7])};
+}
+
+// Store a wave's [32 rows x D] fp32 result held with lane = row (C tiles of
+// the transposed product: register r of tile b is column 32b + 8(r/4) +
+// 4h + r%4) as 16-bit rows of a [N, D] slice, scaled by `mul`.
+template <class T, int D>
+__device__ __forceinline__ void store_rows(__amdgpu_buffer_rsrc_t dst, int row, const f32x16* acc,
+                                           float mul, int lane) {
+  const int h = lane >> 5;
+#pragma unroll
+  for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int col = 32 * b + 8 * g + 4 * h;
+      u32x2 v = {Elem<T>::pack2(acc[b][4 * g + 0] * mul, acc[b][4 * g + 1] * mul),
+                 Elem<T>::pack2(acc[b][4 * g + 2] * mul, acc[b][4 * g + 3] * mul)};
+      bstore8(dst, (uint32_t)((row * D + col) * 2), v);
+    }
+}
+
+}  // namespace fa

@@ -1,0 +1,159 @@
+// Forward kernel: exact attention with the online softmax, one workgroup per
+// BM query rows of one head ("flash-attn-triton" docs, "Tiling softmax is
+// exact algebra" and Fig. 3 "the update, per tile"; FlashAttention-2 layout:
+// queries in the outer loop, accumulator in registers, one divide after the
+// loop, grid split over the sequence).
+//
+// Workgroup: 4 waves; wave w owns queries q0 + 32w .. q0 + 32w + 31.
+// Per key tile of BN = 64 rows (K and V staged through swizzled LDS, double
+// buffered, the next tile's global loads in flight during this tile's math):
+//   S^T = K Q^T          MFMA, A = K rows from LDS, B = Q^T kept in registers;
+//                        lane l holds query l % 32 and 32 of the 64 keys
+//   mask                 only on tiles that cross the diagonal or the end of N
+//   m_new = max(m, rowmax S)     in-lane max, then one v_permlane32_swap
+//   p = 2^(S c - m_new c), alpha = 2^((m - m_new) c), c = scale * log2(e)
+//   l = alpha l + rowsum p;  acc = alpha acc
+//   O^T += V^T P^T       MFMA, A = V^T by transposed LDS reads, B = P^T
+//                        converted from the S^T registers in place
+// After the last tile: O = acc / l, L = (m c + log2 l) ln 2.
+#include "fa_device.h"
+#include "fa_launch.h"
+
+namespace fa {
+
+template <class T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void fwd_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
+                                                  const void* __restrict__ vp, void* __restrict__ op,
+                                                  float* __restrict__ lsep, int N, int BH, int nqb,
+                                                  float c) {
+  constexpr int BM = 128, BN = 64, NT = 256, NKK = D / 16, NB = D / 32;
+  constexpr int TILE = BN * D * 2;
+  __shared__ __attribute__((aligned(16))) char smem[4 * TILE];
+  lds_char* lds = (lds_char*)smem;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5;
+  const int x = blockIdx.x;
+  const int qb = CAUSAL ? (nqb - 1 - x / BH) : (x / BH);
+  const int bh = x % BH;
+  const int q0 = qb * BM;
+  const size_t head = (size_t)bh * N * D * 2;
+  const uint32_t bytes = (uint32_t)N * D * 2;
+  const auto rq = make_rsrc((const char*)qp + head, bytes);
+  const auto rk = make_rsrc((const char*)kp + head, bytes);
+  const auto rv = make_rsrc((const char*)vp + head, bytes);
+  const auto ro = make_rsrc((char*)op + head, bytes);
+
+  const int qrow = q0 + 32 * w + (lane & 31);  // this lane's query
+  u32x4 qf[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) qf[kk] = bload16(rq, (uint32_t)((qrow * D + 16 * kk + 8 * h) * 2));
+
+  const int kend = CAUSAL ? min(N, q0 + BM) : N;
+  const int nt = (kend + BN - 1) / BN;
+
+  Stage<BN, D, NT> sk, sv;
+  sk.load(rk, 0, tid);
+  sv.load(rv, 0, tid);
+
+  f32x16 acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = (f32x16){};
+  float m = -INFINITY, l = 0.f;
+  const int wq0 = q0 + 32 * w;  // first query of this wave
+
+  for (int t = 0; t < nt; ++t) {
+    lds_char* kt = lds + (t & 1) * 2 * TILE;
+    lds_char* vt = kt + TILE;
+    sk.store(kt, tid);
+    sv.store(vt, tid);
+    __syncthreads();
+    if (t + 1 < nt) {
+      sk.load(rk, (t + 1) * BN, tid);
+      sv.load(rv, (t + 1) * BN, tid);
+    }
+    const int j0 = t * BN;
+
+    f32x16 s[2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      s[a] = (f32x16){};
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) s[a] = Elem<T>::mma(lds_rows_operand<D>(kt, 32 * a, kk, lane), qf[kk], s[a]);
+    }
+
+    const bool edge = (j0 + BN > N) || (CAUSAL && j0 + BN - 1 > wq0);
+    if (edge) {
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = j0 + 32 * a + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (key >= N || (CAUSAL && key > qrow)) s[a][r] = -INFINITY;
+        }
+    }
+
+    float mx = s[0][0];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[a][r]);
+    mx = max_with_partner(mx);
+    const float m_new = fmaxf(m, mx);
+    const float mc = m_new * c;
+    const float alpha = exp2_fast(m * c - mc);
+    float rs = 0.f;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = exp2_fast(__builtin_fmaf(s[a][r], c, -mc));
+        s[a][r] = p;
+        rs += p;
+      }
+    l = l * alpha + rs;
+    m = m_new;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b] *= alpha;
+
+    u32x4 pf[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pf[j] = pack8<T>(s[j >> 1], j & 1);
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[b] = Elem<T>::mma(lds_cols_operand<D>(vt, j, 32 * b, lane), pf[j], acc[b]);
+  }
+
+  const float lt = sum_with_partner(l);
+  store_rows<T, D>(ro, qrow, acc, 1.0f / lt, lane);
+  if (h == 0 && qrow < N) lsep[(size_t)bh * N + qrow] = (m * c + log2_fast(lt)) * kLn2;
+}
+
+template <class T, int D, bool CAUSAL>
+static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
+  const int BH = a.B * a.H;
+  const int nqb = (a.N + 127) / 128;
+  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL>), dim3(nqb * BH), dim3(256), 0, st, a.q, a.k, a.v, a.o,
+                     a.lse, a.N, BH, nqb, a.scale * kLog2e);
+  return hipGetLastError();
+}
+
+template <class T, int D>
+static hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t st) {
+  return a.causal ? launch_fwd_t<T, D, true>(a, st) : launch_fwd_t<T, D, false>(a, st);
+}
+
+template <class T>
+static hipError_t launch_fwd_e(const FwdArgs& a, hipStream_t st) {
+  switch (a.d) {
+    case 32: return launch_fwd_d<T, 32>(a, st);
+    case 64: return launch_fwd_d<T, 64>(a, st);
+    default: return launch_fwd_d<T, 128>(a, st);
+  }
+}
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
+  return a.bf16 ? launch_fwd_e<bf16_tag>(a, st) : launch_fwd_e<f16_tag>(a, st);
+}
+
+}  // namespace fa

@@ -1,0 +1,39 @@
+// Host-side launch descriptors shared by the C-ABI layer and the kernel files.
+// Arguments arrive here already validated (fa_api.cpp).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const void *q, *k, *v;
+  void* o;
+  float* lse;
+  int B, H, N, d;
+  float scale;
+  bool causal, bf16;
+};
+
+struct PreArgs {
+  const void *o, *dO;
+  float* delta;
+  int B, H, N, d;
+  bool bf16;
+};
+
+struct BwdArgs {
+  const void *q, *k, *v, *dO;
+  const float *lse, *delta;
+  void *dq, *dk, *dv;
+  int B, H, N, d;
+  float scale;
+  bool causal, bf16;
+};
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t st);
+hipError_t launch_preprocess(const PreArgs& a, hipStream_t st);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t st);
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t st);
+
+}  // namespace fa

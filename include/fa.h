@@ -1,0 +1,124 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) exact FlashAttention-2 library.
+ *
+ * The operation is exact softmax attention O = softmax(scale * Q K^T [+ causal
+ * mask]) V and its gradient, computed tile by tile without the N x N score
+ * matrix ever reaching device memory ("flash-attn-triton" docs, spec sheet and
+ * "Tiling softmax is exact algebra"; "flash attention" note, "Key
+ * Mechanisms").
+ *
+ * Conventions shared by every entry point
+ * ----------------------------------------
+ * Tensors      Q, K, V, O, dO, dQ, dK, dV: device pointers to contiguous
+ *              [B, H, N, d] arrays (d fastest, then N, then H, then B) of the
+ *              element type `dt`.  L (lse) and D (delta): device pointers to
+ *              contiguous [B, H, N] float32 arrays.
+ * Sizes        B, H, N >= 1; d in {32, 64, 128}; N * d * 2 <= 2^31 - 2^20
+ *              (one head slice is addressed with 32-bit byte offsets);
+ *              B * H * ceil(N / 64) < 2^24.  N need not be a multiple of any
+ *              tile size.  Larger sizes return FA_ERR_UNSUPPORTED.
+ * Mask         causal = 0: every key is visible to every query.  causal = 1:
+ *              key j is visible to query i iff j <= i ("flash attention"
+ *              note, "Key Mechanisms": lower-triangular causal mask).
+ * Scale        scale > 0 and finite; the caller passes 1/sqrt(d) for the
+ *              usual attention ("flash-attn-triton" docs, "The argument").
+ * Alignment    every pointer 16-byte aligned.
+ * Ownership    the caller allocates and owns every buffer.  The library
+ *              allocates no device memory, keeps no mutable global state and
+ *              may be called from several host threads.
+ * Streams      `stream` is a hipStream_t (NULL = the default stream).  Every
+ *              call only enqueues kernels on that stream and returns; nothing
+ *              synchronises.  Outputs are valid once the stream reaches them.
+ * Errors       arguments are checked before anything is enqueued; a failed
+ *              check returns a negative FA_ERR_* code and enqueues nothing.
+ *              FA_ERR_HIP means a kernel launch was refused by the runtime.
+ *              Faults during execution surface at the caller's next
+ *              synchronisation as HIP errors.  Outputs must not overlap
+ *              inputs or each other (FA_ERR_ALIAS).
+ * Determinism  no atomics: repeated calls on the same inputs give the same bits.
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
+
+enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, bad mask/scale/dtype */
+  FA_ERR_UNSUPPORTED = -2, /* head dim not in {32,64,128}, or sizes beyond the limits above */
+  FA_ERR_ALIGNMENT = -3,   /* a pointer is not 16-byte aligned */
+  FA_ERR_HIP = -4,         /* the HIP runtime refused a launch */
+  FA_ERR_ALIAS = -5        /* an output overlaps an input or another output */
+};
+
+/*
+ * fa_fwd -- forward pass ("flash-attn-triton" docs, Fig. 3 "the update, per
+ * tile", and "Tiling softmax is exact algebra").
+ *   in : q, k, v  [B,H,N,d] of dt
+ *   out: o        [B,H,N,d] of dt, o = softmax(scale*q k^T, masked) v,
+ *                 rounded to nearest even
+ *        lse      [B,H,N] float32, lse_i = log(sum_j exp(scale*q_i.k_j)) over
+ *                 the keys visible to query i (natural logarithm).  This is
+ *                 the only state the backward needs besides the inputs.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale, int causal, fa_dtype dt,
+           void* stream);
+
+/*
+ * fa_bwd_preprocess -- the delta pre-pass of the backward ("flash-attn-triton"
+ * docs, "Where things live": delta pre-pass, then dK/dV and dQ).
+ *   in : o, dO    [B,H,N,d] of dt (o as written by fa_fwd)
+ *   out: delta    [B,H,N] float32, delta_i = sum_k dO_ik * o_ik (fp32 sum)
+ */
+int fa_bwd_preprocess(const void* o, const void* dO, float* delta,
+                      int B, int H, int N, int d, fa_dtype dt, void* stream);
+
+/*
+ * fa_bwd -- backward pass: rebuilds P from lse and produces dQ, dK, dV
+ * ("flash-attn-triton" docs, "Scope": backward kernels for dQ, dK, dV
+ * rebuilding P from the saved L; "flash attention" note, "Key Mechanisms":
+ * backward recomputation).  Enqueues fa_bwd_dkdv then fa_bwd_dq.
+ *   in : q, k, v, dO   [B,H,N,d] of dt
+ *        lse           [B,H,N] float32 from fa_fwd (same q, k, scale, causal)
+ *        delta         [B,H,N] float32 from fa_bwd_preprocess
+ *   out: dq, dk, dv    [B,H,N,d] of dt, the gradients of sum(dO * o) with
+ *                      respect to q, k, v:
+ *                        P = exp(scale*q k^T - lse), masked entries 0
+ *                        dv = P^T dO;  dP = dO v^T;  dS = P * (dP - delta)
+ *                        dq = scale * dS k;  dk = scale * dS^T q
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* dO,
+           const float* lse, const float* delta, void* dq, void* dk, void* dv,
+           int B, int H, int N, int d, float scale, int causal, fa_dtype dt,
+           void* stream);
+
+/* fa_bwd_dkdv -- the first half of fa_bwd: dk and dv only (key-block outer
+ * loop over query blocks).  Same arguments and rules as fa_bwd. */
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO,
+                const float* lse, const float* delta, void* dk, void* dv,
+                int B, int H, int N, int d, float scale, int causal,
+                fa_dtype dt, void* stream);
+
+/* fa_bwd_dq -- the second half of fa_bwd: dq only (query-block outer loop
+ * over key blocks).  Same arguments and rules as fa_bwd. */
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
+              const float* lse, const float* delta, void* dq,
+              int B, int H, int N, int d, float scale, int causal,
+              fa_dtype dt, void* stream);
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* fa_status_string(int status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

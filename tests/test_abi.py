@@ -1,0 +1,154 @@
+"""The C-ABI library loads, exports every function include/fa.h declares, and
+rejects bad arguments before enqueuing anything (no GPU needed).
+
+Where a GPU is visible the pointers handed to rejected calls are real device
+buffers of the stated sizes, so that even a wrongly accepted call would stay
+in bounds; without a GPU they are plain addresses that are never touched.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+from exact_io_aware_30_amd import binding  # noqa: E402
+
+lib = binding._lib
+OK, INVALID, UNSUPPORTED, ALIGN, HIPERR, ALIAS = 0, -1, -2, -3, -4, -5
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_functions_are_exported():
+    names = declared_functions()
+    assert names == sorted(["fa_fwd", "fa_bwd_preprocess", "fa_bwd", "fa_bwd_dkdv", "fa_bwd_dq",
+                            "fa_status_string", "fa_version"])
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (fa_\w+)$", out, flags=re.M))
+    for n in names:
+        assert n in exported, n
+        assert hasattr(lib, n)
+    assert set(binding.EXPORTED) == set(names)
+
+
+def test_status_strings_and_version():
+    for code in (OK, INVALID, UNSUPPORTED, ALIGN, HIPERR, ALIAS):
+        s = binding.fa_status_string(code)
+        assert s and s != "unknown status"
+    assert binding.fa_status_string(12345) == "unknown status"
+    assert binding.fa_version() >= 100
+
+
+class Ptrs:
+    """Pointer values for argument checks: device buffers if a GPU exists."""
+
+    def __init__(self, nbytes=1 << 16, count=12):
+        self.keep = []
+        if torch.cuda.is_available():
+            for _ in range(count):
+                t = torch.zeros(nbytes // 2, dtype=torch.float16, device="cuda")
+                self.keep.append(t)
+            self.p = [t.data_ptr() for t in self.keep]
+        else:
+            self.p = [0x10000000 * (i + 1) for i in range(count)]
+
+
+SMALL = dict(B=1, H=1, N=64, d=64)  # 8 KiB per tensor, fits the 64 KiB buffers
+
+
+def fwd(p, q=None, k=None, v=None, o=None, lse=None, B=1, H=1, N=64, d=64, scale=0.125, causal=0, dt=1):
+    a = [p[0] if q is None else q, p[1] if k is None else k, p[2] if v is None else v,
+         p[3] if o is None else o, p[4] if lse is None else lse]
+    return lib.fa_fwd(*a, B, H, N, d, scale, causal, dt, None)
+
+
+def bwd(p, fn="fa_bwd", B=1, H=1, N=64, d=64, scale=0.125, causal=0, dt=1, **over):
+    names = ["q", "k", "v", "do", "lse", "delta", "dq", "dk", "dv"]
+    vals = {n: p[i] for i, n in enumerate(names)}
+    vals.update(over)
+    if fn == "fa_bwd":
+        args = [vals[n] for n in names]
+    elif fn == "fa_bwd_dkdv":
+        args = [vals[n] for n in names if n != "dq"]
+    else:
+        args = [vals[n] for n in names if n not in ("dk", "dv")]
+    return getattr(lib, fn)(*args, B, H, N, d, scale, causal, dt, None)
+
+
+@pytest.fixture(scope="module")
+def p():
+    return Ptrs().p
+
+
+def test_fwd_rejects(p):
+    for i in range(5):
+        args = {k: None for k in ("q", "k", "v", "o", "lse")}
+        key = list(args)[i]
+        assert fwd(p, **{key: 0}) == INVALID
+    assert fwd(p, B=0) == INVALID
+    assert fwd(p, H=-1) == INVALID
+    assert fwd(p, N=0) == INVALID
+    for d in (0, 16, 48, 96, 256):
+        assert fwd(p, d=d) == UNSUPPORTED
+    for s in (0.0, -1.0, float("nan"), float("inf")):
+        assert fwd(p, scale=s) == INVALID
+    assert fwd(p, causal=2) == INVALID
+    assert fwd(p, causal=-1) == INVALID
+    assert fwd(p, dt=2) == INVALID
+    assert fwd(p, q=p[0] + 8) == ALIGN
+    assert fwd(p, lse=p[4] + 4) == ALIGN
+    # one head slice must fit 32-bit byte offsets
+    assert fwd(p, N=((1 << 31) - (1 << 20)) // 256 + 1, d=128) == UNSUPPORTED
+    assert fwd(p, B=1 << 12, H=1 << 12, N=64) == UNSUPPORTED
+    # outputs overlapping inputs or each other
+    assert fwd(p, o=p[0]) == ALIAS
+    assert fwd(p, lse=p[3] + 16) == ALIAS
+    assert fwd(p, o=p[2] + 4096) == ALIAS
+
+
+def test_preprocess_rejects(p):
+    pre = lambda o=p[0], do=p[1], dl=p[2], B=1, H=1, N=64, d=64, dt=1: \
+        lib.fa_bwd_preprocess(o, do, dl, B, H, N, d, dt, None)  # noqa: E731
+    assert pre(o=0) == INVALID
+    assert pre(dl=0) == INVALID
+    assert pre(N=0) == INVALID
+    assert pre(d=80) == UNSUPPORTED
+    assert pre(dt=5) == INVALID
+    assert pre(do=p[1] + 2) == ALIGN
+    assert pre(dl=p[0] + 64) == ALIAS
+
+
+@pytest.mark.parametrize("fn", ["fa_bwd", "fa_bwd_dkdv", "fa_bwd_dq"])
+def test_bwd_rejects(p, fn):
+    outs = {"fa_bwd": ["dq", "dk", "dv"], "fa_bwd_dkdv": ["dk", "dv"], "fa_bwd_dq": ["dq"]}[fn]
+    for name in ["q", "k", "v", "do", "lse", "delta"] + outs:
+        assert bwd(p, fn, **{name: 0}) == INVALID, name
+    assert bwd(p, fn, N=0) == INVALID
+    assert bwd(p, fn, d=100) == UNSUPPORTED
+    assert bwd(p, fn, scale=float("nan")) == INVALID
+    assert bwd(p, fn, causal=3) == INVALID
+    assert bwd(p, fn, dt=9) == INVALID
+    assert bwd(p, fn, delta=p[5] + 4) == ALIGN
+    assert bwd(p, fn, **{outs[0]: p[0]}) == ALIAS
+    assert bwd(p, fn, **{outs[-1]: p[4]}) == ALIAS
+    if len(outs) > 1:
+        assert bwd(p, fn, **{outs[0]: p[11], outs[1]: p[11] + 64}) == ALIAS
+
+
+def test_binding_rejects_host_tensors():
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    lse = torch.zeros(1, 1, 8)
+    with pytest.raises(ValueError):
+        binding.fa_fwd(q, q, q, q.clone(), lse, 0.125, False)
+    with pytest.raises(ValueError):
+        binding.fa_bwd_preprocess(q.float(), q.float(), lse)
