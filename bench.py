@@ -14,8 +14,8 @@ Prints one JSON line.  Besides the contract fields it carries
                 the dense bf16 MFMA peak, plus its HBM traffic per launch
                 from the committed rocprofv3 counter summary when that was
                 taken on the current kernel sources (else null);
-  cpu_baseline  the CPU fp64 oracle timed on one head of the same workload
-                (a bounded sample), in the same unit;
+  cpu_baseline  the CPU fp64 oracle timed on 24 of the 32 heads of the same
+                workload (a bounded sample), in the same unit;
   kernels       average duration, TFLOP/s and fraction of peak per kernel.
 """
 
@@ -62,15 +62,15 @@ def traffic_from_summary(kernel: str):
     return float(m.group(1)) if m else None
 
 
-def cpu_baseline(w, heads: int = 4):
-    """The oracle, as it stands, on the first `heads` heads of batch 0."""
+def cpu_baseline(w, heads: int = 24):
+    """The oracle, as it stands, on the first `heads` of the B*H heads."""
     import numpy as np
 
     import oracle
     from exact_io_aware_30_amd import workloads
 
     q, k, v, do = workloads.make_inputs(w)
-    one = [x[:1, :heads].to("cpu").double().numpy() for x in (q, k, v, do)]
+    one = [x.reshape(1, w.B * w.H, w.N, w.d)[:, :heads].to("cpu").double().numpy() for x in (q, k, v, do)]
     cores = os.cpu_count() or 1
     try:
         from threadpoolctl import threadpool_info
@@ -83,7 +83,8 @@ def cpu_baseline(w, heads: int = 4):
     sample = workloads.Workload("sample", w.dtype, 1, heads, w.N, w.d, w.causal, w.q_scale, w.seed)
     fb = workloads.flops(sample)[2]
     return {"value": fb / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"heads (b=0, h=0..{heads - 1}) of {w.describe()}: fwd+bwd, {dt:.1f} s wall, numpy fp64",
+            "sample": f"the first {heads} of {w.B * w.H} heads of {w.describe()}: fwd+bwd, {dt:.1f} s wall, "
+                      f"numpy fp64",
             "seconds": round(dt, 3)}
 
 
@@ -94,6 +95,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after the timed steps, copy a buffer of this many MiB once (a kernel of known "
+                         "traffic for scaling hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -143,6 +147,14 @@ def main():
     wall = time.perf_counter() - t0
     per = {p: sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / args.steps for j, p in enumerate(phases)}
     assert torch.isfinite(o).all() and torch.isfinite(dq).all(), "non-finite output"
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     f, b, fb = workloads.flops(w)
     ms = wall * 1e3 / args.steps
