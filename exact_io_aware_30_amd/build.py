@@ -30,6 +30,9 @@ FLAGS = [
     "-std=c++17",
     "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA sources and accumulators in VGPRs: without this the backend keeps
+    # accumulators in AGPRs and copies them through VGPRs for every VALU use.
+    "-mllvm", "--amdgpu-mfma-vgpr-form",
     "-I" + os.path.join(ROOT, "include"),
 ]
 

@@ -42,6 +42,57 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const void* __restrict_
   }
 }
 
+// One query tile of the dK/dV kernel for one wave (MASK: the tile crosses
+// the causal diagonal of this wave's keys).
+template <class T, int D, bool MASK>
+__device__ __forceinline__ void dkdv_tile(const lds_char* qt, const lds_char* dot, const float* st, const u32x4* kf,
+                                          const u32x4* vf, f32x16* dka, f32x16* dva, int i0, int krow, float c,
+                                          int lane) {
+  constexpr int NKK = D / 16, NB = D / 32;
+  const int h = lane >> 5;
+  f32x16 s[2], dp[2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    s[a] = (f32x16){};
+    dp[a] = (f32x16){};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      s[a] = Elem<T>::mma(lds_rows_operand<D>(qt, 32 * a, kk, lane), kf[kk], s[a]);
+      dp[a] = Elem<T>::mma(lds_rows_operand<D>(dot, 32 * a, kk, lane), vf[kk], dp[a]);
+    }
+  }
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int qi = 32 * a + 8 * g + 4 * h;
+      const f32x4 l2 = *(const f32x4*)(st + qi);
+      const f32x4 dd = *(const f32x4*)(st + 64 + qi);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * g + e;
+        float x = s[a][r];
+        if constexpr (MASK) x = krow > i0 + qi + e ? -INFINITY : x;
+        const float p = exp2_fast(__builtin_fmaf(x, c, -l2[e]));
+        s[a][r] = p;
+        dp[a][r] = p * (dp[a][r] - dd[e]);
+      }
+    }
+  u32x4 pf[4], dsf[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    pf[j] = pack8<T>(s[j >> 1], j & 1);
+    dsf[j] = pack8<T>(dp[j >> 1], j & 1);
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      dva[b] = Elem<T>::mma(lds_cols_operand<D>(dot, j, 32 * b, lane), pf[j], dva[b]);
+      dka[b] = Elem<T>::mma(lds_cols_operand<D>(qt, j, 32 * b, lane), dsf[j], dka[b]);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // dK, dV.  Workgroup = 128 keys of one head (wave w owns keys k0 + 32w ..
 // k0 + 32w + 31, with its K and V rows resident as MFMA B operands), looping
@@ -122,51 +173,53 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const void* __restrict__ qp, 
       load_rowstats(i0 + BMQ);
     }
     if (CAUSAL && i0 + BMQ - 1 < wk0) continue;  // every query of the tile precedes every key of the wave
-
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      s[a] = (f32x16){};
-      dp[a] = (f32x16){};
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        s[a] = Elem<T>::mma(lds_rows_operand<D>(qt, 32 * a, kk, lane), kf[kk], s[a]);
-        dp[a] = Elem<T>::mma(lds_rows_operand<D>(dot, 32 * a, kk, lane), vf[kk], dp[a]);
-      }
-    }
-    const bool edge = CAUSAL && (i0 < wk0 + 31);
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int qi = 32 * a + 8 * g + 4 * h;
-        const f32x4 l2 = *(const f32x4*)(st + qi);
-        const f32x4 dd = *(const f32x4*)(st + 64 + qi);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g + e;
-          float p = exp2_fast(__builtin_fmaf(s[a][r], c, -l2[e]));
-          if (edge && krow > i0 + qi + e) p = 0.f;
-          s[a][r] = p;
-          dp[a][r] = p * (dp[a][r] - dd[e]);
-        }
-      }
-    u32x4 pf[4], dsf[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      pf[j] = pack8<T>(s[j >> 1], j & 1);
-      dsf[j] = pack8<T>(dp[j >> 1], j & 1);
-    }
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        dva[b] = Elem<T>::mma(lds_cols_operand<D>(dot, j, 32 * b, lane), pf[j], dva[b]);
-        dka[b] = Elem<T>::mma(lds_cols_operand<D>(qt, j, 32 * b, lane), dsf[j], dka[b]);
-      }
+    if (CAUSAL && i0 < wk0 + 31)
+      dkdv_tile<T, D, true>(qt, dot, st, kf, vf, dka, dva, i0, krow, c, lane);
+    else
+      dkdv_tile<T, D, false>(qt, dot, st, kf, vf, dka, dva, i0, krow, c, lane);
   }
   store_rows<T, D>(rdk, krow, dka, scale, lane);
   store_rows<T, D>(rdv, krow, dva, 1.0f, lane);
+}
+
+// One key tile of the dQ kernel for one wave (MASK: the tile crosses the
+// causal diagonal of this wave's queries or the end of N).
+template <class T, int D, bool CAUSAL, bool MASK>
+__device__ __forceinline__ void dq_tile(const lds_char* kt, const lds_char* vt, const u32x4* qf, const u32x4* dof,
+                                        f32x16* dqa, float l2, float dd, int j0, int qrow, int N, float c,
+                                        int lane) {
+  constexpr int NKK = D / 16, NB = D / 32;
+  const int h = lane >> 5;
+  f32x16 s[2], dp[2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    s[a] = (f32x16){};
+    dp[a] = (f32x16){};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      s[a] = Elem<T>::mma(lds_rows_operand<D>(kt, 32 * a, kk, lane), qf[kk], s[a]);
+      dp[a] = Elem<T>::mma(lds_rows_operand<D>(vt, 32 * a, kk, lane), dof[kk], dp[a]);
+    }
+  }
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float x = s[a][r];
+      if constexpr (MASK) {
+        const int key = j0 + 32 * a + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (key >= N || (CAUSAL && key > qrow)) x = -INFINITY;
+      }
+      const float p = exp2_fast(__builtin_fmaf(x, c, -l2));
+      dp[a][r] = p * (dp[a][r] - dd);
+    }
+  u32x4 dsf[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) dsf[j] = pack8<T>(dp[j >> 1], j & 1);
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dqa[b] = Elem<T>::mma(lds_cols_operand<D>(kt, j, 32 * b, lane), dsf[j], dqa[b]);
 }
 
 // ---------------------------------------------------------------------------
@@ -234,37 +287,10 @@ __global__ __launch_bounds__(256) void dq_kernel(const void* __restrict__ qp, co
     }
     const int j0 = t * BN;
     if (CAUSAL && j0 > wq0 + 31) continue;  // every key of the tile follows every query of the wave
-
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      s[a] = (f32x16){};
-      dp[a] = (f32x16){};
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        s[a] = Elem<T>::mma(lds_rows_operand<D>(kt, 32 * a, kk, lane), qf[kk], s[a]);
-        dp[a] = Elem<T>::mma(lds_rows_operand<D>(vt, 32 * a, kk, lane), dof[kk], dp[a]);
-      }
-    }
-    const bool edge = (j0 + BN > N) || (CAUSAL && j0 + BN - 1 > wq0);
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = exp2_fast(__builtin_fmaf(s[a][r], c, -l2));
-        if (edge) {
-          const int key = j0 + 32 * a + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (key >= N || (CAUSAL && key > qrow)) p = 0.f;
-        }
-        dp[a][r] = p * (dp[a][r] - dd);
-      }
-    u32x4 dsf[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dsf[j] = pack8<T>(dp[j >> 1], j & 1);
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) dqa[b] = Elem<T>::mma(lds_cols_operand<D>(kt, j, 32 * b, lane), dsf[j], dqa[b]);
+    if ((j0 + BN > N) || (CAUSAL && j0 + BN - 1 > wq0))
+      dq_tile<T, D, CAUSAL, true>(kt, vt, qf, dof, dqa, l2, dd, j0, qrow, N, c, lane);
+    else
+      dq_tile<T, D, CAUSAL, false>(kt, vt, qf, dof, dqa, l2, dd, j0, qrow, N, c, lane);
   }
   store_rows<T, D>(rdq, qrow, dqa, scale, lane);
 }

@@ -21,6 +21,68 @@
 
 namespace fa {
 
+// Rescale threshold in base-2 units: the reference maximum used for the
+// exponentials is moved only when a row's maximum exceeds it by more than
+// this, so p = 2^(S c - ref) stays below 2^8 and most tiles skip the
+// rescale of l and acc.  O = acc / l and L = ref + log2 l hold for any
+// reference, so the result is the same up to rounding.
+constexpr float kRescaleSlack = 8.0f;
+
+// One key tile for one wave: S^T, optional mask, online-softmax update, PV.
+template <class T, int D, bool CAUSAL, bool MASK>
+__device__ __forceinline__ void fwd_tile(const lds_char* kt, const lds_char* vt, const u32x4* qf, f32x16* acc,
+                                         float& mref, float& l, int j0, int qrow, int N, float c, int lane) {
+  constexpr int NKK = D / 16, NB = D / 32;
+  const int h = lane >> 5;
+  f32x16 s[2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    s[a] = (f32x16){};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) s[a] = Elem<T>::mma(lds_rows_operand<D>(kt, 32 * a, kk, lane), qf[kk], s[a]);
+  }
+  if constexpr (MASK) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = j0 + 32 * a + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (key >= N || (CAUSAL && key > qrow)) s[a][r] = -INFINITY;
+      }
+  }
+  float mx = s[0][0];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[a][r]);
+  const float mxc = max_with_partner(mx) * c;  // row max in base-2 units
+  if (__builtin_amdgcn_ballot_w64(mxc > mref + kRescaleSlack)) {
+    const float mnew = fmaxf(mref, mxc);
+    const float alpha = exp2_fast(mref - mnew);  // 0 on the first tile (mref = -inf)
+    mref = mnew;
+    l *= alpha;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b] *= alpha;
+  }
+  float rs = 0.f;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = exp2_fast(__builtin_fmaf(s[a][r], c, -mref));
+      s[a][r] = p;
+      rs += p;
+    }
+  l += rs;
+  u32x4 pf[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) pf[j] = pack8<T>(s[j >> 1], j & 1);
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[b] = Elem<T>::mma(lds_cols_operand<D>(vt, j, 32 * b, lane), pf[j], acc[b]);
+}
+
 template <class T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void fwd_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
                                                   const void* __restrict__ vp, void* __restrict__ op,
@@ -58,8 +120,8 @@ __global__ __launch_bounds__(256) void fwd_kernel(const void* __restrict__ qp, c
   f32x16 acc[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) acc[b] = (f32x16){};
-  float m = -INFINITY, l = 0.f;
-  const int wq0 = q0 + 32 * w;  // first query of this wave
+  float mref = -INFINITY, l = 0.f;  // reference max (base 2) and this lane's part of the row sum
+  const int wq0 = q0 + 32 * w;      // first query of this wave
 
   for (int t = 0; t < nt; ++t) {
     lds_char* kt = lds + (t & 1) * 2 * TILE;
@@ -72,61 +134,17 @@ __global__ __launch_bounds__(256) void fwd_kernel(const void* __restrict__ qp, c
       sv.load(rv, (t + 1) * BN, tid);
     }
     const int j0 = t * BN;
-
-    f32x16 s[2];
-#pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      s[a] = (f32x16){};
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) s[a] = Elem<T>::mma(lds_rows_operand<D>(kt, 32 * a, kk, lane), qf[kk], s[a]);
-    }
-
+    if (CAUSAL && j0 > wq0 + 31) continue;  // every key of the tile follows every query of the wave
     const bool edge = (j0 + BN > N) || (CAUSAL && j0 + BN - 1 > wq0);
-    if (edge) {
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = j0 + 32 * a + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (key >= N || (CAUSAL && key > qrow)) s[a][r] = -INFINITY;
-        }
-    }
-
-    float mx = s[0][0];
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[a][r]);
-    mx = max_with_partner(mx);
-    const float m_new = fmaxf(m, mx);
-    const float mc = m_new * c;
-    const float alpha = exp2_fast(m * c - mc);
-    float rs = 0.f;
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2_fast(__builtin_fmaf(s[a][r], c, -mc));
-        s[a][r] = p;
-        rs += p;
-      }
-    l = l * alpha + rs;
-    m = m_new;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) acc[b] *= alpha;
-
-    u32x4 pf[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) pf[j] = pack8<T>(s[j >> 1], j & 1);
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[b] = Elem<T>::mma(lds_cols_operand<D>(vt, j, 32 * b, lane), pf[j], acc[b]);
+    if (edge)
+      fwd_tile<T, D, CAUSAL, true>(kt, vt, qf, acc, mref, l, j0, qrow, N, c, lane);
+    else
+      fwd_tile<T, D, CAUSAL, false>(kt, vt, qf, acc, mref, l, j0, qrow, N, c, lane);
   }
 
   const float lt = sum_with_partner(l);
   store_rows<T, D>(ro, qrow, acc, 1.0f / lt, lane);
-  if (h == 0 && qrow < N) lsep[(size_t)bh * N + qrow] = (m * c + log2_fast(lt)) * kLn2;
+  if (h == 0 && qrow < N) lsep[(size_t)bh * N + qrow] = (mref + log2_fast(lt)) * kLn2;
 }
 
 template <class T, int D, bool CAUSAL>
