@@ -66,7 +66,7 @@ __device__ __forceinline__ void dkdv_tile(const lds_char* qt, const lds_char* do
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int qi = 32 * a + 8 * g + 4 * h;
-      const f32x4 l2 = *(const f32x4*)(st + qi);
+      const f32x4 l2 = *(const f32x4*)(st + qi) * kLog2e;
       const f32x4 dd = *(const f32x4*)(st + 64 + qi);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -93,11 +93,44 @@ __device__ __forceinline__ void dkdv_tile(const lds_char* qt, const lds_char* do
     }
 }
 
+// Enqueue the DMA of query tile i0: Q rows, dO rows, then L and D (one
+// dword per lane, waves 0 and 1).  Rows past N load as zeros: their Q and
+// dO rows are zero, so they add nothing to dV (dO = 0) or to dK
+// (dS = P (0 - 0) = 0) whatever P is.
+template <int D>
+__device__ __forceinline__ void dkdv_issue(lds_char* b, int i0, const DmaTile<64, D, 4>& dma,
+                                           __amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rdo,
+                                           __amdgpu_buffer_rsrc_t rl, __amdgpu_buffer_rsrc_t rd, int w, int lane) {
+  constexpr int BMQ = 64, TILE = BMQ * D * 2;
+  dma.issue(rq, b, i0, w);
+  dma.issue(rdo, b + TILE, i0, w);
+  if (w < 2) dma4(w == 0 ? rl : rd, b + 2 * TILE + w * BMQ * 4, (uint32_t)((i0 + lane) * 4));
+}
+
+template <class T, int D, bool CAUSAL>
+__device__ __forceinline__ void dkdv_step(lds_char* cur, lds_char* nxt, int t, int nt, int i_start,
+                                          const DmaTile<64, D, 4>& dma, __amdgpu_buffer_rsrc_t rq,
+                                          __amdgpu_buffer_rsrc_t rdo, __amdgpu_buffer_rsrc_t rl,
+                                          __amdgpu_buffer_rsrc_t rd, const u32x4* kf, const u32x4* vf, f32x16* dka,
+                                          f32x16* dva, int wk0, int krow, float c, int w, int lane) {
+  constexpr int BMQ = 64, TILE = BMQ * D * 2;
+  dma_barrier();
+  const int i0 = i_start + t * BMQ;
+  if (t + 1 < nt) dkdv_issue<D>(nxt, i0 + BMQ, dma, rq, rdo, rl, rd, w, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  if (CAUSAL && i0 + BMQ - 1 < wk0) return;  // every query of the tile precedes every key of the wave
+  const float* st = (const float*)(cur + 2 * TILE);
+  if (CAUSAL && i0 < wk0 + 31)
+    dkdv_tile<T, D, true>(cur, cur + TILE, st, kf, vf, dka, dva, i0, krow, c, lane);
+  else
+    dkdv_tile<T, D, false>(cur, cur + TILE, st, kf, vf, dka, dva, i0, krow, c, lane);
+}
+
 // ---------------------------------------------------------------------------
 // dK, dV.  Workgroup = 128 keys of one head (wave w owns keys k0 + 32w ..
 // k0 + 32w + 31, with its K and V rows resident as MFMA B operands), looping
-// over query tiles of 64 rows: Q and dO tiles plus their L and D staged
-// through swizzled LDS, double buffered.  Per tile and wave:
+// over query tiles of 64 rows: Q and dO tiles plus their L and D copied by
+// buffer DMA into swizzled LDS, double buffered.  Per tile and wave:
 //   S = Q K^T, dP = dO V^T          (lane = key, registers = queries)
 //   P = 2^(S c - L2), dS = P (dP - D)
 //   dV^T += dO^T P, dK^T += Q^T dS  (A operands by transposed LDS reads)
@@ -110,11 +143,11 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const void* __restrict__ qp, 
                                                    const float* __restrict__ lsep, const float* __restrict__ deltap,
                                                    void* __restrict__ dkp, void* __restrict__ dvp, int N, int BH,
                                                    float c, float scale) {
-  constexpr int BNK = 128, BMQ = 64, NT = 256, NKK = D / 16, NB = D / 32;
+  constexpr int BNK = 128, BMQ = 64, NW = 4, NKK = D / 16, NB = D / 32;
   constexpr int TILE = BMQ * D * 2;
-  constexpr int BUF = 2 * TILE + 2 * BMQ * 4;
-  __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
-  lds_char* lds = (lds_char*)smem;
+  constexpr int BUF = 2 * TILE + 2 * BMQ * 4;  // Q tile, dO tile, L[64], D[64]
+  __shared__ __attribute__((aligned(16))) char buf0[BUF];
+  __shared__ __attribute__((aligned(16))) char buf1[BUF];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5;
   const int x = blockIdx.x;
@@ -128,8 +161,14 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const void* __restrict__ qp, 
   const auto rdo = make_rsrc((const char*)dop + head, bytes);
   const auto rdk = make_rsrc((char*)dkp + head, bytes);
   const auto rdv = make_rsrc((char*)dvp + head, bytes);
-  const float* lse = lsep + (size_t)bh * N;
-  const float* dlt = deltap + (size_t)bh * N;
+  const auto rl = make_rsrc(lsep + (size_t)bh * N, (uint32_t)N * 4);
+  const auto rd = make_rsrc(deltap + (size_t)bh * N, (uint32_t)N * 4);
+
+  const int i_start = CAUSAL ? k0 : 0;
+  const int nt = (N - i_start + BMQ - 1) / BMQ;
+  DmaTile<BMQ, D, NW> dma;
+  dma.init(w, lane);
+  dkdv_issue<D>((lds_char*)buf0, i_start, dma, rq, rdo, rl, rd, w, lane);
 
   const int wk0 = k0 + 32 * w;
   const int krow = wk0 + (lane & 31);
@@ -139,44 +178,16 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const void* __restrict__ qp, 
     kf[kk] = bload16(rk, (uint32_t)((krow * D + 16 * kk + 8 * h) * 2));
     vf[kk] = bload16(rv, (uint32_t)((krow * D + 16 * kk + 8 * h) * 2));
   }
-
-  const int i_start = CAUSAL ? k0 : 0;
-  const int nt = (N - i_start + BMQ - 1) / BMQ;
-
-  Stage<BMQ, D, NT> sq, sdo;
-  float ld = 0.f;  // this thread's L (tid < 64) or D (64 <= tid < 128) for the next tile
-  auto load_rowstats = [&](int i0) {
-    const int r = i0 + (tid & 63);
-    if (tid < 64) ld = r < N ? lse[r] * kLog2e : INFINITY;
-    else if (tid < 128) ld = r < N ? dlt[r] : 0.f;
-  };
-  sq.load(rq, i_start, tid);
-  sdo.load(rdo, i_start, tid);
-  load_rowstats(i_start);
-
   f32x16 dka[NB], dva[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) dka[b] = dva[b] = (f32x16){};
 
-  for (int t = 0; t < nt; ++t) {
-    lds_char* qt = lds + (t & 1) * BUF;
-    lds_char* dot = qt + TILE;
-    float* st = (float*)(dot + TILE);  // [0, 64): L * log2 e, [64, 128): D
-    sq.store(qt, tid);
-    sdo.store(dot, tid);
-    if (tid < 128) st[tid] = ld;
-    __syncthreads();
-    const int i0 = i_start + t * BMQ;
-    if (t + 1 < nt) {
-      sq.load(rq, i0 + BMQ, tid);
-      sdo.load(rdo, i0 + BMQ, tid);
-      load_rowstats(i0 + BMQ);
-    }
-    if (CAUSAL && i0 + BMQ - 1 < wk0) continue;  // every query of the tile precedes every key of the wave
-    if (CAUSAL && i0 < wk0 + 31)
-      dkdv_tile<T, D, true>(qt, dot, st, kf, vf, dka, dva, i0, krow, c, lane);
-    else
-      dkdv_tile<T, D, false>(qt, dot, st, kf, vf, dka, dva, i0, krow, c, lane);
+  for (int t = 0; t < nt; t += 2) {
+    dkdv_step<T, D, CAUSAL>((lds_char*)buf0, (lds_char*)buf1, t, nt, i_start, dma, rq, rdo, rl, rd, kf, vf, dka, dva,
+                            wk0, krow, c, w, lane);
+    if (t + 1 < nt)
+      dkdv_step<T, D, CAUSAL>((lds_char*)buf1, (lds_char*)buf0, t + 1, nt, i_start, dma, rq, rdo, rl, rd, kf, vf, dka,
+                              dva, wk0, krow, c, w, lane);
   }
   store_rows<T, D>(rdk, krow, dka, scale, lane);
   store_rows<T, D>(rdv, krow, dva, 1.0f, lane);
@@ -222,10 +233,30 @@ __device__ __forceinline__ void dq_tile(const lds_char* kt, const lds_char* vt, 
     for (int j = 0; j < 4; ++j) dqa[b] = Elem<T>::mma(lds_cols_operand<D>(kt, j, 32 * b, lane), dsf[j], dqa[b]);
 }
 
+template <class T, int D, bool CAUSAL>
+__device__ __forceinline__ void dq_step(lds_char* cur, lds_char* nxt, int t, int nt, const DmaTile<64, D, 4>& dma,
+                                        __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, const u32x4* qf,
+                                        const u32x4* dof, f32x16* dqa, float l2, float dd, int wq0, int qrow, int N,
+                                        float c, int w, int lane) {
+  constexpr int BN = 64, TILE = BN * D * 2;
+  dma_barrier();
+  if (t + 1 < nt) {
+    dma.issue(rk, nxt, (t + 1) * BN, w);
+    dma.issue(rv, nxt + TILE, (t + 1) * BN, w);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const int j0 = t * BN;
+  if (CAUSAL && j0 > wq0 + 31) return;  // every key of the tile follows every query of the wave
+  if ((j0 + BN > N) || (CAUSAL && j0 + BN - 1 > wq0))
+    dq_tile<T, D, CAUSAL, true>(cur, cur + TILE, qf, dof, dqa, l2, dd, j0, qrow, N, c, lane);
+  else
+    dq_tile<T, D, CAUSAL, false>(cur, cur + TILE, qf, dof, dqa, l2, dd, j0, qrow, N, c, lane);
+}
+
 // ---------------------------------------------------------------------------
 // dQ.  Workgroup = 128 queries of one head (wave w owns 32, with its Q and dO
 // rows resident as MFMA B operands and its L and D in registers), looping
-// over key tiles of 64 rows (K and V staged through swizzled LDS):
+// over key tiles of 64 rows (K and V copied by buffer DMA into swizzled LDS):
 //   S^T = K Q^T, dP^T = V dO^T   (lane = query, registers = keys)
 //   P = 2^(S c - L2), dS = P (dP - D)
 //   dQ^T += K^T dS^T             (A operand by transposed LDS reads)
@@ -236,10 +267,10 @@ __global__ __launch_bounds__(256) void dq_kernel(const void* __restrict__ qp, co
                                                  const float* __restrict__ lsep, const float* __restrict__ deltap,
                                                  void* __restrict__ dqp, int N, int BH, int nqb, float c,
                                                  float scale) {
-  constexpr int BM = 128, BN = 64, NT = 256, NKK = D / 16, NB = D / 32;
+  constexpr int BM = 128, BN = 64, NW = 4, NKK = D / 16, NB = D / 32;
   constexpr int TILE = BN * D * 2;
-  __shared__ __attribute__((aligned(16))) char smem[4 * TILE];
-  lds_char* lds = (lds_char*)smem;
+  __shared__ __attribute__((aligned(16))) char buf0[2 * TILE];
+  __shared__ __attribute__((aligned(16))) char buf1[2 * TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5;
   const int x = blockIdx.x;
@@ -254,6 +285,13 @@ __global__ __launch_bounds__(256) void dq_kernel(const void* __restrict__ qp, co
   const auto rdo = make_rsrc((const char*)dop + head, bytes);
   const auto rdq = make_rsrc((char*)dqp + head, bytes);
 
+  const int kend = CAUSAL ? min(N, q0 + BM) : N;
+  const int nt = (kend + BN - 1) / BN;
+  DmaTile<BN, D, NW> dma;
+  dma.init(w, lane);
+  dma.issue(rk, (lds_char*)buf0, 0, w);
+  dma.issue(rv, (lds_char*)buf0 + TILE, 0, w);
+
   const int wq0 = q0 + 32 * w;
   const int qrow = wq0 + (lane & 31);
   u32x4 qf[NKK], dof[NKK];
@@ -264,33 +302,16 @@ __global__ __launch_bounds__(256) void dq_kernel(const void* __restrict__ qp, co
   }
   const float l2 = qrow < N ? lsep[(size_t)bh * N + qrow] * kLog2e : INFINITY;
   const float dd = qrow < N ? deltap[(size_t)bh * N + qrow] : 0.f;
-
-  const int kend = CAUSAL ? min(N, q0 + BM) : N;
-  const int nt = (kend + BN - 1) / BN;
-  Stage<BN, D, NT> sk, sv;
-  sk.load(rk, 0, tid);
-  sv.load(rv, 0, tid);
-
   f32x16 dqa[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) dqa[b] = (f32x16){};
 
-  for (int t = 0; t < nt; ++t) {
-    lds_char* kt = lds + (t & 1) * 2 * TILE;
-    lds_char* vt = kt + TILE;
-    sk.store(kt, tid);
-    sv.store(vt, tid);
-    __syncthreads();
-    if (t + 1 < nt) {
-      sk.load(rk, (t + 1) * BN, tid);
-      sv.load(rv, (t + 1) * BN, tid);
-    }
-    const int j0 = t * BN;
-    if (CAUSAL && j0 > wq0 + 31) continue;  // every key of the tile follows every query of the wave
-    if ((j0 + BN > N) || (CAUSAL && j0 + BN - 1 > wq0))
-      dq_tile<T, D, CAUSAL, true>(kt, vt, qf, dof, dqa, l2, dd, j0, qrow, N, c, lane);
-    else
-      dq_tile<T, D, CAUSAL, false>(kt, vt, qf, dof, dqa, l2, dd, j0, qrow, N, c, lane);
+  for (int t = 0; t < nt; t += 2) {
+    dq_step<T, D, CAUSAL>((lds_char*)buf0, (lds_char*)buf1, t, nt, dma, rk, rv, qf, dof, dqa, l2, dd, wq0, qrow, N, c,
+                          w, lane);
+    if (t + 1 < nt)
+      dq_step<T, D, CAUSAL>((lds_char*)buf1, (lds_char*)buf0, t + 1, nt, dma, rk, rv, qf, dof, dqa, l2, dd, wq0, qrow,
+                            N, c, w, lane);
   }
   store_rows<T, D>(rdq, qrow, dqa, scale, lane);
 }

@@ -142,31 +142,58 @@ __device__ __forceinline__ u32x4 lds_cols_operand(const lds_char* tile, int kc, 
 }
 
 // ---------------------------------------------------------------------------
-// Global -> register -> LDS staging of a ROWS x D tile by NT threads.
+// Global -> LDS tile loads without registers (buffer_load_dwordx4 ... lds).
+// One instruction moves 64 x 16 bytes: lane l's 16 bytes land at LDS
+// base + 16 l, so a wave writes 1024 contiguous LDS bytes per instruction and
+// each lane picks the global chunk that belongs in its LDS slot under the
+// swizzle.  Lanes past the end of the head slice write zeros.  Completion is
+// tracked by vmcnt; readers wait for vmcnt(0) and then a barrier.
 // ---------------------------------------------------------------------------
-template <int ROWS, int D, int NT>
-struct Stage {
+// buffer_load ... lds of 16 (dma16) or 4 (dma4) bytes per lane.  The builtin
+// is emitted in the device pass only: when the host pass (which only needs
+// each kernel's launch stub) sees it, clang silently drops the launch stubs
+// of some kernel instantiations.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t src, lds_char* dst, uint32_t voffset) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, voffset, 0, 0, 0);
+#endif
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t src, lds_char* dst, uint32_t voffset) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void*)dst, 4, voffset, 0, 0, 0);
+#endif
+}
+
+template <int ROWS, int D, int NW>
+struct DmaTile {
   static constexpr int CPR = D / 8;
-  static constexpr int PER = ROWS * CPR / NT;
-  static_assert(ROWS * CPR % NT == 0, "tile must split evenly over the threads");
-  u32x4 r[PER];
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t src, int row0, int tid) {
+  static constexpr int SLOTS = ROWS * CPR;
+  static constexpr int PER = SLOTS / (64 * NW);  // instructions per wave per tile
+  static_assert(SLOTS % (64 * NW) == 0, "tile must split evenly over the waves");
+  uint32_t off[PER];  // per-lane byte offset of its chunk relative to the tile's first row
+  __device__ __forceinline__ void init(int w, int lane) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int c = tid + i * NT;
-      const int row = c / CPR, col = c % CPR;
-      r[i] = bload16(src, (uint32_t)(((row0 + row) * D + col * 8) * 2));
+      const int slot = (i * NW + w) * 64 + lane;
+      const int r = slot / CPR, p = slot % CPR;
+      off[i] = (uint32_t)((r * D + 8 * (p ^ Swz<D>::f(r))) * 2);
     }
   }
-  __device__ __forceinline__ void store(lds_char* tile, int tid) const {
+  // Enqueue the tile whose first row is row0 (the row offset is added per
+  // lane so that the out-of-range check sees the full offset).
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t src, lds_char* tile, int row0, int w) const {
+    const uint32_t base = (uint32_t)(row0 * D * 2);
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int c = tid + i * NT;
-      const int row = c / CPR, col = c % CPR;
-      *(u32x4*)(tile + Swz<D>::chunk(row, col)) = r[i];
-    }
+    for (int i = 0; i < PER; ++i) dma16(src, tile + (i * NW + w) * 1024, base + off[i]);
   }
 };
+
+// Wait for this wave's outstanding vector-memory operations (including LDS
+// DMA), then for every wave of the workgroup.
+__device__ __forceinline__ void dma_barrier() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
 
 // Value of x in lane l ^ 32, combined with x: returns {x_own, x_partner} as
 // the two halves of v_permlane32_swap (order depends on the lane half).

@@ -5,8 +5,9 @@
 // loop, grid split over the sequence).
 //
 // Workgroup: 4 waves; wave w owns queries q0 + 32w .. q0 + 32w + 31.
-// Per key tile of BN = 64 rows (K and V staged through swizzled LDS, double
-// buffered, the next tile's global loads in flight during this tile's math):
+// Per key tile of BN = 64 rows (K and V copied global -> LDS by buffer DMA into
+// a swizzled layout, double buffered, the next tile in flight during this
+// tile's math):
 //   S^T = K Q^T          MFMA, A = K rows from LDS, B = Q^T kept in registers;
 //                        lane l holds query l % 32 and 32 of the 64 keys
 //   mask                 only on tiles that cross the diagonal or the end of N
@@ -83,15 +84,39 @@ __device__ __forceinline__ void fwd_tile(const lds_char* kt, const lds_char* vt,
     for (int j = 0; j < 4; ++j) acc[b] = Elem<T>::mma(lds_cols_operand<D>(vt, j, 32 * b, lane), pf[j], acc[b]);
 }
 
+// One pipeline step: wait for tile t in `cur`, start the DMA of tile t + 1
+// into `nxt` (every wave is past its reads of `nxt`), then the math on `cur`.
 template <class T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void fwd_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
+__device__ __forceinline__ void fwd_step(lds_char* cur, lds_char* nxt, int t, int nt, const DmaTile<64, D, 4>& dma,
+                                         __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, const u32x4* qf,
+                                         f32x16* acc, float& mref, float& l, int wq0, int qrow, int N, float c, int w,
+                                         int lane) {
+  constexpr int BN = 64, TILE = BN * D * 2;
+  dma_barrier();
+  if (t + 1 < nt) {
+    dma.issue(rk, nxt, (t + 1) * BN, w);
+    dma.issue(rv, nxt + TILE, (t + 1) * BN, w);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const int j0 = t * BN;
+  if (CAUSAL && j0 > wq0 + 31) return;  // every key of the tile follows every query of the wave
+  if ((j0 + BN > N) || (CAUSAL && j0 + BN - 1 > wq0))
+    fwd_tile<T, D, CAUSAL, true>(cur, cur + TILE, qf, acc, mref, l, j0, qrow, N, c, lane);
+  else
+    fwd_tile<T, D, CAUSAL, false>(cur, cur + TILE, qf, acc, mref, l, j0, qrow, N, c, lane);
+}
+
+template <class T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void fwd_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
                                                   const void* __restrict__ vp, void* __restrict__ op,
                                                   float* __restrict__ lsep, int N, int BH, int nqb,
                                                   float c) {
-  constexpr int BM = 128, BN = 64, NT = 256, NKK = D / 16, NB = D / 32;
+  constexpr int BM = 128, BN = 64, NW = 4, NKK = D / 16, NB = D / 32;
   constexpr int TILE = BN * D * 2;
-  __shared__ __attribute__((aligned(16))) char smem[4 * TILE];
-  lds_char* lds = (lds_char*)smem;
+  // Two K/V buffers as separate objects, so that the compiler can tell the
+  // tile being read from the tile being filled by DMA.
+  __shared__ __attribute__((aligned(16))) char buf0[2 * TILE];
+  __shared__ __attribute__((aligned(16))) char buf1[2 * TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5;
   const int x = blockIdx.x;
@@ -105,17 +130,17 @@ __global__ __launch_bounds__(256) void fwd_kernel(const void* __restrict__ qp, c
   const auto rv = make_rsrc((const char*)vp + head, bytes);
   const auto ro = make_rsrc((char*)op + head, bytes);
 
+  const int kend = CAUSAL ? min(N, q0 + BM) : N;
+  const int nt = (kend + BN - 1) / BN;
+  DmaTile<BN, D, NW> dma;
+  dma.init(w, lane);
+  dma.issue(rk, (lds_char*)buf0, 0, w);
+  dma.issue(rv, (lds_char*)buf0 + TILE, 0, w);
+
   const int qrow = q0 + 32 * w + (lane & 31);  // this lane's query
   u32x4 qf[NKK];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) qf[kk] = bload16(rq, (uint32_t)((qrow * D + 16 * kk + 8 * h) * 2));
-
-  const int kend = CAUSAL ? min(N, q0 + BM) : N;
-  const int nt = (kend + BN - 1) / BN;
-
-  Stage<BN, D, NT> sk, sv;
-  sk.load(rk, 0, tid);
-  sv.load(rv, 0, tid);
 
   f32x16 acc[NB];
 #pragma unroll
@@ -123,23 +148,12 @@ __global__ __launch_bounds__(256) void fwd_kernel(const void* __restrict__ qp, c
   float mref = -INFINITY, l = 0.f;  // reference max (base 2) and this lane's part of the row sum
   const int wq0 = q0 + 32 * w;      // first query of this wave
 
-  for (int t = 0; t < nt; ++t) {
-    lds_char* kt = lds + (t & 1) * 2 * TILE;
-    lds_char* vt = kt + TILE;
-    sk.store(kt, tid);
-    sv.store(vt, tid);
-    __syncthreads();
-    if (t + 1 < nt) {
-      sk.load(rk, (t + 1) * BN, tid);
-      sv.load(rv, (t + 1) * BN, tid);
-    }
-    const int j0 = t * BN;
-    if (CAUSAL && j0 > wq0 + 31) continue;  // every key of the tile follows every query of the wave
-    const bool edge = (j0 + BN > N) || (CAUSAL && j0 + BN - 1 > wq0);
-    if (edge)
-      fwd_tile<T, D, CAUSAL, true>(kt, vt, qf, acc, mref, l, j0, qrow, N, c, lane);
-    else
-      fwd_tile<T, D, CAUSAL, false>(kt, vt, qf, acc, mref, l, j0, qrow, N, c, lane);
+  for (int t = 0; t < nt; t += 2) {
+    fwd_step<T, D, CAUSAL>((lds_char*)buf0, (lds_char*)buf1, t, nt, dma, rk, rv, qf, acc, mref, l, wq0, qrow, N, c,
+                           w, lane);
+    if (t + 1 < nt)
+      fwd_step<T, D, CAUSAL>((lds_char*)buf1, (lds_char*)buf0, t + 1, nt, dma, rk, rv, qf, acc, mref, l, wq0, qrow,
+                             N, c, w, lane);
   }
 
   const float lt = sum_with_partner(l);

@@ -152,3 +152,11 @@ def test_binding_rejects_host_tensors():
         binding.fa_fwd(q, q, q, q.clone(), lse, 0.125, False)
     with pytest.raises(ValueError):
         binding.fa_bwd_preprocess(q.float(), q.float(), lse)
+
+
+def test_every_kernel_launch_stub_is_defined():
+    # A host pass that drops a kernel's launch stub leaves an undefined
+    # symbol that only fails when the library is loaded.
+    out = subprocess.run(["nm", "-D", binding.LIB_PATH], capture_output=True, text=True).stdout
+    missing = [line for line in out.splitlines() if " U " in line and "device_stub" in line]
+    assert not missing, missing[:3]
