@@ -13,6 +13,11 @@
 
 #include <algorithm>
 
+// Tile configuration (compile-time; defaults chosen by measurement).
+#ifndef FA_BWD_STAGES
+#define FA_BWD_STAGES 2
+#endif
+
 namespace fa {
 
 // ---------------------------------------------------------------------------
@@ -42,12 +47,13 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const void* __restrict_
   }
 }
 
-// One query tile of the dK/dV kernel for one wave (MASK: the tile crosses
-// the causal diagonal of this wave's keys).
-template <class T, int D, bool MASK>
+// One query tile of the dK/dV kernel for one wave (`edge`: the tile crosses
+// the causal diagonal of this wave's keys).  One code path for every tile,
+// so the accumulator registers need no copies at merges.
+template <class T, int D>
 __device__ __forceinline__ void dkdv_tile(const lds_char* qt, const lds_char* dot, const float* st, const u32x4* kf,
-                                          const u32x4* vf, f32x16* dka, f32x16* dva, int i0, int krow, float c,
-                                          int lane) {
+                                          const u32x4* vf, f32x16* dka, f32x16* dva, bool edge, int i0, int krow,
+                                          float c, int lane) {
   constexpr int NKK = D / 16, NB = D / 32;
   const int h = lane >> 5;
   f32x16 s[2], dp[2];
@@ -72,7 +78,7 @@ __device__ __forceinline__ void dkdv_tile(const lds_char* qt, const lds_char* do
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * g + e;
         float x = s[a][r];
-        if constexpr (MASK) x = krow > i0 + qi + e ? -INFINITY : x;
+        if (edge) x = krow > i0 + qi + e ? -INFINITY : x;
         const float p = exp2_fast(__builtin_fmaf(x, c, -l2[e]));
         s[a][r] = p;
         dp[a][r] = p * (dp[a][r] - dd[e]);
@@ -93,44 +99,50 @@ __device__ __forceinline__ void dkdv_tile(const lds_char* qt, const lds_char* do
     }
 }
 
+constexpr int kBwdWaves = 4, kBwdTile = 64, kBwdStages = FA_BWD_STAGES;
+
 // Enqueue the DMA of query tile i0: Q rows, dO rows, then L and D (one
 // dword per lane, waves 0 and 1).  Rows past N load as zeros: their Q and
 // dO rows are zero, so they add nothing to dV (dO = 0) or to dK
 // (dS = P (0 - 0) = 0) whatever P is.
 template <int D>
-__device__ __forceinline__ void dkdv_issue(lds_char* b, int i0, const DmaTile<64, D, 4>& dma,
-                                           __amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rdo,
-                                           __amdgpu_buffer_rsrc_t rl, __amdgpu_buffer_rsrc_t rd, int w, int lane) {
-  constexpr int BMQ = 64, TILE = BMQ * D * 2;
+__device__ __forceinline__ void dkdv_issue(lds_char* b, int i0, const DmaTile<kBwdTile, D, kBwdWaves>& dma, Rsrc rq,
+                                           Rsrc rdo, Rsrc rl, Rsrc rd, int w, int lane) {
+  constexpr int TILE = kBwdTile * D * 2;
   dma.issue(rq, b, i0, w);
   dma.issue(rdo, b + TILE, i0, w);
-  if (w < 2) dma4(w == 0 ? rl : rd, b + 2 * TILE + w * BMQ * 4, (uint32_t)((i0 + lane) * 4));
+  if (w < 2) dma4(w == 0 ? rl : rd, b + 2 * TILE + w * kBwdTile * 4, (uint32_t)((i0 + lane) * 4));
 }
 
-template <class T, int D, bool CAUSAL>
-__device__ __forceinline__ void dkdv_step(lds_char* cur, lds_char* nxt, int t, int nt, int i_start,
-                                          const DmaTile<64, D, 4>& dma, __amdgpu_buffer_rsrc_t rq,
-                                          __amdgpu_buffer_rsrc_t rdo, __amdgpu_buffer_rsrc_t rl,
-                                          __amdgpu_buffer_rsrc_t rd, const u32x4* kf, const u32x4* vf, f32x16* dka,
-                                          f32x16* dva, int wk0, int krow, float c, int w, int lane) {
-  constexpr int BMQ = 64, TILE = BMQ * D * 2;
-  dma_barrier();
+// One ring step on query tile t, held in ring buffer IDX = t % S (a
+// compile-time index, so LDS operand addresses are register + immediate):
+// wait and barrier, DMA of tile t + S - 1, then the math.
+template <class T, int D, bool CAUSAL, int IDX>
+__device__ __forceinline__ void dkdv_step(lds_char* lds, int t, int nt, int i_start,
+                                          const DmaTile<kBwdTile, D, kBwdWaves>& dma, Rsrc rq, Rsrc rdo, Rsrc rl,
+                                          Rsrc rd, const u32x4* kf, const u32x4* vf, f32x16* dka, f32x16* dva,
+                                          int wk0, int krow, float c, int w, int lane) {
+  constexpr int S = kBwdStages, BMQ = kBwdTile, TILE = BMQ * D * 2, BUF = 2 * TILE + 2 * BMQ * 4;
+  constexpr int PT = 2 * DmaTile<kBwdTile, D, kBwdWaves>::PER;  // per tile; waves 0, 1 add an L or D dword
+  if (w < 2)
+    ring_wait<S, PT + 1>(t, nt);
+  else
+    ring_wait<S, PT>(t, nt);
   const int i0 = i_start + t * BMQ;
-  if (t + 1 < nt) dkdv_issue<D>(nxt, i0 + BMQ, dma, rq, rdo, rl, rd, w, lane);
+  if (t + S - 1 < nt) dkdv_issue<D>(lds + ((IDX + S - 1) % S) * BUF, i0 + (S - 1) * BMQ, dma, rq, rdo, rl, rd, w, lane);
   __builtin_amdgcn_sched_barrier(0);
   if (CAUSAL && i0 + BMQ - 1 < wk0) return;  // every query of the tile precedes every key of the wave
+  const lds_char* cur = lds + IDX * BUF;
   const float* st = (const float*)(cur + 2 * TILE);
-  if (CAUSAL && i0 < wk0 + 31)
-    dkdv_tile<T, D, true>(cur, cur + TILE, st, kf, vf, dka, dva, i0, krow, c, lane);
-  else
-    dkdv_tile<T, D, false>(cur, cur + TILE, st, kf, vf, dka, dva, i0, krow, c, lane);
+  dkdv_tile<T, D>(cur, cur + TILE, st, kf, vf, dka, dva, CAUSAL && i0 < wk0 + 31, i0, krow, c, lane);
 }
 
 // ---------------------------------------------------------------------------
 // dK, dV.  Workgroup = 128 keys of one head (wave w owns keys k0 + 32w ..
 // k0 + 32w + 31, with its K and V rows resident as MFMA B operands), looping
 // over query tiles of 64 rows: Q and dO tiles plus their L and D copied by
-// buffer DMA into swizzled LDS, double buffered.  Per tile and wave:
+// buffer DMA into swizzled LDS through a ring of S buffers (tiles t+1 ..
+// t+S-1 in flight during tile t).  Per tile and wave:
 //   S = Q K^T, dP = dO V^T          (lane = key, registers = queries)
 //   P = 2^(S c - L2), dS = P (dP - D)
 //   dV^T += dO^T P, dK^T += Q^T dS  (A operands by transposed LDS reads)
@@ -138,37 +150,38 @@ __device__ __forceinline__ void dkdv_step(lds_char* cur, lds_char* nxt, int t, i
 // tiles that cross the diagonal are masked.
 // ---------------------------------------------------------------------------
 template <class T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void dkdv_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
-                                                   const void* __restrict__ vp, const void* __restrict__ dop,
-                                                   const float* __restrict__ lsep, const float* __restrict__ deltap,
-                                                   void* __restrict__ dkp, void* __restrict__ dvp, int N, int BH,
-                                                   float c, float scale) {
-  constexpr int BNK = 128, BMQ = 64, NW = 4, NKK = D / 16, NB = D / 32;
+__global__ __launch_bounds__(64 * kBwdWaves) void dkdv_kernel(
+    const void* __restrict__ qp, const void* __restrict__ kp, const void* __restrict__ vp,
+    const void* __restrict__ dop, const float* __restrict__ lsep, const float* __restrict__ deltap,
+    void* __restrict__ dkp, void* __restrict__ dvp, int N, int BH, float c, float scale) {
+  constexpr int NW = kBwdWaves, BNK = 32 * NW, BMQ = kBwdTile, NKK = D / 16, NB = D / 32;
   constexpr int TILE = BMQ * D * 2;
+  constexpr int S = kBwdStages;
   constexpr int BUF = 2 * TILE + 2 * BMQ * 4;  // Q tile, dO tile, L[64], D[64]
-  __shared__ __attribute__((aligned(16))) char buf0[BUF];
-  __shared__ __attribute__((aligned(16))) char buf1[BUF];
+  __shared__ __attribute__((aligned(16))) char smem[S * BUF];
+  lds_char* const lds = (lds_char*)smem;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, known uniform
   const int x = blockIdx.x;
   const int kb = x / BH, bh = x % BH;
   const int k0 = kb * BNK;
   const size_t head = (size_t)bh * N * D * 2;
   const uint32_t bytes = (uint32_t)N * D * 2;
-  const auto rq = make_rsrc((const char*)qp + head, bytes);
   const auto rk = make_rsrc((const char*)kp + head, bytes);
   const auto rv = make_rsrc((const char*)vp + head, bytes);
-  const auto rdo = make_rsrc((const char*)dop + head, bytes);
   const auto rdk = make_rsrc((char*)dkp + head, bytes);
   const auto rdv = make_rsrc((char*)dvp + head, bytes);
-  const auto rl = make_rsrc(lsep + (size_t)bh * N, (uint32_t)N * 4);
-  const auto rd = make_rsrc(deltap + (size_t)bh * N, (uint32_t)N * 4);
+  const Rsrc rq = make_rsrc_words((const char*)qp + head, bytes);
+  const Rsrc rdo = make_rsrc_words((const char*)dop + head, bytes);
+  const Rsrc rl = make_rsrc_words(lsep + (size_t)bh * N, (uint32_t)N * 4);
+  const Rsrc rd = make_rsrc_words(deltap + (size_t)bh * N, (uint32_t)N * 4);
 
   const int i_start = CAUSAL ? k0 : 0;
   const int nt = (N - i_start + BMQ - 1) / BMQ;
   DmaTile<BMQ, D, NW> dma;
   dma.init(w, lane);
-  dkdv_issue<D>((lds_char*)buf0, i_start, dma, rq, rdo, rl, rd, w, lane);
+  dkdv_issue<D>(lds, i_start, dma, rq, rdo, rl, rd, w, lane);
 
   const int wk0 = k0 + 32 * w;
   const int krow = wk0 + (lane & 31);
@@ -178,26 +191,42 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const void* __restrict__ qp, 
     kf[kk] = bload16(rk, (uint32_t)((krow * D + 16 * kk + 8 * h) * 2));
     vf[kk] = bload16(rv, (uint32_t)((krow * D + 16 * kk + 8 * h) * 2));
   }
+  // K and V (and with them tile 0) land before the ring starts.
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    land(kf[kk]);
+    land(vf[kk]);
+  }
+  if (S > 2 && nt > 1) dkdv_issue<D>(lds + (1 % S) * BUF, i_start + BMQ, dma, rq, rdo, rl, rd, w, lane);
+  if (S > 3 && nt > 2) dkdv_issue<D>(lds + (2 % S) * BUF, i_start + 2 * BMQ, dma, rq, rdo, rl, rd, w, lane);
   f32x16 dka[NB], dva[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) dka[b] = dva[b] = (f32x16){};
 
-  for (int t = 0; t < nt; t += 2) {
-    dkdv_step<T, D, CAUSAL>((lds_char*)buf0, (lds_char*)buf1, t, nt, i_start, dma, rq, rdo, rl, rd, kf, vf, dka, dva,
-                            wk0, krow, c, w, lane);
+  for (int t = 0; t < nt; t += S) {
+    dkdv_step<T, D, CAUSAL, 0>(lds, t, nt, i_start, dma, rq, rdo, rl, rd, kf, vf, dka, dva, wk0, krow, c, w, lane);
     if (t + 1 < nt)
-      dkdv_step<T, D, CAUSAL>((lds_char*)buf1, (lds_char*)buf0, t + 1, nt, i_start, dma, rq, rdo, rl, rd, kf, vf, dka,
-                              dva, wk0, krow, c, w, lane);
+      dkdv_step<T, D, CAUSAL, 1>(lds, t + 1, nt, i_start, dma, rq, rdo, rl, rd, kf, vf, dka, dva, wk0, krow, c, w,
+                                 lane);
+    if constexpr (S > 2)
+      if (t + 2 < nt)
+        dkdv_step<T, D, CAUSAL, 2 % S>(lds, t + 2, nt, i_start, dma, rq, rdo, rl, rd, kf, vf, dka, dva, wk0, krow, c,
+                                       w, lane);
+    if constexpr (S > 3)
+      if (t + 3 < nt)
+        dkdv_step<T, D, CAUSAL, 3 % S>(lds, t + 3, nt, i_start, dma, rq, rdo, rl, rd, kf, vf, dka, dva, wk0, krow, c,
+                                       w, lane);
   }
   store_rows<T, D>(rdk, krow, dka, scale, lane);
   store_rows<T, D>(rdv, krow, dva, 1.0f, lane);
 }
 
-// One key tile of the dQ kernel for one wave (MASK: the tile crosses the
-// causal diagonal of this wave's queries or the end of N).
-template <class T, int D, bool CAUSAL, bool MASK>
+// One key tile of the dQ kernel for one wave (`edge`: the tile crosses the
+// causal diagonal of this wave's queries or the end of N).  One code path
+// for every tile, so the accumulator registers need no copies at merges.
+template <class T, int D, bool CAUSAL>
 __device__ __forceinline__ void dq_tile(const lds_char* kt, const lds_char* vt, const u32x4* qf, const u32x4* dof,
-                                        f32x16* dqa, float l2, float dd, int j0, int qrow, int N, float c,
+                                        f32x16* dqa, float l2, float dd, bool edge, int j0, int qrow, int N, float c,
                                         int lane) {
   constexpr int NKK = D / 16, NB = D / 32;
   const int h = lane >> 5;
@@ -217,7 +246,7 @@ __device__ __forceinline__ void dq_tile(const lds_char* kt, const lds_char* vt, 
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float x = s[a][r];
-      if constexpr (MASK) {
+      if (edge) {
         const int key = j0 + 32 * a + 8 * (r >> 2) + 4 * h + (r & 3);
         if (key >= N || (CAUSAL && key > qrow)) x = -INFINITY;
       }
@@ -233,46 +262,54 @@ __device__ __forceinline__ void dq_tile(const lds_char* kt, const lds_char* vt, 
     for (int j = 0; j < 4; ++j) dqa[b] = Elem<T>::mma(lds_cols_operand<D>(kt, j, 32 * b, lane), dsf[j], dqa[b]);
 }
 
-template <class T, int D, bool CAUSAL>
-__device__ __forceinline__ void dq_step(lds_char* cur, lds_char* nxt, int t, int nt, const DmaTile<64, D, 4>& dma,
-                                        __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, const u32x4* qf,
-                                        const u32x4* dof, f32x16* dqa, float l2, float dd, int wq0, int qrow, int N,
-                                        float c, int w, int lane) {
-  constexpr int BN = 64, TILE = BN * D * 2;
-  dma_barrier();
-  if (t + 1 < nt) {
-    dma.issue(rk, nxt, (t + 1) * BN, w);
-    dma.issue(rv, nxt + TILE, (t + 1) * BN, w);
-  }
+// DMA of key tile t (K then V) into ring buffer IDX.
+template <int D, int IDX>
+__device__ __forceinline__ void dq_issue(lds_char* lds, int t, const DmaTile<kBwdTile, D, kBwdWaves>& dma, Rsrc rk,
+                                         Rsrc rv, int w) {
+  constexpr int TILE = kBwdTile * D * 2;
+  lds_char* b = lds + IDX * 2 * TILE;
+  dma.issue(rk, b, t * kBwdTile, w);
+  dma.issue(rv, b + TILE, t * kBwdTile, w);
+}
+
+// One ring step on key tile t, held in ring buffer IDX = t % S.
+template <class T, int D, bool CAUSAL, int IDX>
+__device__ __forceinline__ void dq_step(lds_char* lds, int t, int nt, const DmaTile<kBwdTile, D, kBwdWaves>& dma,
+                                        Rsrc rk, Rsrc rv, const u32x4* qf, const u32x4* dof, f32x16* dqa, float l2,
+                                        float dd, int wq0, int qrow, int N, float c, int w, int lane) {
+  constexpr int S = kBwdStages, BN = kBwdTile, TILE = BN * D * 2;
+  ring_wait<S, 2 * DmaTile<kBwdTile, D, kBwdWaves>::PER>(t, nt);
+  if (t + S - 1 < nt) dq_issue<D, (IDX + S - 1) % S>(lds, t + S - 1, dma, rk, rv, w);
   __builtin_amdgcn_sched_barrier(0);
   const int j0 = t * BN;
   if (CAUSAL && j0 > wq0 + 31) return;  // every key of the tile follows every query of the wave
-  if ((j0 + BN > N) || (CAUSAL && j0 + BN - 1 > wq0))
-    dq_tile<T, D, CAUSAL, true>(cur, cur + TILE, qf, dof, dqa, l2, dd, j0, qrow, N, c, lane);
-  else
-    dq_tile<T, D, CAUSAL, false>(cur, cur + TILE, qf, dof, dqa, l2, dd, j0, qrow, N, c, lane);
+  const lds_char* cur = lds + IDX * 2 * TILE;
+  const bool edge = (j0 + BN > N) || (CAUSAL && j0 + BN - 1 > wq0);
+  dq_tile<T, D, CAUSAL>(cur, cur + TILE, qf, dof, dqa, l2, dd, edge, j0, qrow, N, c, lane);
 }
 
 // ---------------------------------------------------------------------------
 // dQ.  Workgroup = 128 queries of one head (wave w owns 32, with its Q and dO
 // rows resident as MFMA B operands and its L and D in registers), looping
-// over key tiles of 64 rows (K and V copied by buffer DMA into swizzled LDS):
+// over key tiles of 64 rows (K and V copied by buffer DMA into swizzled LDS
+// through a ring of S buffers):
 //   S^T = K Q^T, dP^T = V dO^T   (lane = query, registers = keys)
 //   P = 2^(S c - L2), dS = P (dP - D)
 //   dQ^T += K^T dS^T             (A operand by transposed LDS reads)
 // ---------------------------------------------------------------------------
 template <class T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void dq_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
-                                                 const void* __restrict__ vp, const void* __restrict__ dop,
-                                                 const float* __restrict__ lsep, const float* __restrict__ deltap,
-                                                 void* __restrict__ dqp, int N, int BH, int nqb, float c,
-                                                 float scale) {
-  constexpr int BM = 128, BN = 64, NW = 4, NKK = D / 16, NB = D / 32;
-  constexpr int TILE = BN * D * 2;
-  __shared__ __attribute__((aligned(16))) char buf0[2 * TILE];
-  __shared__ __attribute__((aligned(16))) char buf1[2 * TILE];
+__global__ __launch_bounds__(64 * kBwdWaves, 2) void dq_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
+                                                            const void* __restrict__ vp, const void* __restrict__ dop,
+                                                            const float* __restrict__ lsep,
+                                                            const float* __restrict__ deltap, void* __restrict__ dqp,
+                                                            int N, int BH, int nqb, float c, float scale) {
+  constexpr int NW = kBwdWaves, BM = 32 * NW, BN = kBwdTile, NKK = D / 16, NB = D / 32;
+  constexpr int S = kBwdStages, TILE = BN * D * 2;
+  __shared__ __attribute__((aligned(16))) char smem[S * 2 * TILE];
+  lds_char* const lds = (lds_char*)smem;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, known uniform
   const int x = blockIdx.x;
   const int qb = CAUSAL ? (nqb - 1 - x / BH) : (x / BH);
   const int bh = x % BH;
@@ -280,17 +317,16 @@ __global__ __launch_bounds__(256) void dq_kernel(const void* __restrict__ qp, co
   const size_t head = (size_t)bh * N * D * 2;
   const uint32_t bytes = (uint32_t)N * D * 2;
   const auto rq = make_rsrc((const char*)qp + head, bytes);
-  const auto rk = make_rsrc((const char*)kp + head, bytes);
-  const auto rv = make_rsrc((const char*)vp + head, bytes);
   const auto rdo = make_rsrc((const char*)dop + head, bytes);
   const auto rdq = make_rsrc((char*)dqp + head, bytes);
+  const Rsrc rk = make_rsrc_words((const char*)kp + head, bytes);
+  const Rsrc rv = make_rsrc_words((const char*)vp + head, bytes);
 
   const int kend = CAUSAL ? min(N, q0 + BM) : N;
   const int nt = (kend + BN - 1) / BN;
   DmaTile<BN, D, NW> dma;
   dma.init(w, lane);
-  dma.issue(rk, (lds_char*)buf0, 0, w);
-  dma.issue(rv, (lds_char*)buf0 + TILE, 0, w);
+  dq_issue<D, 0>(lds, 0, dma, rk, rv, w);
 
   const int wq0 = q0 + 32 * w;
   const int qrow = wq0 + (lane & 31);
@@ -302,16 +338,29 @@ __global__ __launch_bounds__(256) void dq_kernel(const void* __restrict__ qp, co
   }
   const float l2 = qrow < N ? lsep[(size_t)bh * N + qrow] * kLog2e : INFINITY;
   const float dd = qrow < N ? deltap[(size_t)bh * N + qrow] : 0.f;
+  // Q, dO, L, D (and with them tile 0) land before the ring starts.
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    land(qf[kk]);
+    land(dof[kk]);
+  }
+  land(l2);
+  land(dd);
+  if (S > 2 && nt > 1) dq_issue<D, 1 % S>(lds, 1, dma, rk, rv, w);
+  if (S > 3 && nt > 2) dq_issue<D, 2 % S>(lds, 2, dma, rk, rv, w);
   f32x16 dqa[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) dqa[b] = (f32x16){};
 
-  for (int t = 0; t < nt; t += 2) {
-    dq_step<T, D, CAUSAL>((lds_char*)buf0, (lds_char*)buf1, t, nt, dma, rk, rv, qf, dof, dqa, l2, dd, wq0, qrow, N, c,
-                          w, lane);
-    if (t + 1 < nt)
-      dq_step<T, D, CAUSAL>((lds_char*)buf1, (lds_char*)buf0, t + 1, nt, dma, rk, rv, qf, dof, dqa, l2, dd, wq0, qrow,
-                            N, c, w, lane);
+  for (int t = 0; t < nt; t += S) {
+    dq_step<T, D, CAUSAL, 0>(lds, t, nt, dma, rk, rv, qf, dof, dqa, l2, dd, wq0, qrow, N, c, w, lane);
+    if (t + 1 < nt) dq_step<T, D, CAUSAL, 1>(lds, t + 1, nt, dma, rk, rv, qf, dof, dqa, l2, dd, wq0, qrow, N, c, w, lane);
+    if constexpr (S > 2)
+      if (t + 2 < nt)
+        dq_step<T, D, CAUSAL, 2 % S>(lds, t + 2, nt, dma, rk, rv, qf, dof, dqa, l2, dd, wq0, qrow, N, c, w, lane);
+    if constexpr (S > 3)
+      if (t + 3 < nt)
+        dq_step<T, D, CAUSAL, 3 % S>(lds, t + 3, nt, dma, rk, rv, qf, dof, dqa, l2, dd, wq0, qrow, N, c, w, lane);
   }
   store_rows<T, D>(rdq, qrow, dqa, scale, lane);
 }

@@ -142,57 +142,139 @@ __device__ __forceinline__ u32x4 lds_cols_operand(const lds_char* tile, int kc, 
 }
 
 // ---------------------------------------------------------------------------
-// Global -> LDS tile loads without registers (buffer_load_dwordx4 ... lds).
-// One instruction moves 64 x 16 bytes: lane l's 16 bytes land at LDS
-// base + 16 l, so a wave writes 1024 contiguous LDS bytes per instruction and
-// each lane picks the global chunk that belongs in its LDS slot under the
-// swizzle.  Lanes past the end of the head slice write zeros.  Completion is
-// tracked by vmcnt; readers wait for vmcnt(0) and then a barrier.
+// Global -> LDS copies without registers: buffer_load_dword{,x4} ... lds.  One
+// instruction moves 64 lanes x 4 or 16 bytes; lane l's bytes land at LDS
+// M0 + l * size, so a wave fills a contiguous LDS range and each lane chooses
+// the global chunk that belongs in its slot.  Lanes past num_records write
+// zeros.  The loads are issued from inline assembly on purpose: the compiler
+// then does not track them, and all waiting for them is explicit (counted
+// vmcnt waits before the workgroup barrier of a multi-buffer ring) instead of
+// the compiler's conservative vmcnt(0) before every LDS read, which would wait
+// for the prefetch of later tiles too.  Kernels must therefore have no
+// compiler-tracked vector-memory load pending inside the ring loop.
 // ---------------------------------------------------------------------------
-// buffer_load ... lds of 16 (dma16) or 4 (dma4) bytes per lane.  The builtin
-// is emitted in the device pass only: when the host pass (which only needs
-// each kernel's launch stub) sees it, clang silently drops the launch stubs
-// of some kernel instantiations.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t src, lds_char* dst, uint32_t voffset) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, voffset, 0, 0, 0);
-#endif
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+struct Rsrc {
+  i32x4 v;  // buffer resource words: base lo, base hi | stride 0, num_records, format
+};
+__device__ __forceinline__ Rsrc make_rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  Rsrc r;
+  r.v = (i32x4){(int)__builtin_amdgcn_readfirstlane((uint32_t)a),
+                (int)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu),
+                (int)__builtin_amdgcn_readfirstlane(bytes), (int)kRsrcWord3};
+  return r;
 }
-__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t src, lds_char* dst, uint32_t voffset) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void*)dst, 4, voffset, 0, 0, 0);
-#endif
+// M0 is saved and restored around each copy; one wait state separates the
+// M0 write from the load that reads it.
+__device__ __forceinline__ void dma16(Rsrc src, lds_char* dst, uint32_t voffset) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m0), "v"(voffset), "s"(src.v)
+      : "memory");
+}
+__device__ __forceinline__ void dma4(Rsrc src, lds_char* dst, uint32_t voffset) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m0), "v"(voffset), "s"(src.v)
+      : "memory");
+}
+
+// Force a value loaded from memory to have landed (the compiler waits for its
+// load before this point); used to drain compiler-tracked loads before a
+// DMA ring loop.
+template <class V>
+__device__ __forceinline__ void land(const V& v) {
+  asm volatile("" ::"v"(v));
 }
 
 template <int ROWS, int D, int NW>
 struct DmaTile {
   static constexpr int CPR = D / 8;
   static constexpr int SLOTS = ROWS * CPR;
-  static constexpr int PER = SLOTS / (64 * NW);  // instructions per wave per tile
-  static_assert(SLOTS % (64 * NW) == 0, "tile must split evenly over the waves");
+  static constexpr int NI = SLOTS / 64;              // wave-instructions per tile
+  static constexpr int PER = (NI + NW - 1) / NW;     // per wave (waves past NI issue fewer)
+  static_assert(SLOTS % 64 == 0, "tile must be a whole number of 1 KiB DMA instructions");
+  // Every wave issues either PER or no instructions per tile, so a counted
+  // vmcnt wait based on PER is exact for the waves that issue any.
+  static_assert(NI % NW == 0 || NI < NW, "uneven DMA split");
   uint32_t off[PER];  // per-lane byte offset of its chunk relative to the tile's first row
   __device__ __forceinline__ void init(int w, int lane) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int slot = (i * NW + w) * 64 + lane;
-      const int r = slot / CPR, p = slot % CPR;
+      const int r = (slot / CPR) % ROWS, p = slot % CPR;
       off[i] = (uint32_t)((r * D + 8 * (p ^ Swz<D>::f(r))) * 2);
     }
   }
   // Enqueue the tile whose first row is row0 (the row offset is added per
   // lane so that the out-of-range check sees the full offset).
-  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t src, lds_char* tile, int row0, int w) const {
+  __device__ __forceinline__ void issue(Rsrc src, lds_char* tile, int row0, int w) const {
     const uint32_t base = (uint32_t)(row0 * D * 2);
 #pragma unroll
-    for (int i = 0; i < PER; ++i) dma16(src, tile + (i * NW + w) * 1024, base + off[i]);
+    for (int i = 0; i < PER; ++i)
+      if (i * NW + w < NI) dma16(src, tile + (i * NW + w) * 1024, base + off[i]);
   }
 };
 
-// Wait for this wave's outstanding vector-memory operations (including LDS
-// DMA), then for every wave of the workgroup.
-__device__ __forceinline__ void dma_barrier() {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+// s_waitcnt vmcnt(N) lgkmcnt(0), expcnt left alone (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt out of range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// Workgroup barrier for the DMA ring: this wave's DMA instructions older than
+// its last N have landed in LDS and its LDS reads are done, then every wave
+// arrives.  Unlike __syncthreads() there is no memory fence, which would wait
+// for all outstanding DMA (vmcnt(0)) and defeat the ring.  The empty asm
+// statements keep the compiler from moving LDS accesses across the barrier.
+template <int N>
+__device__ __forceinline__ void dma_wait_barrier() {
+  asm volatile("" ::: "memory");
+  wait_vmcnt_lgkm0<N>();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Ring of S LDS buffers fed by DMA: before working on tile t a wave waits
+// until at most its DMA instructions for tiles t+1 .. t+S-2 are in flight
+// (PT instructions per tile), then the workgroup barrier.  After it, tile t
+// is in LDS for every wave and every wave is done with tile t - 1, whose
+// buffer can receive tile t + S - 1.
+template <int S, int PT>
+__device__ __forceinline__ void ring_wait(int t, int nt) {
+  static_assert(S >= 2 && S <= 4, "ring depth");
+  if constexpr (S == 2) {
+    dma_wait_barrier<0>();
+  } else if constexpr (S == 3) {
+    if (t + 1 < nt)
+      dma_wait_barrier<PT>();
+    else
+      dma_wait_barrier<0>();
+  } else {
+    if (t + 2 < nt)
+      dma_wait_barrier<2 * PT>();
+    else if (t + 1 < nt)
+      dma_wait_barrier<PT>();
+    else
+      dma_wait_barrier<0>();
+  }
 }
 
 // Value of x in lane l ^ 32, combined with x: returns {x_own, x_partner} as

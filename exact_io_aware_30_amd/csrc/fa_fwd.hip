@@ -4,23 +4,41 @@
 // queries in the outer loop, accumulator in registers, one divide after the
 // loop, grid split over the sequence).
 //
-// Workgroup: 4 waves; wave w owns queries q0 + 32w .. q0 + 32w + 31.
-// Per key tile of BN = 64 rows (K and V copied global -> LDS by buffer DMA into
-// a swizzled layout, double buffered, the next tile in flight during this
-// tile's math):
+// Workgroup: NW waves; wave w owns queries q0 + 32w .. q0 + 32w + 31.
+// Per key tile of BN = 32 NA rows (K and V copied global -> LDS by buffer DMA
+// into a swizzled layout, through a ring of S buffers, so tiles t+1 .. t+S-1
+// are in flight during tile t's math):
 //   S^T = K Q^T          MFMA, A = K rows from LDS, B = Q^T kept in registers;
-//                        lane l holds query l % 32 and 32 of the 64 keys
+//                        lane l holds query l % 32 and half of the tile's keys
 //   mask                 only on tiles that cross the diagonal or the end of N
-//   m_new = max(m, rowmax S)     in-lane max, then one v_permlane32_swap
-//   p = 2^(S c - m_new c), alpha = 2^((m - m_new) c), c = scale * log2(e)
-//   l = alpha l + rowsum p;  acc = alpha acc
+//   row max              in-lane max, then one v_permlane32_swap
+//   p = 2^(S c - ref), c = scale * log2(e); l += rowsum p
 //   O^T += V^T P^T       MFMA, A = V^T by transposed LDS reads, B = P^T
 //                        converted from the S^T registers in place
-// After the last tile: O = acc / l, L = (m c + log2 l) ln 2.
+// The reference ref (a running row maximum in base-2 units) moves only when a
+// row maximum exceeds it by more than 2^8; then l and acc are rescaled by
+// alpha = 2^(ref_old - ref_new).  After the last tile: O = acc / l and
+// L = (ref + log2 l) ln 2.
 #include "fa_device.h"
 #include "fa_launch.h"
 
+// Tile configuration (compile-time; defaults chosen by measurement).
+#ifndef FA_FWD_WAVES
+#define FA_FWD_WAVES 8
+#endif
+#ifndef FA_FWD_STAGES
+#define FA_FWD_STAGES 3
+#endif
+#ifndef FA_FWD_KEYBLOCKS
+#define FA_FWD_KEYBLOCKS 2
+#endif
+
 namespace fa {
+
+constexpr int kFwdWaves = FA_FWD_WAVES;    // waves per workgroup (32 query rows each)
+constexpr int kFwdStages = FA_FWD_STAGES;  // LDS ring depth
+constexpr int kFwdNA = FA_FWD_KEYBLOCKS;   // key tile = 32 * kFwdNA rows
+constexpr int kFwdBN = 32 * kFwdNA;
 
 // Rescale threshold in base-2 units: the reference maximum used for the
 // exponentials is moved only when a row's maximum exceeds it by more than
@@ -29,22 +47,25 @@ namespace fa {
 // reference, so the result is the same up to rounding.
 constexpr float kRescaleSlack = 8.0f;
 
-// One key tile for one wave: S^T, optional mask, online-softmax update, PV.
-template <class T, int D, bool CAUSAL, bool MASK>
+// One key tile for one wave: S^T, mask (only when `edge`: the tile crosses
+// the diagonal or the end of N), online-softmax update, PV.  One code path
+// for every tile, so the accumulator registers need no copies at merges.
+template <class T, int D, bool CAUSAL>
 __device__ __forceinline__ void fwd_tile(const lds_char* kt, const lds_char* vt, const u32x4* qf, f32x16* acc,
-                                         float& mref, float& l, int j0, int qrow, int N, float c, int lane) {
-  constexpr int NKK = D / 16, NB = D / 32;
+                                         float& mref, float& l, bool edge, int j0, int qrow, int N, float c,
+                                         int lane) {
+  constexpr int NKK = D / 16, NB = D / 32, NA = kFwdNA;
   const int h = lane >> 5;
-  f32x16 s[2];
+  f32x16 s[NA];
 #pragma unroll
-  for (int a = 0; a < 2; ++a) {
+  for (int a = 0; a < NA; ++a) {
     s[a] = (f32x16){};
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) s[a] = Elem<T>::mma(lds_rows_operand<D>(kt, 32 * a, kk, lane), qf[kk], s[a]);
   }
-  if constexpr (MASK) {
+  if (edge) {
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < NA; ++a)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = j0 + 32 * a + 8 * (r >> 2) + 4 * h + (r & 3);
@@ -53,7 +74,7 @@ __device__ __forceinline__ void fwd_tile(const lds_char* kt, const lds_char* vt,
   }
   float mx = s[0][0];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < NA; ++a)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[a][r]);
   const float mxc = max_with_partner(mx) * c;  // row max in base-2 units
@@ -67,7 +88,7 @@ __device__ __forceinline__ void fwd_tile(const lds_char* kt, const lds_char* vt,
   }
   float rs = 0.f;
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < NA; ++a)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float p = exp2_fast(__builtin_fmaf(s[a][r], c, -mref));
@@ -75,50 +96,59 @@ __device__ __forceinline__ void fwd_tile(const lds_char* kt, const lds_char* vt,
       rs += p;
     }
   l += rs;
-  u32x4 pf[4];
+  u32x4 pf[2 * NA];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) pf[j] = pack8<T>(s[j >> 1], j & 1);
+  for (int j = 0; j < 2 * NA; ++j) pf[j] = pack8<T>(s[j >> 1], j & 1);
 #pragma unroll
   for (int b = 0; b < NB; ++b)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[b] = Elem<T>::mma(lds_cols_operand<D>(vt, j, 32 * b, lane), pf[j], acc[b]);
+    for (int j = 0; j < 2 * NA; ++j)
+      acc[b] = Elem<T>::mma(lds_cols_operand<D>(vt, j, 32 * b, lane), pf[j], acc[b]);
 }
 
-// One pipeline step: wait for tile t in `cur`, start the DMA of tile t + 1
-// into `nxt` (every wave is past its reads of `nxt`), then the math on `cur`.
-template <class T, int D, bool CAUSAL>
-__device__ __forceinline__ void fwd_step(lds_char* cur, lds_char* nxt, int t, int nt, const DmaTile<64, D, 4>& dma,
-                                         __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, const u32x4* qf,
-                                         f32x16* acc, float& mref, float& l, int wq0, int qrow, int N, float c, int w,
-                                         int lane) {
-  constexpr int BN = 64, TILE = BN * D * 2;
-  dma_barrier();
-  if (t + 1 < nt) {
-    dma.issue(rk, nxt, (t + 1) * BN, w);
-    dma.issue(rv, nxt + TILE, (t + 1) * BN, w);
-  }
+// DMA of key tile t (K then V) into ring buffer IDX.
+template <int D, int IDX>
+__device__ __forceinline__ void fwd_issue(lds_char* lds, int t, const DmaTile<kFwdBN, D, kFwdWaves>& dma, Rsrc rk,
+                                          Rsrc rv, int w) {
+  constexpr int TILE = kFwdBN * D * 2;
+  lds_char* b = lds + IDX * 2 * TILE;
+  dma.issue(rk, b, t * kFwdBN, w);
+  dma.issue(rv, b + TILE, t * kFwdBN, w);
+}
+
+// Ring step on tile t, which sits in buffer IDX = t % S (a compile-time
+// index, so that every LDS operand address is a register plus an immediate):
+// wait and barrier, DMA of tile t + S - 1 into the buffer tile t - 1 used,
+// then the math.
+template <class T, int D, bool CAUSAL, int IDX>
+__device__ __forceinline__ void fwd_step(lds_char* lds, int t, int nt, const DmaTile<kFwdBN, D, kFwdWaves>& dma,
+                                         Rsrc rk, Rsrc rv, const u32x4* qf, f32x16* acc, float& mref, float& l,
+                                         int wq0, int qrow, int N, float c, int w, int lane) {
+  constexpr int S = kFwdStages, BN = kFwdBN, TILE = BN * D * 2;
+  ring_wait<S, 2 * DmaTile<kFwdBN, D, kFwdWaves>::PER>(t, nt);
+  if (t + S - 1 < nt) fwd_issue<D, (IDX + S - 1) % S>(lds, t + S - 1, dma, rk, rv, w);
   __builtin_amdgcn_sched_barrier(0);
   const int j0 = t * BN;
   if (CAUSAL && j0 > wq0 + 31) return;  // every key of the tile follows every query of the wave
-  if ((j0 + BN > N) || (CAUSAL && j0 + BN - 1 > wq0))
-    fwd_tile<T, D, CAUSAL, true>(cur, cur + TILE, qf, acc, mref, l, j0, qrow, N, c, lane);
-  else
-    fwd_tile<T, D, CAUSAL, false>(cur, cur + TILE, qf, acc, mref, l, j0, qrow, N, c, lane);
+  const lds_char* cur = lds + IDX * 2 * TILE;
+  const bool edge = (j0 + BN > N) || (CAUSAL && j0 + BN - 1 > wq0);
+  fwd_tile<T, D, CAUSAL>(cur, cur + TILE, qf, acc, mref, l, edge, j0, qrow, N, c, lane);
 }
 
 template <class T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
-                                                  const void* __restrict__ vp, void* __restrict__ op,
-                                                  float* __restrict__ lsep, int N, int BH, int nqb,
-                                                  float c) {
-  constexpr int BM = 128, BN = 64, NW = 4, NKK = D / 16, NB = D / 32;
-  constexpr int TILE = BN * D * 2;
-  // Two K/V buffers as separate objects, so that the compiler can tell the
-  // tile being read from the tile being filled by DMA.
-  __shared__ __attribute__((aligned(16))) char buf0[2 * TILE];
-  __shared__ __attribute__((aligned(16))) char buf1[2 * TILE];
+__global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_kernel(const void* __restrict__ qp,
+                                                                const void* __restrict__ kp,
+                                                                const void* __restrict__ vp, void* __restrict__ op,
+                                                                float* __restrict__ lsep, int N, int BH, int nqb,
+                                                                float c) {
+  constexpr int NW = kFwdWaves, S = kFwdStages, BM = 32 * NW, BN = kFwdBN, NKK = D / 16, NB = D / 32;
+  constexpr int TILE = BN * D * 2, BUF = 2 * TILE;
+  using Dma = DmaTile<BN, D, NW>;
+  __shared__ __attribute__((aligned(16))) char smem[S * BUF];
+  lds_char* const lds = (lds_char*)smem;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, known uniform
   const int x = blockIdx.x;
   const int qb = CAUSAL ? (nqb - 1 - x / BH) : (x / BH);
   const int bh = x % BH;
@@ -126,21 +156,26 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const void* __restrict__ qp
   const size_t head = (size_t)bh * N * D * 2;
   const uint32_t bytes = (uint32_t)N * D * 2;
   const auto rq = make_rsrc((const char*)qp + head, bytes);
-  const auto rk = make_rsrc((const char*)kp + head, bytes);
-  const auto rv = make_rsrc((const char*)vp + head, bytes);
   const auto ro = make_rsrc((char*)op + head, bytes);
+  const Rsrc rk = make_rsrc_words((const char*)kp + head, bytes);
+  const Rsrc rv = make_rsrc_words((const char*)vp + head, bytes);
 
   const int kend = CAUSAL ? min(N, q0 + BM) : N;
   const int nt = (kend + BN - 1) / BN;
-  DmaTile<BN, D, NW> dma;
+  Dma dma;
   dma.init(w, lane);
-  dma.issue(rk, (lds_char*)buf0, 0, w);
-  dma.issue(rv, (lds_char*)buf0 + TILE, 0, w);
+  fwd_issue<D, 0>(lds, 0, dma, rk, rv, w);
 
   const int qrow = q0 + 32 * w + (lane & 31);  // this lane's query
   u32x4 qf[NKK];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) qf[kk] = bload16(rq, (uint32_t)((qrow * D + 16 * kk + 8 * h) * 2));
+  // Q has landed (and with it tile 0) before the ring starts: no load the
+  // compiler tracks may be pending inside the loop.
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) land(qf[kk]);
+  if (S > 2 && nt > 1) fwd_issue<D, 1 % S>(lds, 1, dma, rk, rv, w);
+  if (S > 3 && nt > 2) fwd_issue<D, 2 % S>(lds, 2, dma, rk, rv, w);
 
   f32x16 acc[NB];
 #pragma unroll
@@ -148,12 +183,15 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const void* __restrict__ qp
   float mref = -INFINITY, l = 0.f;  // reference max (base 2) and this lane's part of the row sum
   const int wq0 = q0 + 32 * w;      // first query of this wave
 
-  for (int t = 0; t < nt; t += 2) {
-    fwd_step<T, D, CAUSAL>((lds_char*)buf0, (lds_char*)buf1, t, nt, dma, rk, rv, qf, acc, mref, l, wq0, qrow, N, c,
-                           w, lane);
-    if (t + 1 < nt)
-      fwd_step<T, D, CAUSAL>((lds_char*)buf1, (lds_char*)buf0, t + 1, nt, dma, rk, rv, qf, acc, mref, l, wq0, qrow,
-                             N, c, w, lane);
+  for (int t = 0; t < nt; t += S) {
+    fwd_step<T, D, CAUSAL, 0>(lds, t, nt, dma, rk, rv, qf, acc, mref, l, wq0, qrow, N, c, w, lane);
+    if (t + 1 < nt) fwd_step<T, D, CAUSAL, 1>(lds, t + 1, nt, dma, rk, rv, qf, acc, mref, l, wq0, qrow, N, c, w, lane);
+    if constexpr (S > 2)
+      if (t + 2 < nt)
+        fwd_step<T, D, CAUSAL, 2 % S>(lds, t + 2, nt, dma, rk, rv, qf, acc, mref, l, wq0, qrow, N, c, w, lane);
+    if constexpr (S > 3)
+      if (t + 3 < nt)
+        fwd_step<T, D, CAUSAL, 3 % S>(lds, t + 3, nt, dma, rk, rv, qf, acc, mref, l, wq0, qrow, N, c, w, lane);
   }
 
   const float lt = sum_with_partner(l);
@@ -164,8 +202,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(const void* __restrict__ qp
 template <class T, int D, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   const int BH = a.B * a.H;
-  const int nqb = (a.N + 127) / 128;
-  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL>), dim3(nqb * BH), dim3(256), 0, st, a.q, a.k, a.v, a.o,
+  const int BM = 32 * kFwdWaves;
+  const int nqb = (a.N + BM - 1) / BM;
+  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL>), dim3(nqb * BH), dim3(64 * kFwdWaves), 0, st, a.q, a.k, a.v, a.o,
                      a.lse, a.N, BH, nqb, a.scale * kLog2e);
   return hipGetLastError();
 }
