@@ -58,14 +58,21 @@ __device__ __forceinline__ void dkdv_tile(const lds_char* qt, const lds_char* do
   const int h = lane >> 5;
   f32x16 s[2], dp[2];
 #pragma unroll
-  for (int a = 0; a < 2; ++a) {
-    s[a] = (f32x16){};
-    dp[a] = (f32x16){};
+  for (int a = 0; a < 2; ++a) s[a] = dp[a] = (f32x16){};
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
+  for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
       s[a] = Elem<T>::mma(lds_rows_operand<D>(qt, 32 * a, kk, lane), kf[kk], s[a]);
       dp[a] = Elem<T>::mma(lds_rows_operand<D>(dot, 32 * a, kk, lane), vf[kk], dp[a]);
     }
+  sched_mfma_lds<4 * NKK, 1, 6>();
+  if (edge) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (krow > i0 + 32 * a + 8 * (r >> 2) + 4 * h + (r & 3)) s[a][r] = -INFINITY;
   }
 #pragma unroll
   for (int a = 0; a < 2; ++a)
@@ -77,9 +84,7 @@ __device__ __forceinline__ void dkdv_tile(const lds_char* qt, const lds_char* do
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * g + e;
-        float x = s[a][r];
-        if (edge) x = krow > i0 + qi + e ? -INFINITY : x;
-        const float p = exp2_fast(__builtin_fmaf(x, c, -l2[e]));
+        const float p = exp2_fast(__builtin_fmaf(s[a][r], c, -l2[e]));
         s[a][r] = p;
         dp[a][r] = p * (dp[a][r] - dd[e]);
       }
@@ -91,12 +96,13 @@ __device__ __forceinline__ void dkdv_tile(const lds_char* qt, const lds_char* do
     dsf[j] = pack8<T>(dp[j >> 1], j & 1);
   }
 #pragma unroll
-  for (int b = 0; b < NB; ++b)
+  for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int b = 0; b < NB; ++b) {
       dva[b] = Elem<T>::mma(lds_cols_operand<D>(dot, j, 32 * b, lane), pf[j], dva[b]);
       dka[b] = Elem<T>::mma(lds_cols_operand<D>(qt, j, 32 * b, lane), dsf[j], dka[b]);
     }
+  sched_mfma_lds<8 * NB, 2, 3>();
 }
 
 constexpr int kBwdWaves = 4, kBwdTile = 64, kBwdStages = FA_BWD_STAGES;
@@ -232,34 +238,39 @@ __device__ __forceinline__ void dq_tile(const lds_char* kt, const lds_char* vt, 
   const int h = lane >> 5;
   f32x16 s[2], dp[2];
 #pragma unroll
-  for (int a = 0; a < 2; ++a) {
-    s[a] = (f32x16){};
-    dp[a] = (f32x16){};
+  for (int a = 0; a < 2; ++a) s[a] = dp[a] = (f32x16){};
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
+  for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
       s[a] = Elem<T>::mma(lds_rows_operand<D>(kt, 32 * a, kk, lane), qf[kk], s[a]);
       dp[a] = Elem<T>::mma(lds_rows_operand<D>(vt, 32 * a, kk, lane), dof[kk], dp[a]);
     }
+  sched_mfma_lds<4 * NKK, 1, 6>();
+  if (edge) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = j0 + 32 * a + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (key >= N || (CAUSAL && key > qrow)) s[a][r] = -INFINITY;
+      }
   }
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float x = s[a][r];
-      if (edge) {
-        const int key = j0 + 32 * a + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (key >= N || (CAUSAL && key > qrow)) x = -INFINITY;
-      }
-      const float p = exp2_fast(__builtin_fmaf(x, c, -l2));
+      const float p = exp2_fast(__builtin_fmaf(s[a][r], c, -l2));
       dp[a][r] = p * (dp[a][r] - dd);
     }
   u32x4 dsf[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) dsf[j] = pack8<T>(dp[j >> 1], j & 1);
 #pragma unroll
-  for (int b = 0; b < NB; ++b)
+  for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dqa[b] = Elem<T>::mma(lds_cols_operand<D>(kt, j, 32 * b, lane), dsf[j], dqa[b]);
+    for (int b = 0; b < NB; ++b) dqa[b] = Elem<T>::mma(lds_cols_operand<D>(kt, j, 32 * b, lane), dsf[j], dqa[b]);
+  sched_mfma_lds<4 * NB, 2, 3>();
 }
 
 // DMA of key tile t (K then V) into ring buffer IDX.

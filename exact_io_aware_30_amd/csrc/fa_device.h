@@ -277,6 +277,22 @@ __device__ __forceinline__ void ring_wait(int t, int nt) {
   }
 }
 
+// Scheduling hints for a straight run of MFMAs that each consume RPM LDS
+// reads: the scheduler keeps PRE MFMAs' worth of reads issued ahead of the
+// MFMA that uses them, so LDS latency overlaps earlier MFMAs instead of
+// stalling each one.  Masks: 0x008 MFMA, 0x100 LDS read, 0x002 VALU.
+template <int NM, int RPM, int PRE, int SYNC = 0>
+__device__ __forceinline__ void sched_mfma_lds() {
+  static_assert(PRE <= NM, "prefetch depth");
+  __builtin_amdgcn_sched_group_barrier(0x100, PRE * RPM, SYNC);
+#pragma unroll
+  for (int i = 0; i < NM - PRE; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, SYNC);
+    __builtin_amdgcn_sched_group_barrier(0x100, RPM, SYNC);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, PRE, SYNC);
+}
+
 // Value of x in lane l ^ 32, combined with x: returns {x_own, x_partner} as
 // the two halves of v_permlane32_swap (order depends on the lane half).
 __device__ __forceinline__ float max_with_partner(float x) {

@@ -58,11 +58,12 @@ __device__ __forceinline__ void fwd_tile(const lds_char* kt, const lds_char* vt,
   const int h = lane >> 5;
   f32x16 s[NA];
 #pragma unroll
-  for (int a = 0; a < NA; ++a) {
-    s[a] = (f32x16){};
+  for (int a = 0; a < NA; ++a) s[a] = (f32x16){};
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) s[a] = Elem<T>::mma(lds_rows_operand<D>(kt, 32 * a, kk, lane), qf[kk], s[a]);
-  }
+  for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+    for (int a = 0; a < NA; ++a) s[a] = Elem<T>::mma(lds_rows_operand<D>(kt, 32 * a, kk, lane), qf[kk], s[a]);
+  sched_mfma_lds<NA * NKK, 1, (NA * NKK < 6 ? NA * NKK : 6)>();
   if (edge) {
 #pragma unroll
     for (int a = 0; a < NA; ++a)
@@ -100,10 +101,10 @@ __device__ __forceinline__ void fwd_tile(const lds_char* kt, const lds_char* vt,
 #pragma unroll
   for (int j = 0; j < 2 * NA; ++j) pf[j] = pack8<T>(s[j >> 1], j & 1);
 #pragma unroll
-  for (int b = 0; b < NB; ++b)
+  for (int j = 0; j < 2 * NA; ++j)
 #pragma unroll
-    for (int j = 0; j < 2 * NA; ++j)
-      acc[b] = Elem<T>::mma(lds_cols_operand<D>(vt, j, 32 * b, lane), pf[j], acc[b]);
+    for (int b = 0; b < NB; ++b) acc[b] = Elem<T>::mma(lds_cols_operand<D>(vt, j, 32 * b, lane), pf[j], acc[b]);
+  sched_mfma_lds<2 * NA * NB, 2, 3>();
 }
 
 // DMA of key tile t (K then V) into ring buffer IDX.
