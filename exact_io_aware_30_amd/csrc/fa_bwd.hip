@@ -17,7 +17,6 @@
 #ifndef FA_BWD_STAGES
 #define FA_BWD_STAGES 2
 #endif
-
 namespace fa {
 
 // ---------------------------------------------------------------------------
@@ -47,40 +46,113 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const void* __restrict_
   }
 }
 
+constexpr int kBwdWaves = 4, kBwdTile = 64, kBwdStages = FA_BWD_STAGES;
+// dK/dV kernel configuration per head dimension (chosen by measurement):
+// query tile rows (32 or 64), workgroups per CU the registers are limited
+// for, ring depth, MFMAs' worth of LDS operand reads kept in flight in the
+// S/dP and dV/dK phases, and whether V's operand is read from LDS instead of
+// being held in registers.  FA_DKDV_* macros override every head dimension.
+template <int D>
+struct DkdvCfg {
+  static constexpr int kTile = D == 32 ? 64 : 32;
+  static constexpr int kOcc = D == 128 ? 2 : D == 64 ? 3 : 1;
+  static constexpr bool kVLds = D == 128;
+  static constexpr int kStages = 2, kPre1 = 6, kPre2 = 3;
+};
+#ifdef FA_DKDV_TILE
+#define FA_DKDV_CFG_TILE FA_DKDV_TILE
+#else
+#define FA_DKDV_CFG_TILE DkdvCfg<D>::kTile
+#endif
+#ifdef FA_DKDV_OCC
+#define FA_DKDV_CFG_OCC FA_DKDV_OCC
+#else
+#define FA_DKDV_CFG_OCC DkdvCfg<D>::kOcc
+#endif
+#ifdef FA_DKDV_VLDS
+#define FA_DKDV_CFG_VLDS (FA_DKDV_VLDS != 0)
+#else
+#define FA_DKDV_CFG_VLDS DkdvCfg<D>::kVLds
+#endif
+#ifdef FA_DKDV_STAGES
+#define FA_DKDV_CFG_STAGES FA_DKDV_STAGES
+#else
+#define FA_DKDV_CFG_STAGES DkdvCfg<D>::kStages
+#endif
+#ifdef FA_DKDV_PRE1
+#define FA_DKDV_CFG_PRE1 FA_DKDV_PRE1
+#else
+#define FA_DKDV_CFG_PRE1 DkdvCfg<D>::kPre1
+#endif
+#ifdef FA_DKDV_PRE2
+#define FA_DKDV_CFG_PRE2 FA_DKDV_PRE2
+#else
+#define FA_DKDV_CFG_PRE2 DkdvCfg<D>::kPre2
+#endif
+template <int D>
+struct Dkdv {
+  static constexpr int kTile = FA_DKDV_CFG_TILE, kOcc = FA_DKDV_CFG_OCC, kStages = FA_DKDV_CFG_STAGES;
+  static constexpr int kPre1 = FA_DKDV_CFG_PRE1, kPre2 = FA_DKDV_CFG_PRE2;
+  static constexpr bool kVLds = FA_DKDV_CFG_VLDS;
+  static_assert(kTile == 32 || kTile == 64, "dK/dV query tile");
+};
+// L and D of a query tile: one dword per lane of a wave, so 64 rows of each
+// are copied (rows past the tile are not read).
+constexpr int kStatsRows = 64;
+
+// The wave's V rows as the B operand of dP^T (k = head dimension, n = key).
+struct VRegs {
+  static constexpr int kReads = 0;
+  const u32x4* f;
+  __device__ __forceinline__ u32x4 operator()(int kk, int) const { return f[kk]; }
+};
+template <int D>
+struct VLds {
+  static constexpr int kReads = 1;
+  const lds_char* tile;  // the workgroup's key rows of V, swizzled like the Q tile
+  int row0;              // the wave's first row in it
+  __device__ __forceinline__ u32x4 operator()(int kk, int lane) const {
+    return lds_rows_operand<D>(tile, row0, kk, lane);
+  }
+};
+
 // One query tile of the dK/dV kernel for one wave (`edge`: the tile crosses
 // the causal diagonal of this wave's keys).  One code path for every tile,
 // so the accumulator registers need no copies at merges.
-template <class T, int D>
+template <class T, int D, int NA, class VOp>
 __device__ __forceinline__ void dkdv_tile(const lds_char* qt, const lds_char* dot, const float* st, const u32x4* kf,
-                                          const u32x4* vf, f32x16* dka, f32x16* dva, bool edge, int i0, int krow,
+                                          const VOp& vop, f32x16* dka, f32x16* dva, bool edge, int i0, int krow,
                                           float c, int lane) {
   constexpr int NKK = D / 16, NB = D / 32;
   const int h = lane >> 5;
-  f32x16 s[2], dp[2];
+  f32x16 s[NA], dp[NA];
 #pragma unroll
-  for (int a = 0; a < 2; ++a) s[a] = dp[a] = (f32x16){};
+  for (int a = 0; a < NA; ++a) s[a] = dp[a] = (f32x16){};
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
+    for (int a = 0; a < NA; ++a) {
       s[a] = Elem<T>::mma(lds_rows_operand<D>(qt, 32 * a, kk, lane), kf[kk], s[a]);
-      dp[a] = Elem<T>::mma(lds_rows_operand<D>(dot, 32 * a, kk, lane), vf[kk], dp[a]);
+      dp[a] = Elem<T>::mma(lds_rows_operand<D>(dot, 32 * a, kk, lane), vop(kk, lane), dp[a]);
     }
-  sched_mfma_lds<4 * NKK, 1, 6>();
+  {
+    constexpr int NM = 2 * NA * NKK, TR = NM + NA * NKK * VOp::kReads;
+    sched_mfma_reads<NM, TR, (TR < Dkdv<D>::kPre1 ? TR : Dkdv<D>::kPre1)>();
+  }
   if (edge) {
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < NA; ++a)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if (krow > i0 + 32 * a + 8 * (r >> 2) + 4 * h + (r & 3)) s[a][r] = -INFINITY;
   }
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < NA; ++a)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int qi = 32 * a + 8 * g + 4 * h;
       const f32x4 l2 = *(const f32x4*)(st + qi) * kLog2e;
-      const f32x4 dd = *(const f32x4*)(st + 64 + qi);
+      const f32x4 dd = *(const f32x4*)(st + kStatsRows + qi);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * g + e;
@@ -89,47 +161,46 @@ __device__ __forceinline__ void dkdv_tile(const lds_char* qt, const lds_char* do
         dp[a][r] = p * (dp[a][r] - dd[e]);
       }
     }
-  u32x4 pf[4], dsf[4];
+  u32x4 pf[2 * NA], dsf[2 * NA];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < 2 * NA; ++j) {
     pf[j] = pack8<T>(s[j >> 1], j & 1);
     dsf[j] = pack8<T>(dp[j >> 1], j & 1);
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < 2 * NA; ++j)
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       dva[b] = Elem<T>::mma(lds_cols_operand<D>(dot, j, 32 * b, lane), pf[j], dva[b]);
       dka[b] = Elem<T>::mma(lds_cols_operand<D>(qt, j, 32 * b, lane), dsf[j], dka[b]);
     }
-  sched_mfma_lds<8 * NB, 2, 3>();
+  sched_mfma_lds<4 * NA * NB, 2, (4 * NA * NB < Dkdv<D>::kPre2 ? 4 * NA * NB : Dkdv<D>::kPre2)>();
 }
 
-constexpr int kBwdWaves = 4, kBwdTile = 64, kBwdStages = FA_BWD_STAGES;
 
 // Enqueue the DMA of query tile i0: Q rows, dO rows, then L and D (one
 // dword per lane, waves 0 and 1).  Rows past N load as zeros: their Q and
 // dO rows are zero, so they add nothing to dV (dO = 0) or to dK
 // (dS = P (0 - 0) = 0) whatever P is.
 template <int D>
-__device__ __forceinline__ void dkdv_issue(lds_char* b, int i0, const DmaTile<kBwdTile, D, kBwdWaves>& dma, Rsrc rq,
+__device__ __forceinline__ void dkdv_issue(lds_char* b, int i0, const DmaTile<Dkdv<D>::kTile, D, kBwdWaves>& dma, Rsrc rq,
                                            Rsrc rdo, Rsrc rl, Rsrc rd, int w, int lane) {
-  constexpr int TILE = kBwdTile * D * 2;
+  constexpr int TILE = Dkdv<D>::kTile * D * 2;
   dma.issue(rq, b, i0, w);
   dma.issue(rdo, b + TILE, i0, w);
-  if (w < 2) dma4(w == 0 ? rl : rd, b + 2 * TILE + w * kBwdTile * 4, (uint32_t)((i0 + lane) * 4));
+  if (w < 2) dma4(w == 0 ? rl : rd, b + 2 * TILE + w * kStatsRows * 4, (uint32_t)((i0 + lane) * 4));
 }
 
 // One ring step on query tile t, held in ring buffer IDX = t % S (a
 // compile-time index, so LDS operand addresses are register + immediate):
 // wait and barrier, DMA of tile t + S - 1, then the math.
-template <class T, int D, bool CAUSAL, int IDX>
+template <class T, int D, bool CAUSAL, int IDX, class VOp>
 __device__ __forceinline__ void dkdv_step(lds_char* lds, int t, int nt, int i_start,
-                                          const DmaTile<kBwdTile, D, kBwdWaves>& dma, Rsrc rq, Rsrc rdo, Rsrc rl,
-                                          Rsrc rd, const u32x4* kf, const u32x4* vf, f32x16* dka, f32x16* dva,
+                                          const DmaTile<Dkdv<D>::kTile, D, kBwdWaves>& dma, Rsrc rq, Rsrc rdo, Rsrc rl,
+                                          Rsrc rd, const u32x4* kf, const VOp& vop, f32x16* dka, f32x16* dva,
                                           int wk0, int krow, float c, int w, int lane) {
-  constexpr int S = kBwdStages, BMQ = kBwdTile, TILE = BMQ * D * 2, BUF = 2 * TILE + 2 * BMQ * 4;
-  constexpr int PT = 2 * DmaTile<kBwdTile, D, kBwdWaves>::PER;  // per tile; waves 0, 1 add an L or D dword
+  constexpr int S = Dkdv<D>::kStages, BMQ = Dkdv<D>::kTile, TILE = BMQ * D * 2, BUF = 2 * TILE + 2 * kStatsRows * 4;
+  constexpr int PT = 2 * DmaTile<Dkdv<D>::kTile, D, kBwdWaves>::PER;  // per tile; waves 0, 1 add an L or D dword
   if (w < 2)
     ring_wait<S, PT + 1>(t, nt);
   else
@@ -140,7 +211,7 @@ __device__ __forceinline__ void dkdv_step(lds_char* lds, int t, int nt, int i_st
   if (CAUSAL && i0 + BMQ - 1 < wk0) return;  // every query of the tile precedes every key of the wave
   const lds_char* cur = lds + IDX * BUF;
   const float* st = (const float*)(cur + 2 * TILE);
-  dkdv_tile<T, D>(cur, cur + TILE, st, kf, vf, dka, dva, CAUSAL && i0 < wk0 + 31, i0, krow, c, lane);
+  dkdv_tile<T, D, BMQ / 32>(cur, cur + TILE, st, kf, vop, dka, dva, CAUSAL && i0 < wk0 + 31, i0, krow, c, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -155,16 +226,46 @@ __device__ __forceinline__ void dkdv_step(lds_char* lds, int t, int nt, int i_st
 // Under the causal mask query tiles start at the block's first key, and only
 // tiles that cross the diagonal are masked.
 // ---------------------------------------------------------------------------
+// The ring loop over query tiles and the final store of dK and dV.
+template <class T, int D, bool CAUSAL, class VOp>
+__device__ __forceinline__ void dkdv_run(lds_char* lds, int nt, int i_start, const DmaTile<Dkdv<D>::kTile, D, kBwdWaves>& dma,
+                                         Rsrc rq, Rsrc rdo, Rsrc rl, Rsrc rd, const u32x4* kf, const VOp& vop,
+                                         __amdgpu_buffer_rsrc_t rdk, __amdgpu_buffer_rsrc_t rdv, int wk0, int krow,
+                                         float c, float scale, int w, int lane) {
+  constexpr int S = Dkdv<D>::kStages, NB = D / 32;
+  f32x16 dka[NB], dva[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) dka[b] = dva[b] = (f32x16){};
+  for (int t = 0; t < nt; t += S) {
+    dkdv_step<T, D, CAUSAL, 0>(lds, t, nt, i_start, dma, rq, rdo, rl, rd, kf, vop, dka, dva, wk0, krow, c, w, lane);
+    if (t + 1 < nt)
+      dkdv_step<T, D, CAUSAL, 1>(lds, t + 1, nt, i_start, dma, rq, rdo, rl, rd, kf, vop, dka, dva, wk0, krow, c, w,
+                                 lane);
+    if constexpr (S > 2)
+      if (t + 2 < nt)
+        dkdv_step<T, D, CAUSAL, 2 % S>(lds, t + 2, nt, i_start, dma, rq, rdo, rl, rd, kf, vop, dka, dva, wk0, krow, c,
+                                       w, lane);
+    if constexpr (S > 3)
+      if (t + 3 < nt)
+        dkdv_step<T, D, CAUSAL, 3 % S>(lds, t + 3, nt, i_start, dma, rq, rdo, rl, rd, kf, vop, dka, dva, wk0, krow, c,
+                                       w, lane);
+  }
+  store_rows<T, D>(rdk, krow, dka, scale, lane);
+  store_rows<T, D>(rdv, krow, dva, 1.0f, lane);
+}
+
 template <class T, int D, bool CAUSAL>
-__global__ __launch_bounds__(64 * kBwdWaves) void dkdv_kernel(
+__global__ __launch_bounds__(64 * kBwdWaves, Dkdv<D>::kOcc) void dkdv_kernel(
     const void* __restrict__ qp, const void* __restrict__ kp, const void* __restrict__ vp,
     const void* __restrict__ dop, const float* __restrict__ lsep, const float* __restrict__ deltap,
     void* __restrict__ dkp, void* __restrict__ dvp, int N, int BH, float c, float scale) {
-  constexpr int NW = kBwdWaves, BNK = 32 * NW, BMQ = kBwdTile, NKK = D / 16, NB = D / 32;
+  constexpr int NW = kBwdWaves, BNK = 32 * NW, BMQ = Dkdv<D>::kTile, NKK = D / 16;
   constexpr int TILE = BMQ * D * 2;
-  constexpr int S = kBwdStages;
-  constexpr int BUF = 2 * TILE + 2 * BMQ * 4;  // Q tile, dO tile, L[64], D[64]
-  __shared__ __attribute__((aligned(16))) char smem[S * BUF];
+  constexpr int S = Dkdv<D>::kStages;
+  constexpr bool VL = Dkdv<D>::kVLds;
+  constexpr int BUF = 2 * TILE + 2 * kStatsRows * 4;  // Q tile, dO tile, L[64], D[64]
+  constexpr int VTILE = VL ? BNK * D * 2 : 0;  // the workgroup's V rows
+  __shared__ __attribute__((aligned(16))) char smem[S * BUF + VTILE];
   lds_char* const lds = (lds_char*)smem;
 
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
@@ -175,7 +276,6 @@ __global__ __launch_bounds__(64 * kBwdWaves) void dkdv_kernel(
   const size_t head = (size_t)bh * N * D * 2;
   const uint32_t bytes = (uint32_t)N * D * 2;
   const auto rk = make_rsrc((const char*)kp + head, bytes);
-  const auto rv = make_rsrc((const char*)vp + head, bytes);
   const auto rdk = make_rsrc((char*)dkp + head, bytes);
   const auto rdv = make_rsrc((char*)dvp + head, bytes);
   const Rsrc rq = make_rsrc_words((const char*)qp + head, bytes);
@@ -188,43 +288,37 @@ __global__ __launch_bounds__(64 * kBwdWaves) void dkdv_kernel(
   DmaTile<BMQ, D, NW> dma;
   dma.init(w, lane);
   dkdv_issue<D>(lds, i_start, dma, rq, rdo, rl, rd, w, lane);
+  lds_char* const vt = lds + S * BUF;
+  if constexpr (VL) {
+    DmaTile<BNK, D, NW> dmav;
+    dmav.init(w, lane);
+    dmav.issue(make_rsrc_words((const char*)vp + head, bytes), vt, k0, w);
+  }
 
   const int wk0 = k0 + 32 * w;
   const int krow = wk0 + (lane & 31);
   u32x4 kf[NKK], vf[NKK];
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
-    kf[kk] = bload16(rk, (uint32_t)((krow * D + 16 * kk + 8 * h) * 2));
-    vf[kk] = bload16(rv, (uint32_t)((krow * D + 16 * kk + 8 * h) * 2));
+  for (int kk = 0; kk < NKK; ++kk) kf[kk] = bload16(rk, (uint32_t)((krow * D + 16 * kk + 8 * h) * 2));
+  if constexpr (!VL) {
+    const auto rv = make_rsrc((const char*)vp + head, bytes);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) vf[kk] = bload16(rv, (uint32_t)((krow * D + 16 * kk + 8 * h) * 2));
   }
-  // K and V (and with them tile 0) land before the ring starts.
+  // K and V (and with them tile 0 and the V tile) land before the ring starts.
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
     land(kf[kk]);
-    land(vf[kk]);
+    if constexpr (!VL) land(vf[kk]);
   }
   if (S > 2 && nt > 1) dkdv_issue<D>(lds + (1 % S) * BUF, i_start + BMQ, dma, rq, rdo, rl, rd, w, lane);
   if (S > 3 && nt > 2) dkdv_issue<D>(lds + (2 % S) * BUF, i_start + 2 * BMQ, dma, rq, rdo, rl, rd, w, lane);
-  f32x16 dka[NB], dva[NB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) dka[b] = dva[b] = (f32x16){};
-
-  for (int t = 0; t < nt; t += S) {
-    dkdv_step<T, D, CAUSAL, 0>(lds, t, nt, i_start, dma, rq, rdo, rl, rd, kf, vf, dka, dva, wk0, krow, c, w, lane);
-    if (t + 1 < nt)
-      dkdv_step<T, D, CAUSAL, 1>(lds, t + 1, nt, i_start, dma, rq, rdo, rl, rd, kf, vf, dka, dva, wk0, krow, c, w,
-                                 lane);
-    if constexpr (S > 2)
-      if (t + 2 < nt)
-        dkdv_step<T, D, CAUSAL, 2 % S>(lds, t + 2, nt, i_start, dma, rq, rdo, rl, rd, kf, vf, dka, dva, wk0, krow, c,
-                                       w, lane);
-    if constexpr (S > 3)
-      if (t + 3 < nt)
-        dkdv_step<T, D, CAUSAL, 3 % S>(lds, t + 3, nt, i_start, dma, rq, rdo, rl, rd, kf, vf, dka, dva, wk0, krow, c,
-                                       w, lane);
-  }
-  store_rows<T, D>(rdk, krow, dka, scale, lane);
-  store_rows<T, D>(rdv, krow, dva, 1.0f, lane);
+  if constexpr (VL)
+    dkdv_run<T, D, CAUSAL>(lds, nt, i_start, dma, rq, rdo, rl, rd, kf, VLds<D>{vt, 32 * w}, rdk, rdv, wk0, krow, c,
+                           scale, w, lane);
+  else
+    dkdv_run<T, D, CAUSAL>(lds, nt, i_start, dma, rq, rdo, rl, rd, kf, VRegs{vf}, rdk, rdv, wk0, krow, c, scale, w,
+                           lane);
 }
 
 // One key tile of the dQ kernel for one wave (`edge`: the tile crosses the

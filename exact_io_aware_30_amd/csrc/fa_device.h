@@ -293,6 +293,25 @@ __device__ __forceinline__ void sched_mfma_lds() {
   __builtin_amdgcn_sched_group_barrier(0x008, PRE, SYNC);
 }
 
+// Same, for a run of NM MFMAs that consume TR LDS reads in all (spread
+// evenly over the MFMAs), with PRE reads issued ahead of the first MFMA.
+template <int NM, int TR, int PRE, int I, int DONE>
+__device__ __forceinline__ void sched_mfma_reads_tail() {
+  if constexpr (I < NM) {
+    constexpr int want = PRE + ((I + 1) * TR) / NM;
+    constexpr int tgt = want < TR ? want : TR;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (tgt > DONE) __builtin_amdgcn_sched_group_barrier(0x100, tgt - DONE, 0);
+    sched_mfma_reads_tail<NM, TR, PRE, I + 1, (tgt > DONE ? tgt : DONE)>();
+  }
+}
+template <int NM, int TR, int PRE>
+__device__ __forceinline__ void sched_mfma_reads() {
+  static_assert(PRE <= TR, "prefetch depth");
+  __builtin_amdgcn_sched_group_barrier(0x100, PRE, 0);
+  sched_mfma_reads_tail<NM, TR, PRE, 0, PRE>();
+}
+
 // Value of x in lane l ^ 32, combined with x: returns {x_own, x_partner} as
 // the two halves of v_permlane32_swap (order depends on the lane half).
 __device__ __forceinline__ float max_with_partner(float x) {
