@@ -136,6 +136,289 @@ __device__ __forceinline__ void fwd_step(lds_char* lds, int t, int nt, const Dma
   fwd_tile<T, D, CAUSAL>(cur, cur + TILE, qf, acc, mref, l, edge, j0, qrow, N, c, lane);
 }
 
+// ---------------------------------------------------------------------------
+// Software-pipelined form: per wave, the QK^T MFMAs of tile t+1 are issued
+// interleaved with the exponentials, row sums and bf16/fp16 packing of tile
+// t, and the PV MFMAs of tile t interleaved with the row maximum of tile
+// t+1, so one wave's VALU work runs under its own MFMAs.  Every tile needs K
+// of t+1 and V of t in LDS, so the ring is four tiles deep: tiles t, t+1 are
+// read while t+2 lands and t+3 is being issued into the buffer of t-1.
+// ---------------------------------------------------------------------------
+constexpr int kPipeStages = 4;
+// Used at d = 128, where a tile's VALU work fits under its MFMAs; at d = 64
+// and 32 (half and a quarter of the MFMAs per score) the plain kernel is
+// faster.  FA_FWD_PIPE=0/1 forces one form for every head dimension.
+#ifdef FA_FWD_PIPE
+template <int D>
+constexpr bool kFwdPipelined = FA_FWD_PIPE != 0;
+#else
+template <int D>
+constexpr bool kFwdPipelined = D == 128;
+#endif
+
+// S^T of one key tile into s (lane = query, registers = keys).
+template <class T, int D>
+__device__ __forceinline__ void fwd_scores(const lds_char* kt, const u32x4* qf, f32x16* s, int lane) {
+  constexpr int NKK = D / 16, NA = kFwdNA;
+#pragma unroll
+  for (int a = 0; a < NA; ++a) s[a] = (f32x16){};
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+    for (int a = 0; a < NA; ++a) s[a] = Elem<T>::mma(lds_rows_operand<D>(kt, 32 * a, kk, lane), qf[kk], s[a]);
+}
+
+// Keys past N, and under the causal mask keys after the lane's query, to
+// -inf: key j0 + 32a + 8(r/4) + 4h + r%4 is dropped when it exceeds
+// lim = min(query, N - 1) (N - 1 without the mask), one compare per element
+// against lim - j0 - 4h.  The bound passes through an empty asm statement so
+// that the compares stay inside the caller's branch.
+template <bool CAUSAL>
+__device__ __forceinline__ void fwd_mask(f32x16* s, int j0, int qrow, int N, int lane) {
+  int rel = (CAUSAL ? min(qrow, N - 1) : N - 1) - j0 - 4 * (lane >> 5);
+  asm volatile("" : "+v"(rel));
+#pragma unroll
+  for (int a = 0; a < kFwdNA; ++a)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (32 * a + 8 * (r >> 2) + (r & 3) > rel) s[a][r] = -INFINITY;
+}
+
+// Row maximum of s in base-2 units (both lane halves).
+__device__ __forceinline__ float fwd_rowmax(const f32x16* s, float c) {
+  float mx = s[0][0];
+#pragma unroll
+  for (int a = 0; a < kFwdNA; ++a)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[a][r]);
+  return max_with_partner(mx) * c;
+}
+
+// Move the reference when some row's maximum exceeds it by more than the
+// slack; l and acc are rescaled with it.
+template <int NB>
+__device__ __forceinline__ void fwd_rescale(float mxc, f32x16* acc, float& mref, float& l) {
+  if (__builtin_amdgcn_ballot_w64(mxc > mref + kRescaleSlack)) {
+    const float mnew = fmaxf(mref, mxc);
+    const float alpha = exp2_fast(mref - mnew);  // 0 on the first tile (mref = -inf)
+    mref = mnew;
+    l *= alpha;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b] *= alpha;
+  }
+}
+
+// p = 2^(s c - mref) packed into MFMA operands; l += row sum.
+template <class T>
+__device__ __forceinline__ void fwd_probs(const f32x16* s, u32x4* pf, float c, float mref, float& l) {
+  float rs = 0.f;
+  f32x16 p[kFwdNA];
+#pragma unroll
+  for (int a = 0; a < kFwdNA; ++a)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      p[a][r] = exp2_fast(__builtin_fmaf(s[a][r], c, -mref));
+      rs += p[a][r];
+    }
+  l += rs;
+#pragma unroll
+  for (int j = 0; j < 2 * kFwdNA; ++j) pf[j] = pack8<T>(p[j >> 1], j & 1);
+}
+
+template <class T, int D>
+__device__ __forceinline__ void fwd_pv(const lds_char* vt, const u32x4* pf, f32x16* acc, int lane) {
+  constexpr int NB = D / 32;
+#pragma unroll
+  for (int j = 0; j < 2 * kFwdNA; ++j)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b] = Elem<T>::mma(lds_cols_operand<D>(vt, j, 32 * b, lane), pf[j], acc[b]);
+}
+
+// Ring layout of the pipelined kernel: the K tiles of all buffers first,
+// then the V tiles, so that within each half every buffer is an immediate
+// offset (under 64 KiB) from one base address.
+template <int D, int IDX>
+__device__ __forceinline__ void fwd_pipe_issue(lds_char* lds, int t, const DmaTile<kFwdBN, D, kFwdWaves>& dma,
+                                               Rsrc rk, Rsrc rv, int w) {
+  constexpr int TILE = kFwdBN * D * 2;
+  dma.issue(rk, lds + IDX * TILE, t * kFwdBN, w);
+  dma.issue(rv, lds + (kPipeStages + IDX) * TILE, t * kFwdBN, w);
+}
+
+// Wait until tile t+1 has landed (tile t already has), allowing the DMA of
+// tile t+2 to be in flight, then the workgroup barrier.
+template <int PT>
+__device__ __forceinline__ void pipe_wait(int t, int nt) {
+  if (t + 2 < nt)
+    dma_wait_barrier<PT>();
+  else
+    dma_wait_barrier<0>();
+}
+
+// One pipelined step: tile t in buffer IDX (its V is read), tile t+1 in
+// buffer IDX+1 (its K is read); s_cur holds S^T of tile t (masked, the
+// reference already moved for it), s_nxt receives S^T of tile t+1.
+// The two MFMA runs are written out in issue order, each MFMA followed by
+// its share of VALU work and the LDS reads for a later MFMA, with
+// scheduling fences between the groups so that the compiler keeps this
+// order (a wave issues VALU work while its own MFMAs execute).
+template <class T, int D, bool CAUSAL, int IDX>
+__device__ __forceinline__ void fwd_pipe_step(lds_char* lds, int t, int nt, int ntw,
+                                              const DmaTile<kFwdBN, D, kFwdWaves>& dma, Rsrc rk, Rsrc rv,
+                                              const u32x4* qf, f32x16* acc, f32x16* s_cur, f32x16* s_nxt,
+                                              float& mref, float& l, int wq0, int qrow, int N, float c, int w,
+                                              int lane) {
+  constexpr int S = kPipeStages, BN = kFwdBN, TILE = BN * D * 2, NB = D / 32, NKK = D / 16, NA = kFwdNA;
+  pipe_wait<2 * DmaTile<kFwdBN, D, kFwdWaves>::PER>(t, nt);
+  if (t + S - 1 < nt) fwd_pipe_issue<D, (IDX + S - 1) % S>(lds, t + S - 1, dma, rk, rv, w);
+  __builtin_amdgcn_sched_barrier(0);
+  if (t >= ntw) return;  // every key from tile t on follows every query of the wave
+  // Tile bases made opaque per step, so that the compiler does not hoist a
+  // full set of per-buffer, per-lane addresses out of the loop.
+  uint32_t vb = (uint32_t)(uintptr_t)lds + (S + IDX) * TILE, kb = (uint32_t)(uintptr_t)lds + ((IDX + 1) % S) * TILE;
+  asm volatile("" : "+v"(vb), "+v"(kb));
+  const lds_char* vcur = (const lds_char*)(uintptr_t)vb;
+  const lds_char* knxt = (const lds_char*)(uintptr_t)kb;
+
+  // Run 1: S^T(t+1) = K(t+1) Q^T, MFMA i = (kk = i / NA, a = i % NA), and
+  // p = 2^(S(t) c - mref), row sums and packing of tile t, E elements per
+  // MFMA.  K of tile t+1 is read even past the wave's (or the sequence's)
+  // last tile: the buffer is in bounds and such scores are masked below.
+  {
+    constexpr int NM = NA * NKK, E = 16 * NA / NM, PRE = NM < 3 ? NM : 3;
+    u32x4 kop[NM];
+    float rs = 0.f;
+    u32x4 pf[2 * NA];
+#pragma unroll
+    for (int i = 0; i < PRE; ++i) kop[i] = lds_rows_operand<D>(knxt, 32 * (i % NA), i / NA, lane);
+#pragma unroll
+    for (int a = 0; a < NA; ++a) s_nxt[a] = (f32x16){};
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      if (i + PRE < NM) kop[i + PRE] = lds_rows_operand<D>(knxt, 32 * ((i + PRE) % NA), (i + PRE) / NA, lane);
+      s_nxt[i % NA] = Elem<T>::mma(kop[i], qf[i / NA], s_nxt[i % NA]);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int x = i * E + e, a = x / 16, r = x % 16;
+        s_cur[a][r] = exp2_fast(__builtin_fmaf(s_cur[a][r], c, -mref));  // P in place
+        rs += s_cur[a][r];
+        if (r % 8 == 7) pf[x / 8] = pack8<T>(s_cur[a], (r / 8));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l += rs;
+    // Pin P and l here, or the compiler sinks their VALU work past the
+    // branch below, away from the MFMAs it is meant to run under.
+#pragma unroll
+    for (int j = 0; j < 2 * NA; ++j) land(pf[j]);
+    land(l);
+
+    const int j1 = (t + 1) * BN;
+    if ((j1 + BN > N) || (CAUSAL && j1 + BN - 1 > wq0)) fwd_mask<CAUSAL>(s_nxt, j1, qrow, N, lane);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Run 2: O^T += V(t)^T P(t)^T, MFMA i = (j = i / NB, b = i % NB), and the
+    // row maximum of S(t+1), F elements per MFMA.
+    constexpr int NM2 = 2 * NA * NB, F = 16 * NA / NM2, PRE2 = NM2 < 2 ? NM2 : 2;
+    u32x4 vop[NM2];
+#pragma unroll
+    for (int i = 0; i < PRE2; ++i) vop[i] = lds_cols_operand<D>(vcur, i / NB, 32 * (i % NB), lane);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NM2; ++i) {
+      if (i + PRE2 < NM2) vop[i + PRE2] = lds_cols_operand<D>(vcur, (i + PRE2) / NB, 32 * ((i + PRE2) % NB), lane);
+      acc[i % NB] = Elem<T>::mma(vop[i], pf[i / NB], acc[i % NB]);
+#pragma unroll
+      for (int e = 0; e < F; ++e) {
+        const int x = i * F + e;
+        mx = fmaxf(mx, s_nxt[x / 16][x % 16]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    fwd_rescale<NB>(max_with_partner(mx) * c, acc, mref, l);
+  }
+}
+
+template <class T, int D, bool CAUSAL>
+__global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_pipe_kernel(const void* __restrict__ qp,
+                                                                     const void* __restrict__ kp,
+                                                                     const void* __restrict__ vp,
+                                                                     void* __restrict__ op, float* __restrict__ lsep,
+                                                                     int N, int BH, int nqb, float c) {
+  constexpr int NW = kFwdWaves, S = kPipeStages, BM = 32 * NW, BN = kFwdBN, NKK = D / 16, NB = D / 32;
+  constexpr int TILE = BN * D * 2, BUF = 2 * TILE;
+  using Dma = DmaTile<BN, D, NW>;
+  constexpr int PT = 2 * Dma::PER;
+  __shared__ __attribute__((aligned(16))) char smem[S * BUF];
+  // The LDS base goes through an empty asm statement: with its bits unknown
+  // the compiler adds (instead of ORing) constant offsets to per-lane
+  // addresses and folds them into the read instructions' immediate offsets.
+  uint32_t lds_base = (uint32_t)(uintptr_t)(lds_char*)smem;
+  asm volatile("" : "+v"(lds_base));
+  lds_char* const lds = (lds_char*)(uintptr_t)lds_base;
+
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, known uniform
+  const int x = blockIdx.x;
+  const int qb = CAUSAL ? (nqb - 1 - x / BH) : (x / BH);
+  const int bh = x % BH;
+  const int q0 = qb * BM;
+  const size_t head = (size_t)bh * N * D * 2;
+  const uint32_t bytes = (uint32_t)N * D * 2;
+  const auto rq = make_rsrc((const char*)qp + head, bytes);
+  const auto ro = make_rsrc((char*)op + head, bytes);
+  const Rsrc rk = make_rsrc_words((const char*)kp + head, bytes);
+  const Rsrc rv = make_rsrc_words((const char*)vp + head, bytes);
+
+  const int kend = CAUSAL ? min(N, q0 + BM) : N;
+  const int nt = (kend + BN - 1) / BN;
+  const int wq0 = q0 + 32 * w;  // first query of this wave
+  // Tiles this wave computes on: under the causal mask those with a key at
+  // or before its last query.
+  const int ntw = CAUSAL ? min(nt, (wq0 + 31) / BN + 1) : nt;
+  Dma dma;
+  dma.init(w, lane);
+  fwd_pipe_issue<D, 0>(lds, 0, dma, rk, rv, w);
+
+  const int qrow = wq0 + (lane & 31);  // this lane's query
+  u32x4 qf[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) qf[kk] = bload16(rq, (uint32_t)((qrow * D + 16 * kk + 8 * h) * 2));
+  // Q has landed (and with it tile 0) before the ring starts: no load the
+  // compiler tracks may be pending inside the loop.
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) land(qf[kk]);
+  if (nt > 1) fwd_pipe_issue<D, 1>(lds, 1, dma, rk, rv, w);
+  if (nt > 2) fwd_pipe_issue<D, 2>(lds, 2, dma, rk, rv, w);
+  // Tile 0 landed (waited above); tiles 1 and 2 may be in flight.
+  dma_wait_barrier<63>();
+
+  f32x16 acc[NB], sa[kFwdNA], sb[kFwdNA];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = (f32x16){};
+  float mref = -INFINITY, l = 0.f;  // reference max (base 2) and this lane's part of the row sum
+  fwd_scores<T, D>(lds, qf, sa, lane);
+  if (BN > N || (CAUSAL && BN - 1 > wq0)) fwd_mask<CAUSAL>(sa, 0, qrow, N, lane);
+  fwd_rescale<NB>(fwd_rowmax(sa, c), acc, mref, l);
+
+  for (int t = 0; t < nt; t += 4) {
+    fwd_pipe_step<T, D, CAUSAL, 0>(lds, t, nt, ntw, dma, rk, rv, qf, acc, sa, sb, mref, l, wq0, qrow, N, c, w, lane);
+    if (t + 1 < nt)
+      fwd_pipe_step<T, D, CAUSAL, 1>(lds, t + 1, nt, ntw, dma, rk, rv, qf, acc, sb, sa, mref, l, wq0, qrow, N, c, w,
+                                     lane);
+    if (t + 2 < nt)
+      fwd_pipe_step<T, D, CAUSAL, 2>(lds, t + 2, nt, ntw, dma, rk, rv, qf, acc, sa, sb, mref, l, wq0, qrow, N, c, w,
+                                     lane);
+    if (t + 3 < nt)
+      fwd_pipe_step<T, D, CAUSAL, 3>(lds, t + 3, nt, ntw, dma, rk, rv, qf, acc, sb, sa, mref, l, wq0, qrow, N, c, w,
+                                     lane);
+  }
+
+  const float lt = sum_with_partner(l);
+  store_rows<T, D>(ro, qrow, acc, 1.0f / lt, lane);
+  if (h == 0 && qrow < N) lsep[(size_t)bh * N + qrow] = (mref + log2_fast(lt)) * kLn2;
+}
+
 template <class T, int D, bool CAUSAL>
 __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_kernel(const void* __restrict__ qp,
                                                                 const void* __restrict__ kp,
@@ -205,8 +488,12 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   const int BH = a.B * a.H;
   const int BM = 32 * kFwdWaves;
   const int nqb = (a.N + BM - 1) / BM;
-  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL>), dim3(nqb * BH), dim3(64 * kFwdWaves), 0, st, a.q, a.k, a.v, a.o,
-                     a.lse, a.N, BH, nqb, a.scale * kLog2e);
+  if constexpr (kFwdPipelined<D>)
+    hipLaunchKernelGGL((fwd_pipe_kernel<T, D, CAUSAL>), dim3(nqb * BH), dim3(64 * kFwdWaves), 0, st, a.q, a.k, a.v,
+                       a.o, a.lse, a.N, BH, nqb, a.scale * kLog2e);
+  else
+    hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL>), dim3(nqb * BH), dim3(64 * kFwdWaves), 0, st, a.q, a.k, a.v, a.o,
+                       a.lse, a.N, BH, nqb, a.scale * kLog2e);
   return hipGetLastError();
 }
 
