@@ -7,8 +7,17 @@ d=128] with the causal mask.  FLOPs: forward 4 B H N^2 d, backward 10 B H N^2 d,
 both halved under the causal mask.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --report    every workload: forward, backward and
+                                forward+backward TFLOP/s (median of 30 timed
+                                calls after 10 warm-up calls, min and max),
+                                device-memory growth, and the oracle on one
+                                head of each (a markdown table, then one JSON
+                                line per workload)
+    python bench.py --sweep     bf16 causal d=128, B=1, H=16, N = 1K .. 64K:
+                                one pass of each kernel per N (for hardware
+                                counters) and its time
 
-Prints one JSON line.  Besides the contract fields it carries
+Without --report or --sweep it prints one JSON line.  Besides the contract fields it carries
   roofline      the dominant kernel (longest average launch, timed with HIP
                 events on the launch stream over the timed region) against
                 the dense bf16 MFMA peak, plus its HBM traffic per launch
@@ -88,6 +97,131 @@ def cpu_baseline(w, heads: int = 24):
             "seconds": round(dt, 3)}
 
 
+def _inputs(w, dev):
+    import torch
+
+    from exact_io_aware_30_amd import workloads
+
+    q, k, v, do = (x.to(dev) for x in workloads.make_inputs(w))
+    o = torch.empty_like(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    delta = torch.empty_like(lse)
+    return q, k, v, do, o, dq, dk, dv, lse, delta
+
+
+def _median_ms(fn, warmup=10, reps=30):
+    """Median, min and max of `reps` calls of fn timed with HIP events on the current stream."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in ev)
+    return t[len(t) // 2], t[0], t[-1]
+
+
+def calib_copy(mib: int):
+    """One device-to-device copy of `mib` MiB: a kernel of known traffic for
+    scaling hardware byte counters."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def report():
+    """Every workload: forward, backward, forward+backward; oracle on one head."""
+    import torch
+
+    from exact_io_aware_30_amd import binding, workloads
+
+    dev = torch.device("cuda:0")
+    rows = []
+    for name, w in workloads.WORKLOADS.items():
+        q, k, v, do, o, dq, dk, dv, lse, delta = _inputs(w, dev)
+        torch.cuda.synchronize()
+        fwd = lambda: binding.fa_fwd(q, k, v, o, lse, w.scale, w.causal)
+
+        def bwd():
+            binding.fa_bwd_preprocess(o, do, delta)
+            binding.fa_bwd(q, k, v, do, lse, delta, dq, dk, dv, w.scale, w.causal)
+
+        def both():
+            fwd()
+            bwd()
+
+        torch.cuda.reset_peak_memory_stats()
+        before = torch.cuda.max_memory_allocated()
+        both()
+        torch.cuda.synchronize()
+        grown = torch.cuda.max_memory_allocated() - before
+        tf, tb, tfb = _median_ms(fwd), _median_ms(bwd), _median_ms(both)
+        f, b, fb = workloads.flops(w)
+        cb = cpu_baseline(w, heads=1)  # the oracle on the first head (heads are independent)
+        r = {"workload": w.describe(), "fwd_ms": [round(x, 4) for x in tf], "bwd_ms": [round(x, 4) for x in tb],
+             "fwd_bwd_ms": [round(x, 4) for x in tfb], "fwd_tflops": round(f / tf[0] / 1e9, 1),
+             "bwd_tflops": round(b / tb[0] / 1e9, 1), "fwd_bwd_tflops": round(fb / tfb[0] / 1e9, 1),
+             "frac_mfma_peak": round(fb / tfb[0] / 1e9 / PEAK_BF16_TFLOPS, 4),
+             "device_memory_growth_bytes": int(grown),
+             "oracle_one_head_s": cb["seconds"], "oracle_tflops": round(cb["value"], 4),
+             "oracle_threads": cb["cores"]}
+        rows.append(r)
+        del q, k, v, do, o, dq, dk, dv, lse, delta
+        torch.cuda.empty_cache()
+    print("| workload | fwd ms (min-max) | bwd ms (min-max) | fwd+bwd ms | fwd TF/s | bwd TF/s | fwd+bwd TF/s "
+          "| % of 2.5 PF | memory growth | oracle, one head |")
+    print("|---|---|---|---|---|---|---|---|---|---|")
+    for r in rows:
+        print(f"| {r['workload']} | {r['fwd_ms'][0]:.4f} ({r['fwd_ms'][1]:.4f}-{r['fwd_ms'][2]:.4f}) "
+              f"| {r['bwd_ms'][0]:.4f} ({r['bwd_ms'][1]:.4f}-{r['bwd_ms'][2]:.4f}) | {r['fwd_bwd_ms'][0]:.4f} "
+              f"| {r['fwd_tflops']} | {r['bwd_tflops']} | {r['fwd_bwd_tflops']} | {100 * r['frac_mfma_peak']:.1f} "
+              f"| {r['device_memory_growth_bytes']} B | {r['oracle_one_head_s']} s ({r['oracle_tflops']} TF/s) |")
+    for r in rows:
+        print(json.dumps(r), flush=True)
+
+
+SWEEP_N = (1024, 2048, 4096, 8192, 16384, 32768, 65536)
+
+
+def sweep():
+    """bf16 causal d=128, B=1, H=16: one pass of each kernel per N, then its time."""
+    import torch
+
+    from exact_io_aware_30_amd import binding, workloads
+
+    dev = torch.device("cuda:0")
+    for n in SWEEP_N:
+        w = workloads.Workload(f"sweep{n}", "bf16", 1, 16, n, 128, True, 1.0, 2000 + n // 1024)
+        q, k, v, do, o, dq, dk, dv, lse, delta = _inputs(w, dev)
+        torch.cuda.synchronize()
+        binding.fa_fwd(q, k, v, o, lse, w.scale, w.causal)
+        binding.fa_bwd_preprocess(o, do, delta)
+        binding.fa_bwd_dkdv(q, k, v, do, lse, delta, dk, dv, w.scale, w.causal)
+        binding.fa_bwd_dq(q, k, v, do, lse, delta, dq, w.scale, w.causal)
+        torch.cuda.synchronize()
+        fb = workloads.flops(w)[2]
+        t = _median_ms(lambda: (binding.fa_fwd(q, k, v, o, lse, w.scale, w.causal),
+                                binding.fa_bwd_preprocess(o, do, delta),
+                                binding.fa_bwd(q, k, v, do, lse, delta, dq, dk, dv, w.scale, w.causal)),
+                       warmup=2, reps=5)
+        print(json.dumps({"N": n, "B": 1, "H": 16, "d": 128, "fwd_bwd_ms": round(t[0], 4),
+                          "fwd_bwd_tflops": round(fb / t[0] / 1e9, 1),
+                          "algorithmic_bytes": workloads.algorithmic_bytes(w)}), flush=True)
+        del q, k, v, do, o, dq, dk, dv, lse, delta
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -95,6 +229,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--report", action="store_true")
+    ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed steps, copy a buffer of this many MiB once (a kernel of known "
                          "traffic for scaling hardware byte counters)")
@@ -103,6 +239,12 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+
+    if args.report or args.sweep:
+        report() if args.report else sweep()
+        if args.calib_copy_mib:
+            calib_copy(args.calib_copy_mib)
+        return
 
     import torch
 
@@ -148,13 +290,7 @@ def main():
     per = {p: sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / args.steps for j, p in enumerate(phases)}
     assert torch.isfinite(o).all() and torch.isfinite(dq).all(), "non-finite output"
     if args.calib_copy_mib:
-        n = args.calib_copy_mib * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        calib_copy(args.calib_copy_mib)
 
     f, b, fb = workloads.flops(w)
     ms = wall * 1e3 / args.steps
