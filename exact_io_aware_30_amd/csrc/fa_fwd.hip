@@ -19,6 +19,10 @@
 // row maximum exceeds it by more than 2^8; then l and acc are rescaled by
 // alpha = 2^(ref_old - ref_new).  After the last tile: O = acc / l and
 // L = (ref + log2 l) ln 2.
+//
+// Two forms: fwd_kernel (above per tile, a 3-deep ring) and, at d = 128,
+// fwd_pipe_kernel, which overlaps tile t's softmax with tile t+1's QK^T
+// inside each wave (see the comment at its step function).
 #include "fa_device.h"
 #include "fa_launch.h"
 
