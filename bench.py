@@ -46,26 +46,29 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
 METRIC = "attention fwd+bwd TFLOP/s (bf16 causal N=8192 d=128) + % of MFMA peak"
 WORKLOAD = "long"
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_traffic_long.txt")
-KERNEL_SOURCES = ("fa_device.h", "fa_launch.h", "fa_fwd.hip", "fa_bwd.hip")
+LIBRARY = os.path.join(ROOT, "exact_io_aware_30_amd", "libfa_mi355x.so")
 
 
-def source_hash() -> str:
-    h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "exact_io_aware_30_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+def library_hash():
+    """First 16 hex digits of the SHA-256 of the built library: it changes
+    exactly when the compiled kernels do (the build is byte-reproducible and
+    comments do not reach it)."""
+    try:
+        with open(LIBRARY, "rb") as f:
+            return hashlib.sha256(f.read()).hexdigest()[:16]
+    except OSError:
+        return None
 
 
 def traffic_from_summary(kernel: str):
     """HBM bytes per launch of `kernel` from the committed counter summary, if
-    it was measured on the current kernel sources."""
+    it was measured on the library that is built now."""
     try:
         text = open(TRAFFIC_SUMMARY).read()
     except OSError:
         return None
-    m = re.search(r"^source_hash:\s*(\S+)", text, re.M)
-    if not m or m.group(1) != source_hash():
+    m = re.search(r"^library_hash:\s*(\S+)", text, re.M)
+    if not m or m.group(1) != library_hash():
         return None
     m = re.search(rf"^traffic_bytes\s+{re.escape(kernel)}:\s*([0-9.eE+]+)", text, re.M)
     return float(m.group(1)) if m else None
@@ -337,7 +340,7 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": None,
-        "kernel_source_hash": source_hash(),
+        "library_hash": library_hash(),
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
