@@ -128,6 +128,7 @@ __device__ __forceinline__ void dkdv_tile(const lds_char* qt, const lds_char* do
   f32x16 s[NA], dp[NA];
 #pragma unroll
   for (int a = 0; a < NA; ++a) s[a] = dp[a] = (f32x16){};
+  prio_mfma_begin();
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
@@ -139,6 +140,7 @@ __device__ __forceinline__ void dkdv_tile(const lds_char* qt, const lds_char* do
     constexpr int NM = 2 * NA * NKK, TR = NM + NA * NKK * VOp::kReads;
     sched_mfma_reads<NM, TR, (TR < Dkdv<D>::kPre1 ? TR : Dkdv<D>::kPre1)>();
   }
+  prio_mfma_end();
   if (edge) {
 #pragma unroll
     for (int a = 0; a < NA; ++a)
@@ -167,6 +169,7 @@ __device__ __forceinline__ void dkdv_tile(const lds_char* qt, const lds_char* do
     pf[j] = pack8<T>(s[j >> 1], j & 1);
     dsf[j] = pack8<T>(dp[j >> 1], j & 1);
   }
+  prio_mfma_begin();
 #pragma unroll
   for (int j = 0; j < 2 * NA; ++j)
 #pragma unroll
@@ -175,6 +178,7 @@ __device__ __forceinline__ void dkdv_tile(const lds_char* qt, const lds_char* do
       dka[b] = Elem<T>::mma(lds_cols_operand<D>(qt, j, 32 * b, lane), dsf[j], dka[b]);
     }
   sched_mfma_lds<4 * NA * NB, 2, (4 * NA * NB < Dkdv<D>::kPre2 ? 4 * NA * NB : Dkdv<D>::kPre2)>();
+  prio_mfma_end();
 }
 
 
@@ -333,6 +337,7 @@ __device__ __forceinline__ void dq_tile(const lds_char* kt, const lds_char* vt, 
   f32x16 s[2], dp[2];
 #pragma unroll
   for (int a = 0; a < 2; ++a) s[a] = dp[a] = (f32x16){};
+  prio_mfma_begin();
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
@@ -341,6 +346,7 @@ __device__ __forceinline__ void dq_tile(const lds_char* kt, const lds_char* vt, 
       dp[a] = Elem<T>::mma(lds_rows_operand<D>(vt, 32 * a, kk, lane), dof[kk], dp[a]);
     }
   sched_mfma_lds<4 * NKK, 1, 6>();
+  prio_mfma_end();
   if (edge) {
 #pragma unroll
     for (int a = 0; a < 2; ++a)
@@ -360,11 +366,13 @@ __device__ __forceinline__ void dq_tile(const lds_char* kt, const lds_char* vt, 
   u32x4 dsf[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) dsf[j] = pack8<T>(dp[j >> 1], j & 1);
+  prio_mfma_begin();
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
     for (int b = 0; b < NB; ++b) dqa[b] = Elem<T>::mma(lds_cols_operand<D>(kt, j, 32 * b, lane), dsf[j], dqa[b]);
   sched_mfma_lds<4 * NB, 2, 3>();
+  prio_mfma_end();
 }
 
 // DMA of key tile t (K then V) into ring buffer IDX.

@@ -312,6 +312,29 @@ __device__ __forceinline__ void sched_mfma_reads() {
   sched_mfma_reads_tail<NM, TR, PRE, 0, PRE>();
 }
 
+// Wave priority around an MFMA run: while its MFMAs issue, a wave wins issue
+// arbitration over a wave that is in its VALU phase on the same SIMD.  The
+// scheduling fences keep the priority changes where they are written.
+#ifndef FA_SETPRIO
+#define FA_SETPRIO 1
+#endif
+__device__ __forceinline__ void prio_mfma_begin_always() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(1);
+  __builtin_amdgcn_sched_barrier(0);
+}
+__device__ __forceinline__ void prio_mfma_end_always() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(0);
+  __builtin_amdgcn_sched_barrier(0);
+}
+__device__ __forceinline__ void prio_mfma_begin() {
+  if constexpr (FA_SETPRIO != 0) prio_mfma_begin_always();
+}
+__device__ __forceinline__ void prio_mfma_end() {
+  if constexpr (FA_SETPRIO != 0) prio_mfma_end_always();
+}
+
 // Value of x in lane l ^ 32, combined with x: returns {x_own, x_partner} as
 // the two halves of v_permlane32_swap (order depends on the lane half).
 __device__ __forceinline__ float max_with_partner(float x) {

@@ -51,6 +51,18 @@ constexpr int kFwdBN = 32 * kFwdNA;
 // reference, so the result is the same up to rounding.
 constexpr float kRescaleSlack = 8.0f;
 
+// Wave priority around MFMA runs in the forward kernels (FA_FWD_PRIO=0 turns
+// it off; the backward kernels use FA_SETPRIO).
+#ifndef FA_FWD_PRIO
+#define FA_FWD_PRIO 0
+#endif
+__device__ __forceinline__ void fwd_prio_begin() {
+  if constexpr (FA_FWD_PRIO != 0) prio_mfma_begin_always();
+}
+__device__ __forceinline__ void fwd_prio_end() {
+  if constexpr (FA_FWD_PRIO != 0) prio_mfma_end_always();
+}
+
 // One key tile for one wave: S^T, mask (only when `edge`: the tile crosses
 // the diagonal or the end of N), online-softmax update, PV.  One code path
 // for every tile, so the accumulator registers need no copies at merges.
@@ -63,11 +75,13 @@ __device__ __forceinline__ void fwd_tile(const lds_char* kt, const lds_char* vt,
   f32x16 s[NA];
 #pragma unroll
   for (int a = 0; a < NA; ++a) s[a] = (f32x16){};
+  fwd_prio_begin();
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
     for (int a = 0; a < NA; ++a) s[a] = Elem<T>::mma(lds_rows_operand<D>(kt, 32 * a, kk, lane), qf[kk], s[a]);
   sched_mfma_lds<NA * NKK, 1, (NA * NKK < 6 ? NA * NKK : 6)>();
+  fwd_prio_end();
   if (edge) {
 #pragma unroll
     for (int a = 0; a < NA; ++a)
@@ -104,11 +118,13 @@ __device__ __forceinline__ void fwd_tile(const lds_char* kt, const lds_char* vt,
   u32x4 pf[2 * NA];
 #pragma unroll
   for (int j = 0; j < 2 * NA; ++j) pf[j] = pack8<T>(s[j >> 1], j & 1);
+  fwd_prio_begin();
 #pragma unroll
   for (int j = 0; j < 2 * NA; ++j)
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[b] = Elem<T>::mma(lds_cols_operand<D>(vt, j, 32 * b, lane), pf[j], acc[b]);
   sched_mfma_lds<2 * NA * NB, 2, 3>();
+  fwd_prio_end();
 }
 
 // DMA of key tile t (K then V) into ring buffer IDX.
@@ -297,6 +313,7 @@ __device__ __forceinline__ void fwd_pipe_step(lds_char* lds, int t, int nt, int 
     for (int i = 0; i < PRE; ++i) kop[i] = lds_rows_operand<D>(knxt, 32 * (i % NA), i / NA, lane);
 #pragma unroll
     for (int a = 0; a < NA; ++a) s_nxt[a] = (f32x16){};
+    fwd_prio_begin();
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
       if (i + PRE < NM) kop[i + PRE] = lds_rows_operand<D>(knxt, 32 * ((i + PRE) % NA), (i + PRE) / NA, lane);
@@ -310,6 +327,7 @@ __device__ __forceinline__ void fwd_pipe_step(lds_char* lds, int t, int nt, int 
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    fwd_prio_end();
     l += rs;
     // Pin P and l here, or the compiler sinks their VALU work past the
     // branch below, away from the MFMAs it is meant to run under.
@@ -328,6 +346,7 @@ __device__ __forceinline__ void fwd_pipe_step(lds_char* lds, int t, int nt, int 
 #pragma unroll
     for (int i = 0; i < PRE2; ++i) vop[i] = lds_cols_operand<D>(vcur, i / NB, 32 * (i % NB), lane);
     float mx = -INFINITY;
+    fwd_prio_begin();
 #pragma unroll
     for (int i = 0; i < NM2; ++i) {
       if (i + PRE2 < NM2) vop[i + PRE2] = lds_cols_operand<D>(vcur, (i + PRE2) / NB, 32 * ((i + PRE2) % NB), lane);
@@ -339,6 +358,7 @@ __device__ __forceinline__ void fwd_pipe_step(lds_char* lds, int t, int nt, int 
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    fwd_prio_end();
     fwd_rescale<NB>(max_with_partner(mx) * c, acc, mref, l);
   }
 }
