@@ -116,16 +116,12 @@ struct VLds {
   }
 };
 
-// One query tile of the dK/dV kernel for one wave (`edge`: the tile crosses
-// the causal diagonal of this wave's keys).  One code path for every tile,
-// so the accumulator registers need no copies at merges.
+// The three phases of one query tile of the dK/dV kernels for one wave.
+// Phase 1 (MFMA): S^T and dP^T of the tile (lane = key, registers = query).
 template <class T, int D, int NA, class VOp>
-__device__ __forceinline__ void dkdv_tile(const lds_char* qt, const lds_char* dot, const float* st, const u32x4* kf,
-                                          const VOp& vop, f32x16* dka, f32x16* dva, bool edge, int i0, int krow,
-                                          float c, int lane) {
-  constexpr int NKK = D / 16, NB = D / 32;
-  const int h = lane >> 5;
-  f32x16 s[NA], dp[NA];
+__device__ __forceinline__ void dkdv_scores(const lds_char* qt, const lds_char* dot, const u32x4* kf, const VOp& vop,
+                                            f32x16* s, f32x16* dp, int lane) {
+  constexpr int NKK = D / 16;
 #pragma unroll
   for (int a = 0; a < NA; ++a) s[a] = dp[a] = (f32x16){};
   prio_mfma_begin();
@@ -141,6 +137,15 @@ __device__ __forceinline__ void dkdv_tile(const lds_char* qt, const lds_char* do
     sched_mfma_reads<NM, TR, (TR < Dkdv<D>::kPre1 ? TR : Dkdv<D>::kPre1)>();
   }
   prio_mfma_end();
+}
+
+// Phase 2 (VALU): mask (only when `edge`: the tile crosses the diagonal of
+// the wave's keys), P = 2^(S c - L log2 e), dS = P (dP - D), packed into
+// MFMA operands.  st holds the tile's L (st[0..63]) and D (st[64..127]).
+template <class T, int NA>
+__device__ __forceinline__ void dkdv_probs(f32x16* s, f32x16* dp, const float* st, u32x4* pf, u32x4* dsf, bool edge,
+                                           int i0, int krow, float c, int lane) {
+  const int h = lane >> 5;
   if (edge) {
 #pragma unroll
     for (int a = 0; a < NA; ++a)
@@ -163,12 +168,19 @@ __device__ __forceinline__ void dkdv_tile(const lds_char* qt, const lds_char* do
         dp[a][r] = p * (dp[a][r] - dd[e]);
       }
     }
-  u32x4 pf[2 * NA], dsf[2 * NA];
 #pragma unroll
   for (int j = 0; j < 2 * NA; ++j) {
     pf[j] = pack8<T>(s[j >> 1], j & 1);
     dsf[j] = pack8<T>(dp[j >> 1], j & 1);
   }
+}
+
+// Phase 3 (MFMA): dV^T += dO^T P and dK^T += Q^T dS, A operands by
+// transposed LDS reads.
+template <class T, int D, int NA>
+__device__ __forceinline__ void dkdv_accum(const lds_char* qt, const lds_char* dot, const u32x4* pf, const u32x4* dsf,
+                                           f32x16* dka, f32x16* dva, int lane) {
+  constexpr int NB = D / 32;
   prio_mfma_begin();
 #pragma unroll
   for (int j = 0; j < 2 * NA; ++j)
@@ -181,6 +193,19 @@ __device__ __forceinline__ void dkdv_tile(const lds_char* qt, const lds_char* do
   prio_mfma_end();
 }
 
+// One query tile of the dK/dV kernel for one wave, the three phases in a
+// row.  One code path for every tile, so the accumulator registers need no
+// copies at merges.
+template <class T, int D, int NA, class VOp>
+__device__ __forceinline__ void dkdv_tile(const lds_char* qt, const lds_char* dot, const float* st, const u32x4* kf,
+                                          const VOp& vop, f32x16* dka, f32x16* dva, bool edge, int i0, int krow,
+                                          float c, int lane) {
+  f32x16 s[NA], dp[NA];
+  u32x4 pf[2 * NA], dsf[2 * NA];
+  dkdv_scores<T, D, NA>(qt, dot, kf, vop, s, dp, lane);
+  dkdv_probs<T, NA>(s, dp, st, pf, dsf, edge, i0, krow, c, lane);
+  dkdv_accum<T, D, NA>(qt, dot, pf, dsf, dka, dva, lane);
+}
 
 // Enqueue the DMA of query tile i0: Q rows, dO rows, then L and D (one
 // dword per lane, waves 0 and 1).  Rows past N load as zeros: their Q and
