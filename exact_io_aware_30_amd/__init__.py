@@ -2,12 +2,13 @@
 
 The compute path is a C-ABI shared library of hand-written HIP kernels for
 gfx950 (``csrc/``, header ``include/fa.h``); ``binding`` marshals torch
-tensors into it.  ``workloads`` draws the seeded synthetic inputs and counts
-FLOPs and bytes.  Submodules are imported on demand so that the input
+tensors into it; ``interface`` adds ``flash_attn``, its autograd.Function
+and the ``FlashSelfAttention`` module on top.  ``workloads`` draws the
+seeded synthetic inputs and counts FLOPs and bytes.  Submodules are imported on demand so that the input
 generator can be used where the native library is not built.
 """
 
-__all__ = ["binding", "workloads"]
+__all__ = ["binding", "interface", "workloads"]
 
 
 def __getattr__(name):
