@@ -37,6 +37,10 @@ _SIG = {
     "fa_bwd": [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _f, _i, _i, _p],
     "fa_bwd_dkdv": [_p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _f, _i, _i, _p],
     "fa_bwd_dq": [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _f, _i, _i, _p],
+    "fa_fwd_gqa": [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _i, _p],
+    "fa_bwd_gqa": [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _i, _p],
+    "fa_bwd_dkdv_gqa": [_p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _i, _p],
+    "fa_bwd_dq_gqa": [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _i, _p],
     "fa_status_string": [_i],
     "fa_version": [],
 }
@@ -138,18 +142,79 @@ def fa_bwd_dq(q, k, v, do, lse, delta, dq, scale: float, causal: bool) -> None:
                           _DT[q.dtype], _stream(q)), "fa_bwd_dq")
 
 
+def _kv(q, pairs):
+    """Hkv of k-shaped tensors [B, Hkv, N, d] that go with q [B, H, N, d]."""
+    B, H, N, d = q.shape
+    Hkv = pairs[0][0].shape[1] if pairs[0][0].dim() == 4 else -1
+    for t, name in pairs:
+        if t.dim() != 4 or t.shape != (B, Hkv, N, d) or t.dtype != q.dtype or not t.is_cuda \
+                or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous [B, Hkv, N, d] GPU tensor of q's dtype")
+    if Hkv < 1 or H % Hkv:
+        raise ValueError(f"the query heads ({H}) must be a multiple of the key/value heads ({Hkv})")
+    return Hkv
+
+
+def fa_fwd_gqa(q, k, v, o, lse, scale: float, causal: bool) -> None:
+    B, H, N, d = _bhnd(q, "q")
+    Hkv = _kv(q, ((k, "k"), (v, "v")))
+    _same(q, (o, "o"))
+    _rows(q, (lse, "lse"))
+    _check(_lib.fa_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                           B, H, Hkv, N, d, float(scale), int(bool(causal)), _DT[q.dtype], _stream(q)),
+           "fa_fwd_gqa")
+
+
+def fa_bwd_gqa(q, k, v, do, lse, delta, dq, dk, dv, scale: float, causal: bool) -> None:
+    B, H, N, d = _bhnd(q, "q")
+    Hkv = _kv(q, ((k, "k"), (v, "v"), (dk, "dk"), (dv, "dv")))
+    _same(q, (do, "do"), (dq, "dq"))
+    _rows(q, (lse, "lse"), (delta, "delta"))
+    _check(_lib.fa_bwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                           delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, N, d,
+                           float(scale), int(bool(causal)), _DT[q.dtype], _stream(q)), "fa_bwd_gqa")
+
+
+def fa_bwd_dkdv_gqa(q, k, v, do, lse, delta, dk, dv, scale: float, causal: bool) -> None:
+    B, H, N, d = _bhnd(q, "q")
+    Hkv = _kv(q, ((k, "k"), (v, "v"), (dk, "dk"), (dv, "dv")))
+    _same(q, (do, "do"))
+    _rows(q, (lse, "lse"), (delta, "delta"))
+    _check(_lib.fa_bwd_dkdv_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                                delta.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, N, d, float(scale),
+                                int(bool(causal)), _DT[q.dtype], _stream(q)), "fa_bwd_dkdv_gqa")
+
+
+def fa_bwd_dq_gqa(q, k, v, do, lse, delta, dq, scale: float, causal: bool) -> None:
+    B, H, N, d = _bhnd(q, "q")
+    Hkv = _kv(q, ((k, "k"), (v, "v")))
+    _same(q, (do, "do"), (dq, "dq"))
+    _rows(q, (lse, "lse"), (delta, "delta"))
+    _check(_lib.fa_bwd_dq_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                              delta.data_ptr(), dq.data_ptr(), B, H, Hkv, N, d, float(scale), int(bool(causal)),
+                              _DT[q.dtype], _stream(q)), "fa_bwd_dq_gqa")
+
+
 def attention_forward(q, k, v, scale: float, causal: bool):
-    """(o, lse) with o like q and lse float32 [B, H, N]."""
+    """(o, lse) with o like q and lse float32 [B, H, N]; k and v may have
+    fewer heads than q (grouped-query attention)."""
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
-    fa_fwd(q, k, v, o, lse, scale, causal)
+    if k.dim() == 4 and k.shape[1] != q.shape[1]:
+        fa_fwd_gqa(q, k, v, o, lse, scale, causal)
+    else:
+        fa_fwd(q, k, v, o, lse, scale, causal)
     return o, lse
 
 
 def attention_backward(q, k, v, o, do, lse, scale: float, causal: bool):
-    """(dq, dk, dv, delta): the pre-pass then the two backward kernels."""
+    """(dq, dk, dv, delta): the pre-pass then the two backward kernels; dk and
+    dv are shaped like k and v."""
     delta = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     fa_bwd_preprocess(o, do, delta)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-    fa_bwd(q, k, v, do, lse, delta, dq, dk, dv, scale, causal)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if k.dim() == 4 and k.shape[1] != q.shape[1]:
+        fa_bwd_gqa(q, k, v, do, lse, delta, dq, dk, dv, scale, causal)
+    else:
+        fa_bwd(q, k, v, do, lse, delta, dq, dk, dv, scale, causal)
     return dq, dk, dv, delta

@@ -59,53 +59,67 @@ int check_alias(const Range* outs, int nout, const Range* ins, int nin) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
+int check_heads(int H, int Hkv) {
+  if (Hkv < 1 || H % Hkv != 0) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
 int check_bwd(const void* q, const void* k, const void* v, const void* dO, const float* lse, const float* delta,
-              const void* dq, const void* dk, const void* dv, int B, int H, int N, int d, float scale, int causal,
-              fa_dtype dt, bool want_dq, bool want_dkdv) {
+              const void* dq, const void* dk, const void* dv, int B, int H, int Hkv, int N, int d, float scale,
+              int causal, fa_dtype dt, bool want_dq, bool want_dkdv) {
   if (!q || !k || !v || !dO || !lse || !delta) return FA_ERR_INVALID_ARG;
   if ((want_dq && !dq) || (want_dkdv && (!dk || !dv))) return FA_ERR_INVALID_ARG;
   int rc = check_common(B, H, N, d, dt);
   if (rc) return rc;
+  if ((rc = check_heads(H, Hkv))) return rc;
   if ((rc = check_scale_mask(scale, causal))) return rc;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) || !aligned16(lse) || !aligned16(delta))
     return FA_ERR_ALIGNMENT;
   if ((want_dq && !aligned16(dq)) || (want_dkdv && (!aligned16(dk) || !aligned16(dv)))) return FA_ERR_ALIGNMENT;
   const long long tb = static_cast<long long>(B) * H * N * d * 2, rb = static_cast<long long>(B) * H * N * 4;
-  const Range ins[6] = {range_of(q, tb), range_of(k, tb), range_of(v, tb), range_of(dO, tb), range_of(lse, rb),
+  const long long kvb = static_cast<long long>(B) * Hkv * N * d * 2;
+  const Range ins[6] = {range_of(q, tb), range_of(k, kvb), range_of(v, kvb), range_of(dO, tb), range_of(lse, rb),
                         range_of(delta, rb)};
   Range outs[3];
   int n = 0;
   if (want_dq) outs[n++] = range_of(dq, tb);
   if (want_dkdv) {
-    outs[n++] = range_of(dk, tb);
-    outs[n++] = range_of(dv, tb);
+    outs[n++] = range_of(dk, kvb);
+    outs[n++] = range_of(dv, kvb);
   }
   return check_alias(outs, n, ins, 6);
 }
 
 fa::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* dO, const float* lse,
-                     const float* delta, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
-                     int causal, fa_dtype dt) {
-  return fa::BwdArgs{q, k, v, dO, lse, delta, dq, dk, dv, B, H, N, d, scale, causal == 1, dt == FA_BF16};
+                     const float* delta, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d,
+                     float scale, int causal, fa_dtype dt) {
+  return fa::BwdArgs{q, k, v, dO, lse, delta, dq, dk, dv, B, H, N, d, Hkv, scale, causal == 1, dt == FA_BF16};
 }
 
 }  // namespace
 
 extern "C" {
 
-int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
-           float scale, int causal, fa_dtype dt, void* stream) {
+int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N,
+               int d, float scale, int causal, fa_dtype dt, void* stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
   int rc = check_common(B, H, N, d, dt);
   if (rc) return rc;
+  if ((rc = check_heads(H, Hkv))) return rc;
   if ((rc = check_scale_mask(scale, causal))) return rc;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGNMENT;
   const long long tb = static_cast<long long>(B) * H * N * d * 2, rb = static_cast<long long>(B) * H * N * 4;
-  const Range ins[3] = {range_of(q, tb), range_of(k, tb), range_of(v, tb)};
+  const long long kvb = static_cast<long long>(B) * Hkv * N * d * 2;
+  const Range ins[3] = {range_of(q, tb), range_of(k, kvb), range_of(v, kvb)};
   const Range outs[2] = {range_of(o, tb), range_of(lse, rb)};
   if ((rc = check_alias(outs, 2, ins, 3))) return rc;
-  const fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, causal == 1, dt == FA_BF16};
+  const fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, Hkv, scale, causal == 1, dt == FA_BF16};
   return hip_status(fa::launch_fwd(a, static_cast<hipStream_t>(stream)));
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+           float scale, int causal, fa_dtype dt, void* stream) {
+  return fa_fwd_gqa(q, k, v, o, lse, B, H, H, N, d, scale, causal, dt, stream);
 }
 
 int fa_bwd_preprocess(const void* o, const void* dO, float* delta, int B, int H, int N, int d, fa_dtype dt,
@@ -122,37 +136,58 @@ int fa_bwd_preprocess(const void* o, const void* dO, float* delta, int B, int H,
   return hip_status(fa::launch_preprocess(a, static_cast<hipStream_t>(stream)));
 }
 
-int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse, const float* delta,
-                void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, fa_dtype dt, void* stream) {
-  const int rc = check_bwd(q, k, v, dO, lse, delta, nullptr, dk, dv, B, H, N, d, scale, causal, dt, false, true);
+int fa_bwd_dkdv_gqa(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                    const float* delta, void* dk, void* dv, int B, int H, int Hkv, int N, int d, float scale,
+                    int causal, fa_dtype dt, void* stream) {
+  const int rc =
+      check_bwd(q, k, v, dO, lse, delta, nullptr, dk, dv, B, H, Hkv, N, d, scale, causal, dt, false, true);
   if (rc) return rc;
-  const fa::BwdArgs a = bwd_args(q, k, v, dO, lse, delta, nullptr, dk, dv, B, H, N, d, scale, causal, dt);
+  const fa::BwdArgs a = bwd_args(q, k, v, dO, lse, delta, nullptr, dk, dv, B, H, Hkv, N, d, scale, causal, dt);
   return hip_status(fa::launch_bwd_dkdv(a, static_cast<hipStream_t>(stream)));
 }
 
-int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse, const float* delta,
-              void* dq, int B, int H, int N, int d, float scale, int causal, fa_dtype dt, void* stream) {
-  const int rc = check_bwd(q, k, v, dO, lse, delta, dq, nullptr, nullptr, B, H, N, d, scale, causal, dt, true, false);
+int fa_bwd_dq_gqa(const void* q, const void* k, const void* v, const void* dO, const float* lse, const float* delta,
+                  void* dq, int B, int H, int Hkv, int N, int d, float scale, int causal, fa_dtype dt,
+                  void* stream) {
+  const int rc =
+      check_bwd(q, k, v, dO, lse, delta, dq, nullptr, nullptr, B, H, Hkv, N, d, scale, causal, dt, true, false);
   if (rc) return rc;
-  const fa::BwdArgs a = bwd_args(q, k, v, dO, lse, delta, dq, nullptr, nullptr, B, H, N, d, scale, causal, dt);
+  const fa::BwdArgs a = bwd_args(q, k, v, dO, lse, delta, dq, nullptr, nullptr, B, H, Hkv, N, d, scale, causal, dt);
   return hip_status(fa::launch_bwd_dq(a, static_cast<hipStream_t>(stream)));
 }
 
-int fa_bwd(const void* q, const void* k, const void* v, const void* dO, const float* lse, const float* delta,
-           void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, fa_dtype dt,
-           void* stream) {
-  int rc = check_bwd(q, k, v, dO, lse, delta, dq, dk, dv, B, H, N, d, scale, causal, dt, true, true);
+int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* dO, const float* lse, const float* delta,
+               void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d, float scale, int causal,
+               fa_dtype dt, void* stream) {
+  int rc = check_bwd(q, k, v, dO, lse, delta, dq, dk, dv, B, H, Hkv, N, d, scale, causal, dt, true, true);
   if (rc) return rc;
-  const fa::BwdArgs a = bwd_args(q, k, v, dO, lse, delta, dq, dk, dv, B, H, N, d, scale, causal, dt);
+  const fa::BwdArgs a = bwd_args(q, k, v, dO, lse, delta, dq, dk, dv, B, H, Hkv, N, d, scale, causal, dt);
   const hipStream_t st = static_cast<hipStream_t>(stream);
   if ((rc = hip_status(fa::launch_bwd_dkdv(a, st)))) return rc;
   return hip_status(fa::launch_bwd_dq(a, st));
 }
 
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse, const float* delta,
+                void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, fa_dtype dt, void* stream) {
+  return fa_bwd_dkdv_gqa(q, k, v, dO, lse, delta, dk, dv, B, H, H, N, d, scale, causal, dt, stream);
+}
+
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse, const float* delta,
+              void* dq, int B, int H, int N, int d, float scale, int causal, fa_dtype dt, void* stream) {
+  return fa_bwd_dq_gqa(q, k, v, dO, lse, delta, dq, B, H, H, N, d, scale, causal, dt, stream);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* dO, const float* lse, const float* delta,
+           void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, fa_dtype dt,
+           void* stream) {
+  return fa_bwd_gqa(q, k, v, dO, lse, delta, dq, dk, dv, B, H, H, N, d, scale, causal, dt, stream);
+}
+
 const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
-    case FA_ERR_INVALID_ARG: return "invalid argument (null pointer, size < 1, bad dtype, mask or scale)";
+    case FA_ERR_INVALID_ARG:
+      return "invalid argument (null pointer, size < 1, bad dtype, mask or scale, or H not a multiple of Hkv)";
     case FA_ERR_UNSUPPORTED: return "unsupported (head dim not 32/64/128, or sizes beyond the library limits)";
     case FA_ERR_ALIGNMENT: return "a pointer is not 16-byte aligned";
     case FA_ERR_HIP: return "the HIP runtime refused a kernel launch";
@@ -161,6 +196,6 @@ const char* fa_status_string(int status) {
   }
 }
 
-int fa_version(void) { return 100; }
+int fa_version(void) { return 200; }
 
 }  // extern "C"

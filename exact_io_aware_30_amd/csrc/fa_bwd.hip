@@ -57,7 +57,7 @@ struct DkdvCfg {
   static constexpr int kTile = D == 32 ? 64 : 32;
   static constexpr int kOcc = D == 128 ? 2 : D == 64 ? 3 : 1;
   static constexpr bool kVLds = D == 128;
-  static constexpr int kStages = 2, kPre1 = 6, kPre2 = 3;
+  static constexpr int kStages = 2, kPre1 = D == 64 ? 4 : 6, kPre2 = 3;
 };
 #ifdef FA_DKDV_TILE
 #define FA_DKDV_CFG_TILE FA_DKDV_TILE
@@ -255,39 +255,62 @@ __device__ __forceinline__ void dkdv_step(lds_char* lds, int t, int nt, int i_st
 // Under the causal mask query tiles start at the block's first key, and only
 // tiles that cross the diagonal are masked.
 // ---------------------------------------------------------------------------
-// The ring loop over query tiles and the final store of dK and dV.
+// The ring loop over query tiles, once per query head of the key/value
+// head's group (G = 1 without grouping: the gradients of a shared K and V
+// are the sums over the heads that read them), and the final store of dK
+// and dV.  The first head's first tiles were issued by the caller.
 template <class T, int D, bool CAUSAL, class VOp>
 __device__ __forceinline__ void dkdv_run(lds_char* lds, int nt, int i_start, const DmaTile<Dkdv<D>::kTile, D, kBwdWaves>& dma,
-                                         Rsrc rq, Rsrc rdo, Rsrc rl, Rsrc rd, const u32x4* kf, const VOp& vop,
+                                         const void* qp, const void* dop, const float* lsep, const float* deltap,
+                                         int bh0, int G, int N, const u32x4* kf, const VOp& vop,
                                          __amdgpu_buffer_rsrc_t rdk, __amdgpu_buffer_rsrc_t rdv, int wk0, int krow,
                                          float c, float scale, int w, int lane) {
-  constexpr int S = Dkdv<D>::kStages, NB = D / 32;
+  constexpr int S = Dkdv<D>::kStages, NB = D / 32, BMQ = Dkdv<D>::kTile;
+  constexpr int BUF = 2 * BMQ * D * 2 + 2 * kStatsRows * 4;
+  const uint32_t bytes = (uint32_t)N * D * 2;
   f32x16 dka[NB], dva[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) dka[b] = dva[b] = (f32x16){};
-  for (int t = 0; t < nt; t += S) {
-    dkdv_step<T, D, CAUSAL, 0>(lds, t, nt, i_start, dma, rq, rdo, rl, rd, kf, vop, dka, dva, wk0, krow, c, w, lane);
-    if (t + 1 < nt)
-      dkdv_step<T, D, CAUSAL, 1>(lds, t + 1, nt, i_start, dma, rq, rdo, rl, rd, kf, vop, dka, dva, wk0, krow, c, w,
-                                 lane);
-    if constexpr (S > 2)
-      if (t + 2 < nt)
-        dkdv_step<T, D, CAUSAL, 2 % S>(lds, t + 2, nt, i_start, dma, rq, rdo, rl, rd, kf, vop, dka, dva, wk0, krow, c,
-                                       w, lane);
-    if constexpr (S > 3)
-      if (t + 3 < nt)
-        dkdv_step<T, D, CAUSAL, 3 % S>(lds, t + 3, nt, i_start, dma, rq, rdo, rl, rd, kf, vop, dka, dva, wk0, krow, c,
-                                       w, lane);
+  for (int g = 0; g < G; ++g) {
+    const int bh = bh0 + g;
+    const size_t head = (size_t)bh * N * D * 2;
+    const Rsrc rq = make_rsrc_words((const char*)qp + head, bytes);
+    const Rsrc rdo = make_rsrc_words((const char*)dop + head, bytes);
+    const Rsrc rl = make_rsrc_words(lsep + (size_t)bh * N, (uint32_t)N * 4);
+    const Rsrc rd = make_rsrc_words(deltap + (size_t)bh * N, (uint32_t)N * 4);
+    if (g > 0) {
+      // Every wave is done with the previous head's ring before it refills.
+      dma_wait_barrier<0>();
+      dkdv_issue<D>(lds, i_start, dma, rq, rdo, rl, rd, w, lane);
+      if (S > 2 && nt > 1) dkdv_issue<D>(lds + (1 % S) * BUF, i_start + BMQ, dma, rq, rdo, rl, rd, w, lane);
+      if (S > 3 && nt > 2) dkdv_issue<D>(lds + (2 % S) * BUF, i_start + 2 * BMQ, dma, rq, rdo, rl, rd, w, lane);
+    }
+    for (int t = 0; t < nt; t += S) {
+      dkdv_step<T, D, CAUSAL, 0>(lds, t, nt, i_start, dma, rq, rdo, rl, rd, kf, vop, dka, dva, wk0, krow, c, w, lane);
+      if (t + 1 < nt)
+        dkdv_step<T, D, CAUSAL, 1>(lds, t + 1, nt, i_start, dma, rq, rdo, rl, rd, kf, vop, dka, dva, wk0, krow, c, w,
+                                   lane);
+      if constexpr (S > 2)
+        if (t + 2 < nt)
+          dkdv_step<T, D, CAUSAL, 2 % S>(lds, t + 2, nt, i_start, dma, rq, rdo, rl, rd, kf, vop, dka, dva, wk0, krow,
+                                         c, w, lane);
+      if constexpr (S > 3)
+        if (t + 3 < nt)
+          dkdv_step<T, D, CAUSAL, 3 % S>(lds, t + 3, nt, i_start, dma, rq, rdo, rl, rd, kf, vop, dka, dva, wk0, krow,
+                                         c, w, lane);
+    }
   }
   store_rows<T, D>(rdk, krow, dka, scale, lane);
   store_rows<T, D>(rdv, krow, dva, 1.0f, lane);
 }
 
+// Grid: key blocks x key/value heads (BHkv = B * H / G of them); the query
+// heads of key/value head hkv of batch b are b H + hkv G .. + G - 1.
 template <class T, int D, bool CAUSAL>
 __global__ __launch_bounds__(64 * kBwdWaves, Dkdv<D>::kOcc) void dkdv_kernel(
     const void* __restrict__ qp, const void* __restrict__ kp, const void* __restrict__ vp,
     const void* __restrict__ dop, const float* __restrict__ lsep, const float* __restrict__ deltap,
-    void* __restrict__ dkp, void* __restrict__ dvp, int N, int BH, float c, float scale) {
+    void* __restrict__ dkp, void* __restrict__ dvp, int N, int BHkv, int H, int G, float c, float scale) {
   constexpr int NW = kBwdWaves, BNK = 32 * NW, BMQ = Dkdv<D>::kTile, NKK = D / 16;
   constexpr int TILE = BMQ * D * 2;
   constexpr int S = Dkdv<D>::kStages;
@@ -300,28 +323,33 @@ __global__ __launch_bounds__(64 * kBwdWaves, Dkdv<D>::kOcc) void dkdv_kernel(
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, known uniform
   const int x = blockIdx.x;
-  const int kb = x / BH, bh = x % BH;
+  const int kb = x / BHkv, bhkv = x % BHkv;
+  const int Hkv = H / G;
+  const int bh0 = (bhkv / Hkv) * H + (bhkv % Hkv) * G;  // first query head of the group
   const int k0 = kb * BNK;
-  const size_t head = (size_t)bh * N * D * 2;
+  const size_t headkv = (size_t)bhkv * N * D * 2;
+  const size_t head0 = (size_t)bh0 * N * D * 2;
   const uint32_t bytes = (uint32_t)N * D * 2;
-  const auto rk = make_rsrc((const char*)kp + head, bytes);
-  const auto rdk = make_rsrc((char*)dkp + head, bytes);
-  const auto rdv = make_rsrc((char*)dvp + head, bytes);
-  const Rsrc rq = make_rsrc_words((const char*)qp + head, bytes);
-  const Rsrc rdo = make_rsrc_words((const char*)dop + head, bytes);
-  const Rsrc rl = make_rsrc_words(lsep + (size_t)bh * N, (uint32_t)N * 4);
-  const Rsrc rd = make_rsrc_words(deltap + (size_t)bh * N, (uint32_t)N * 4);
+  const auto rk = make_rsrc((const char*)kp + headkv, bytes);
+  const auto rdk = make_rsrc((char*)dkp + headkv, bytes);
+  const auto rdv = make_rsrc((char*)dvp + headkv, bytes);
 
   const int i_start = CAUSAL ? k0 : 0;
   const int nt = (N - i_start + BMQ - 1) / BMQ;
   DmaTile<BMQ, D, NW> dma;
   dma.init(w, lane);
-  dkdv_issue<D>(lds, i_start, dma, rq, rdo, rl, rd, w, lane);
+  {
+    const Rsrc rq = make_rsrc_words((const char*)qp + head0, bytes);
+    const Rsrc rdo = make_rsrc_words((const char*)dop + head0, bytes);
+    const Rsrc rl = make_rsrc_words(lsep + (size_t)bh0 * N, (uint32_t)N * 4);
+    const Rsrc rd = make_rsrc_words(deltap + (size_t)bh0 * N, (uint32_t)N * 4);
+    dkdv_issue<D>(lds, i_start, dma, rq, rdo, rl, rd, w, lane);
+  }
   lds_char* const vt = lds + S * BUF;
   if constexpr (VL) {
     DmaTile<BNK, D, NW> dmav;
     dmav.init(w, lane);
-    dmav.issue(make_rsrc_words((const char*)vp + head, bytes), vt, k0, w);
+    dmav.issue(make_rsrc_words((const char*)vp + headkv, bytes), vt, k0, w);
   }
 
   const int wk0 = k0 + 32 * w;
@@ -330,7 +358,7 @@ __global__ __launch_bounds__(64 * kBwdWaves, Dkdv<D>::kOcc) void dkdv_kernel(
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) kf[kk] = bload16(rk, (uint32_t)((krow * D + 16 * kk + 8 * h) * 2));
   if constexpr (!VL) {
-    const auto rv = make_rsrc((const char*)vp + head, bytes);
+    const auto rv = make_rsrc((const char*)vp + headkv, bytes);
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) vf[kk] = bload16(rv, (uint32_t)((krow * D + 16 * kk + 8 * h) * 2));
   }
@@ -340,14 +368,20 @@ __global__ __launch_bounds__(64 * kBwdWaves, Dkdv<D>::kOcc) void dkdv_kernel(
     land(kf[kk]);
     if constexpr (!VL) land(vf[kk]);
   }
-  if (S > 2 && nt > 1) dkdv_issue<D>(lds + (1 % S) * BUF, i_start + BMQ, dma, rq, rdo, rl, rd, w, lane);
-  if (S > 3 && nt > 2) dkdv_issue<D>(lds + (2 % S) * BUF, i_start + 2 * BMQ, dma, rq, rdo, rl, rd, w, lane);
+  {
+    const Rsrc rq = make_rsrc_words((const char*)qp + head0, bytes);
+    const Rsrc rdo = make_rsrc_words((const char*)dop + head0, bytes);
+    const Rsrc rl = make_rsrc_words(lsep + (size_t)bh0 * N, (uint32_t)N * 4);
+    const Rsrc rd = make_rsrc_words(deltap + (size_t)bh0 * N, (uint32_t)N * 4);
+    if (S > 2 && nt > 1) dkdv_issue<D>(lds + (1 % S) * BUF, i_start + BMQ, dma, rq, rdo, rl, rd, w, lane);
+    if (S > 3 && nt > 2) dkdv_issue<D>(lds + (2 % S) * BUF, i_start + 2 * BMQ, dma, rq, rdo, rl, rd, w, lane);
+  }
   if constexpr (VL)
-    dkdv_run<T, D, CAUSAL>(lds, nt, i_start, dma, rq, rdo, rl, rd, kf, VLds<D>{vt, 32 * w}, rdk, rdv, wk0, krow, c,
-                           scale, w, lane);
+    dkdv_run<T, D, CAUSAL>(lds, nt, i_start, dma, qp, dop, lsep, deltap, bh0, G, N, kf, VLds<D>{vt, 32 * w}, rdk,
+                           rdv, wk0, krow, c, scale, w, lane);
   else
-    dkdv_run<T, D, CAUSAL>(lds, nt, i_start, dma, rq, rdo, rl, rd, kf, VRegs{vf}, rdk, rdv, wk0, krow, c, scale, w,
-                           lane);
+    dkdv_run<T, D, CAUSAL>(lds, nt, i_start, dma, qp, dop, lsep, deltap, bh0, G, N, kf, VRegs{vf}, rdk, rdv, wk0,
+                           krow, c, scale, w, lane);
 }
 
 // One key tile of the dQ kernel for one wave (`edge`: the tile crosses the
@@ -440,7 +474,7 @@ __global__ __launch_bounds__(64 * kBwdWaves, 2) void dq_kernel(const void* __res
                                                             const void* __restrict__ vp, const void* __restrict__ dop,
                                                             const float* __restrict__ lsep,
                                                             const float* __restrict__ deltap, void* __restrict__ dqp,
-                                                            int N, int BH, int nqb, float c, float scale) {
+                                                            int N, int BH, int nqb, int H, int G, float c, float scale) {
   constexpr int NW = kBwdWaves, BM = 32 * NW, BN = kBwdTile, NKK = D / 16, NB = D / 32;
   constexpr int S = kBwdStages, TILE = BN * D * 2;
   __shared__ __attribute__((aligned(16))) char smem[S * 2 * TILE];
@@ -453,12 +487,14 @@ __global__ __launch_bounds__(64 * kBwdWaves, 2) void dq_kernel(const void* __res
   const int bh = x % BH;
   const int q0 = qb * BM;
   const size_t head = (size_t)bh * N * D * 2;
+  // K and V of the group (see the forward kernel).
+  const size_t headkv = (size_t)((bh / H) * (H / G) + (bh % H) / G) * N * D * 2;
   const uint32_t bytes = (uint32_t)N * D * 2;
   const auto rq = make_rsrc((const char*)qp + head, bytes);
   const auto rdo = make_rsrc((const char*)dop + head, bytes);
   const auto rdq = make_rsrc((char*)dqp + head, bytes);
-  const Rsrc rk = make_rsrc_words((const char*)kp + head, bytes);
-  const Rsrc rv = make_rsrc_words((const char*)vp + head, bytes);
+  const Rsrc rk = make_rsrc_words((const char*)kp + headkv, bytes);
+  const Rsrc rv = make_rsrc_words((const char*)vp + headkv, bytes);
 
   const int kend = CAUSAL ? min(N, q0 + BM) : N;
   const int nt = (kend + BN - 1) / BN;
@@ -530,10 +566,10 @@ hipError_t launch_preprocess(const PreArgs& a, hipStream_t st) {
 
 template <class T, int D, bool CAUSAL>
 static hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t st) {
-  const int BH = a.B * a.H;
+  const int BHkv = a.B * a.Hkv;
   const int nkb = (a.N + 127) / 128;
-  hipLaunchKernelGGL((dkdv_kernel<T, D, CAUSAL>), dim3(nkb * BH), dim3(256), 0, st, a.q, a.k, a.v, a.dO, a.lse,
-                     a.delta, a.dk, a.dv, a.N, BH, a.scale * kLog2e, a.scale);
+  hipLaunchKernelGGL((dkdv_kernel<T, D, CAUSAL>), dim3(nkb * BHkv), dim3(256), 0, st, a.q, a.k, a.v, a.dO, a.lse,
+                     a.delta, a.dk, a.dv, a.N, BHkv, a.H, a.H / a.Hkv, a.scale * kLog2e, a.scale);
   return hipGetLastError();
 }
 
@@ -542,7 +578,7 @@ static hipError_t launch_dq_t(const BwdArgs& a, hipStream_t st) {
   const int BH = a.B * a.H;
   const int nqb = (a.N + 127) / 128;
   hipLaunchKernelGGL((dq_kernel<T, D, CAUSAL>), dim3(nqb * BH), dim3(256), 0, st, a.q, a.k, a.v, a.dO, a.lse,
-                     a.delta, a.dq, a.N, BH, nqb, a.scale * kLog2e, a.scale);
+                     a.delta, a.dq, a.N, BH, nqb, a.H, a.H / a.Hkv, a.scale * kLog2e, a.scale);
   return hipGetLastError();
 }
 

@@ -368,7 +368,7 @@ __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_pipe_kernel(const void*
                                                                      const void* __restrict__ kp,
                                                                      const void* __restrict__ vp,
                                                                      void* __restrict__ op, float* __restrict__ lsep,
-                                                                     int N, int BH, int nqb, float c) {
+                                                                     int N, int BH, int nqb, int H, int G, float c) {
   constexpr int NW = kFwdWaves, S = kPipeStages, BM = 32 * NW, BN = kFwdBN, NKK = D / 16, NB = D / 32;
   constexpr int TILE = BN * D * 2, BUF = 2 * TILE;
   using Dma = DmaTile<BN, D, NW>;
@@ -388,11 +388,14 @@ __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_pipe_kernel(const void*
   const int bh = x % BH;
   const int q0 = qb * BM;
   const size_t head = (size_t)bh * N * D * 2;
+  // K and V of the group: query head h of batch b reads key/value head
+  // b (H / G) + h / G (G = 1 without grouping).
+  const size_t headkv = (size_t)((bh / H) * (H / G) + (bh % H) / G) * N * D * 2;
   const uint32_t bytes = (uint32_t)N * D * 2;
   const auto rq = make_rsrc((const char*)qp + head, bytes);
   const auto ro = make_rsrc((char*)op + head, bytes);
-  const Rsrc rk = make_rsrc_words((const char*)kp + head, bytes);
-  const Rsrc rv = make_rsrc_words((const char*)vp + head, bytes);
+  const Rsrc rk = make_rsrc_words((const char*)kp + headkv, bytes);
+  const Rsrc rv = make_rsrc_words((const char*)vp + headkv, bytes);
 
   const int kend = CAUSAL ? min(N, q0 + BM) : N;
   const int nt = (kend + BN - 1) / BN;
@@ -448,7 +451,7 @@ __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_kernel(const void* __re
                                                                 const void* __restrict__ kp,
                                                                 const void* __restrict__ vp, void* __restrict__ op,
                                                                 float* __restrict__ lsep, int N, int BH, int nqb,
-                                                                float c) {
+                                                                int H, int G, float c) {
   constexpr int NW = kFwdWaves, S = kFwdStages, BM = 32 * NW, BN = kFwdBN, NKK = D / 16, NB = D / 32;
   constexpr int TILE = BN * D * 2, BUF = 2 * TILE;
   using Dma = DmaTile<BN, D, NW>;
@@ -462,11 +465,14 @@ __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_kernel(const void* __re
   const int bh = x % BH;
   const int q0 = qb * BM;
   const size_t head = (size_t)bh * N * D * 2;
+  // K and V of the group: query head h of batch b reads key/value head
+  // b (H / G) + h / G (G = 1 without grouping).
+  const size_t headkv = (size_t)((bh / H) * (H / G) + (bh % H) / G) * N * D * 2;
   const uint32_t bytes = (uint32_t)N * D * 2;
   const auto rq = make_rsrc((const char*)qp + head, bytes);
   const auto ro = make_rsrc((char*)op + head, bytes);
-  const Rsrc rk = make_rsrc_words((const char*)kp + head, bytes);
-  const Rsrc rv = make_rsrc_words((const char*)vp + head, bytes);
+  const Rsrc rk = make_rsrc_words((const char*)kp + headkv, bytes);
+  const Rsrc rv = make_rsrc_words((const char*)vp + headkv, bytes);
 
   const int kend = CAUSAL ? min(N, q0 + BM) : N;
   const int nt = (kend + BN - 1) / BN;
@@ -514,10 +520,10 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   const int nqb = (a.N + BM - 1) / BM;
   if constexpr (kFwdPipelined<D>)
     hipLaunchKernelGGL((fwd_pipe_kernel<T, D, CAUSAL>), dim3(nqb * BH), dim3(64 * kFwdWaves), 0, st, a.q, a.k, a.v,
-                       a.o, a.lse, a.N, BH, nqb, a.scale * kLog2e);
+                       a.o, a.lse, a.N, BH, nqb, a.H, a.H / a.Hkv, a.scale * kLog2e);
   else
     hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL>), dim3(nqb * BH), dim3(64 * kFwdWaves), 0, st, a.q, a.k, a.v, a.o,
-                       a.lse, a.N, BH, nqb, a.scale * kLog2e);
+                       a.lse, a.N, BH, nqb, a.H, a.H / a.Hkv, a.scale * kLog2e);
   return hipGetLastError();
 }
 

@@ -11,6 +11,7 @@ struct FwdArgs {
   void* o;
   float* lse;
   int B, H, N, d;
+  int Hkv;  // key/value heads; H is a multiple of Hkv
   float scale;
   bool causal, bf16;
 };
@@ -27,6 +28,7 @@ struct BwdArgs {
   const float *lse, *delta;
   void *dq, *dk, *dv;
   int B, H, N, d;
+  int Hkv;  // key/value heads; H is a multiple of Hkv
   float scale;
   bool causal, bf16;
 };

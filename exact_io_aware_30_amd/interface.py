@@ -11,7 +11,9 @@ module.  This module provides the same three names on top of
   the row log-sum-exp L; backward calls ``fa_bwd_preprocess`` then
   ``fa_bwd`` (P is rebuilt from L, never stored).
 * ``flash_attn(q, k, v, causal=False, softmax_scale=None)`` -- the function
-  form; inputs are made contiguous, the scale defaults to 1/sqrt(D).
+  form; inputs are made contiguous, the scale defaults to 1/sqrt(D).  k and
+  v may carry fewer heads than q (Hkv dividing H): grouped-query attention,
+  query head h reading key/value head h / (H / Hkv).
 * ``FlashSelfAttention(embed_dim, num_heads, causal=False, bias=True)`` --
   x (B, N, E) -> (B, N, E): one input projection to Q, K, V, attention
   through the kernels, one output projection.  The two projections are
@@ -35,10 +37,13 @@ HEAD_DIMS = (32, 64, 128)
 
 
 def _check_inputs(q, k, v):
-    if q.dim() != 4:
-        raise ValueError("q, k, v must be (B, H, N, D)")
-    if k.shape != q.shape or v.shape != q.shape:
-        raise ValueError(f"q, k, v must have one shape, got {tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q must be (B, H, N, D) and k, v (B, Hkv, N, D)")
+    B, H, N, D = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2:] != q.shape[2:] or k.shape[1] < 1 \
+            or H % k.shape[1]:
+        raise ValueError(f"k and v must be (B, Hkv, N, D) with H a multiple of Hkv, got q {tuple(q.shape)}, "
+                         f"k {tuple(k.shape)}, v {tuple(v.shape)}")
     if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must all be float16 or all bfloat16")
     if q.shape[-1] not in HEAD_DIMS:
@@ -67,7 +72,8 @@ class FlashAttnFunction(torch.autograd.Function):
 
 
 def flash_attn(q, k, v, causal: bool = False, softmax_scale: float | None = None):
-    """softmax(q k^T * scale [+ causal mask]) v for (B, H, N, D) inputs."""
+    """softmax(q k^T * scale [+ causal mask]) v for q (B, H, N, D) and k, v
+    (B, Hkv, N, D), Hkv dividing H."""
     _check_inputs(q, k, v)
     scale = 1.0 / math.sqrt(q.shape[-1]) if softmax_scale is None else float(softmax_scale)
     if not (math.isfinite(scale) and scale > 0):

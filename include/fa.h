@@ -48,7 +48,7 @@ typedef enum { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
 
 enum {
   FA_OK = 0,
-  FA_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, bad mask/scale/dtype */
+  FA_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, bad mask/scale/dtype, bad Hkv */
   FA_ERR_UNSUPPORTED = -2, /* head dim not in {32,64,128}, or sizes beyond the limits above */
   FA_ERR_ALIGNMENT = -3,   /* a pointer is not 16-byte aligned */
   FA_ERR_HIP = -4,         /* the HIP runtime refused a launch */
@@ -110,6 +110,38 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
               const float* lse, const float* delta, void* dq,
               int B, int H, int N, int d, float scale, int causal,
               fa_dtype dt, void* stream);
+
+/*
+ * Grouped-query forms ("flash attention" note, "Versions and Evolution":
+ * FlashAttention-2 added multi-query and grouped-query attention;
+ * "flash-attn-triton" docs, "Scope", lists MQA/GQA as not yet done there).
+ * Hkv key/value heads serve H query heads, H a multiple of Hkv: query head h
+ * of a batch attends with key/value head h / (H / Hkv) of the same batch.
+ *   q, o, dO, dq   [B,H,N,d] of dt;    k, v, dk, dv   [B,Hkv,N,d] of dt;
+ *   lse, delta     [B,H,N] float32.
+ * The operation is that of the plain entry points with k and v repeated
+ * H / Hkv times along the head axis; dk and dv are the sums of the
+ * gradients over the query heads that share them.  Hkv = H is exactly
+ * fa_fwd / fa_bwd*; Hkv = 1 is multi-query attention.  Hkv < 1 or H not a
+ * multiple of Hkv returns FA_ERR_INVALID_ARG.  Everything else (sizes,
+ * masks, alignment, aliasing, streams, errors, determinism) is as above;
+ * the pre-pass is fa_bwd_preprocess on the query heads.
+ */
+int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int Hkv, int N, int d, float scale, int causal,
+               fa_dtype dt, void* stream);
+int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* dO,
+               const float* lse, const float* delta, void* dq, void* dk,
+               void* dv, int B, int H, int Hkv, int N, int d, float scale,
+               int causal, fa_dtype dt, void* stream);
+int fa_bwd_dkdv_gqa(const void* q, const void* k, const void* v,
+                    const void* dO, const float* lse, const float* delta,
+                    void* dk, void* dv, int B, int H, int Hkv, int N, int d,
+                    float scale, int causal, fa_dtype dt, void* stream);
+int fa_bwd_dq_gqa(const void* q, const void* k, const void* v, const void* dO,
+                  const float* lse, const float* delta, void* dq, int B,
+                  int H, int Hkv, int N, int d, float scale, int causal,
+                  fa_dtype dt, void* stream);
 
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* fa_status_string(int status);

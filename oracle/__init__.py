@@ -15,13 +15,16 @@ partial softmax results are written here too, but only so the tests can pin
 the identity they rely on.
 
 Modules:
-  attention  -- forward (O, L), backward (dQ, dK, dV, D), row/column samplers
+  attention  -- forward (O, L), backward (dQ, dK, dV, D), row/column samplers,
+                grouped-query forms
   softmax    -- safe softmax, the Fig. 3 per-tile recurrence, merge of partials
 """
 
 from .attention import (  # noqa: F401
     attention_forward,
     attention_backward,
+    attention_forward_gqa,
+    attention_backward_gqa,
     delta_rowsum,
     forward_rows,
     dq_rows,

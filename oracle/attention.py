@@ -141,6 +141,40 @@ def attention_backward(q, k, v, do, scale, causal, row_block=None):
 
 
 # ---------------------------------------------------------------------------
+# Grouped-query attention (flash attention note, "Versions and Evolution":
+# multi-query and grouped-query attention).  H query heads share Hkv key/value
+# heads, H a multiple of Hkv; query head h reads key/value head h // G,
+# G = H / Hkv.  By definition that is plain attention with every key/value
+# head repeated G times along the head axis, and the gradient of a shared key
+# or value head is the sum of the gradients of its G copies.
+# ---------------------------------------------------------------------------
+def _group(q, k):
+    H, Hkv = q.shape[1], k.shape[1]
+    if Hkv < 1 or H % Hkv:
+        raise ValueError(f"query heads {H} must be a multiple of key/value heads {Hkv}")
+    return H // Hkv
+
+
+def attention_forward_gqa(q, k, v, scale, causal, row_block=None):
+    """(O [B,H,N,d], L [B,H,N]) for q [B,H,N,d] and k, v [B,Hkv,N,d]."""
+    G = _group(q, k)
+    return attention_forward(q, np.repeat(_as64(k), G, axis=1), np.repeat(_as64(v), G, axis=1), scale, causal,
+                             row_block)
+
+
+def attention_backward_gqa(q, k, v, do, scale, causal, row_block=None):
+    """attention_backward for grouped heads: dk and dv [B,Hkv,N,d] sum the
+    gradients of the G query heads that read each key/value head."""
+    G = _group(q, k)
+    out = attention_backward(q, np.repeat(_as64(k), G, axis=1), np.repeat(_as64(v), G, axis=1), do, scale,
+                             causal, row_block)
+    B, Hkv, N, d = k.shape
+    for name in ("dk", "dv"):
+        out[name] = out[name].reshape(B, Hkv, G, N, d).sum(axis=2)
+    return out
+
+
+# ---------------------------------------------------------------------------
 # Samplers: the same definitions restricted to chosen rows or key columns of
 # one head, for sizes where the whole N x N matrix is too costly on the CPU.
 # ---------------------------------------------------------------------------

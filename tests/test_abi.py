@@ -32,6 +32,7 @@ def declared_functions():
 def test_header_functions_are_exported():
     names = declared_functions()
     assert names == sorted(["fa_fwd", "fa_bwd_preprocess", "fa_bwd", "fa_bwd_dkdv", "fa_bwd_dq",
+                            "fa_fwd_gqa", "fa_bwd_gqa", "fa_bwd_dkdv_gqa", "fa_bwd_dq_gqa",
                             "fa_status_string", "fa_version"])
     out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (fa_\w+)$", out, flags=re.M))
@@ -143,6 +144,35 @@ def test_bwd_rejects(p, fn):
     assert bwd(p, fn, **{outs[-1]: p[4]}) == ALIAS
     if len(outs) > 1:
         assert bwd(p, fn, **{outs[0]: p[11], outs[1]: p[11] + 64}) == ALIAS
+
+
+def test_gqa_rejects(p):
+    # fa_fwd_gqa(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, dt, stream)
+    f = lambda H=2, Hkv=1, **o: lib.fa_fwd_gqa(o.get("q", p[0]), o.get("k", p[1]), o.get("v", p[2]),  # noqa: E731
+                                               o.get("o", p[3]), o.get("lse", p[4]), 1, H, Hkv, 64, 64, 0.125, 0,
+                                               1, None)
+    assert f(Hkv=0) == INVALID
+    assert f(H=4, Hkv=3) == INVALID
+    assert f(H=2, Hkv=4) == INVALID
+    assert f(k=0) == INVALID
+    # o [1,2,64,64] = 16 KiB from p[3]; with Hkv = 1, k is 8 KiB: o at k + 8 KiB is clear, at k + 4 KiB overlaps
+    assert f(o=p[1] + 4096) == ALIAS
+    names = ["q", "k", "v", "do", "lse", "delta", "dq", "dk", "dv"]
+
+    def b(fn, H=2, Hkv=1, **over):
+        vals = {n: p[i] for i, n in enumerate(names)}
+        vals.update(over)
+        keep = {"fa_bwd_gqa": names, "fa_bwd_dkdv_gqa": [n for n in names if n != "dq"],
+                "fa_bwd_dq_gqa": [n for n in names if n not in ("dk", "dv")]}[fn]
+        return getattr(lib, fn)(*[vals[n] for n in keep], 1, H, Hkv, 64, 64, 0.125, 0, 1, None)
+
+    for fn in ("fa_bwd_gqa", "fa_bwd_dkdv_gqa", "fa_bwd_dq_gqa"):
+        assert b(fn, Hkv=0) == INVALID
+        assert b(fn, H=6, Hkv=4) == INVALID
+        assert b(fn, q=0) == INVALID
+    # dk [1,1,64,64] is 8 KiB: placed 4 KiB into v (8 KiB) it overlaps
+    assert b("fa_bwd_dkdv_gqa", dk=p[2] + 4096) == ALIAS
+    assert b("fa_bwd_gqa", dq=p[0] + 8192) == ALIAS  # q is 16 KiB with H = 2
 
 
 def test_binding_rejects_host_tensors():

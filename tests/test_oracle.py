@@ -362,3 +362,81 @@ def test_workload_counts():
     qr, *_ = workloads.make_inputs(workloads.WORKLOADS["ragged"])
     g = torch.Generator().manual_seed(1003)
     assert torch.equal(qr, (torch.randn((3, 12, 2000, 32), generator=g) * 4).half())
+
+
+# --------------------------------------------------------------------------
+# Grouped-query attention (flash attention note, "Versions and Evolution")
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("H,Hkv", [(4, 2), (6, 1), (3, 3)])
+def test_gqa_against_torch_fp64(causal, H, Hkv):
+    # torch autograd through repeat_interleave sums the gradients of the
+    # repeated key/value heads by itself; SDPA gives the forward.
+    B, N, d = 2, 23, 8
+    q, do = (rand((B, H, N, d), 60 + i) for i in range(2))
+    k, v = (rand((B, Hkv, N, d), 70 + i) for i in range(2))
+    scale = 0.4
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    G = H // Hkv
+    s = (tq @ tk.repeat_interleave(G, dim=1).transpose(-1, -2)) * scale
+    if causal:
+        s = s.masked_fill(torch.ones(N, N, dtype=torch.bool).triu(1), float("-inf"))
+    o_t = torch.softmax(s, dim=-1) @ tv.repeat_interleave(G, dim=1)
+    o_t.backward(torch.tensor(do))
+    sdpa = torch.nn.functional.scaled_dot_product_attention(
+        torch.tensor(q), torch.tensor(k).repeat_interleave(G, dim=1), torch.tensor(v).repeat_interleave(G, dim=1),
+        is_causal=causal, scale=scale)
+    out = oracle.attention_backward_gqa(q, k, v, do, scale, causal)
+    o, _ = oracle.attention_forward_gqa(q, k, v, scale, causal)
+    assert out["dk"].shape == k.shape and out["dv"].shape == v.shape and out["dq"].shape == q.shape
+
+    def rel(a, b):
+        return np.max(np.abs(a - b)) / np.max(np.abs(b))
+
+    assert rel(o, sdpa.numpy()) <= 1e-12
+    assert rel(out["o"], o_t.detach().numpy()) <= 1e-12
+    for name, t in (("dq", tq), ("dk", tk), ("dv", tv)):
+        assert rel(out[name], t.grad.numpy()) <= 1e-12, name
+
+
+def test_gqa_one_group_is_plain_attention_and_mqa_sums_heads():
+    B, H, N, d = 1, 4, 19, 6
+    q, k, v, do = (rand((B, H, N, d), 80 + i) for i in range(4))
+    plain = attention_backward(q, k, v, do, 0.5, True)
+    grouped = oracle.attention_backward_gqa(q, k, v, do, 0.5, True)
+    for name in ("o", "dq", "dk", "dv", "lse"):
+        np.testing.assert_array_equal(grouped[name], plain[name])
+    # multi-query: one key/value head read by every query head; its gradient
+    # is the sum of what each head alone would give it
+    k1, v1 = k[:, :1], v[:, :1]
+    mqa = oracle.attention_backward_gqa(q, k1, v1, do, 0.5, False)
+    dk = sum(attention_backward(q[:, h:h + 1], k1, v1, do[:, h:h + 1], 0.5, False)["dk"] for h in range(H))
+    dv = sum(attention_backward(q[:, h:h + 1], k1, v1, do[:, h:h + 1], 0.5, False)["dv"] for h in range(H))
+    np.testing.assert_allclose(mqa["dk"], dk, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(mqa["dv"], dv, rtol=1e-13, atol=1e-13)
+    with pytest.raises(ValueError):
+        oracle.attention_forward_gqa(q, k[:, :3], v[:, :3], 0.5, False)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_gradients_match_central_differences(causal):
+    rng = np.random.default_rng(515 + int(causal))
+    H, Hkv, N, d = 4, 2, 5, 3
+    q, do = (rng.standard_normal((1, H, N, d)) for _ in range(2))
+    k, v = (rng.standard_normal((1, Hkv, N, d)) for _ in range(2))
+    out = oracle.attention_backward_gqa(q, k, v, do, 0.7, causal)
+    h = 1e-6
+
+    def f(kk, vv):
+        o, _ = oracle.attention_forward_gqa(q, kk, vv, 0.7, causal)
+        return float(np.sum(do * o))
+
+    for name, x in (("dk", k), ("dv", v)):
+        g = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            g[idx] = (f(*[xp if x is t else t for t in (k, v)]) - f(*[xm if x is t else t for t in (k, v)])) / (2 * h)
+        assert np.max(np.abs(g - out[name])) / np.max(np.abs(g)) <= 1e-7, name

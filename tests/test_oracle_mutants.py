@@ -32,6 +32,14 @@ MUTANTS = {
     "transposed_p_in_bwd_pv": ("ob = p @ vh[:nk]", "ob = p.T @ vh[:nk]"),
     "transposed_p_in_fwd_pv": ("o[b, h, r0:r1] = p @ v[b, h, :nk]", "o[b, h, r0:r1] = p.T @ v[b, h, :nk]"),
     "delta_wrong_axis": ("dsum = np.sum(p * dp, axis=1)", "dsum = np.sum(p * dp, axis=0)"),
+    # grouped-query attention: query head h must read key/value head h // G
+    "gqa_heads_interleaved": ("return attention_forward(q, np.repeat(_as64(k), G, axis=1), np.repeat(_as64(v), G, axis=1)",
+                              "return attention_forward(q, np.tile(_as64(k), (1, G, 1, 1)), "
+                              "np.tile(_as64(v), (1, G, 1, 1))"),
+    "gqa_grad_not_summed": ('out[name] = out[name].reshape(B, Hkv, G, N, d).sum(axis=2)',
+                            'out[name] = out[name].reshape(B, Hkv, G, N, d)[:, :, 0]'),
+    "gqa_grad_wrong_group_axis": ('out[name] = out[name].reshape(B, Hkv, G, N, d).sum(axis=2)',
+                                  'out[name] = out[name].reshape(B, G, Hkv, N, d).sum(axis=1)'),
 }
 
 
@@ -84,6 +92,22 @@ def pin_battery(m):
         np.testing.assert_allclose(out["o"], ot.detach().numpy(), rtol=1e-10, atol=1e-12)
         np.testing.assert_allclose(out["delta"], out["delta_o"], rtol=1e-10, atol=1e-12)
         assert np.max(np.abs(out["dk"].sum(axis=2))) <= 1e-10
+    # grouped-query forms against torch fp64 through repeat_interleave
+    for causal in (False, True):
+        H, Hkv, N, d = 4, 2, 5, 3
+        q, do = (rng.standard_normal((1, H, N, d)) for _ in range(2))
+        k, v = (rng.standard_normal((1, Hkv, N, d)) for _ in range(2))
+        tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        s = (tq @ tk.repeat_interleave(2, dim=1).transpose(-1, -2)) * 0.8
+        if causal:
+            s = s.masked_fill(torch.ones(N, N, dtype=torch.bool).triu(1), float("-inf"))
+        ot = torch.softmax(s, -1) @ tv.repeat_interleave(2, dim=1)
+        ot.backward(torch.tensor(do))
+        o, _ = m.attention_forward_gqa(q, k, v, 0.8, causal)
+        out = m.attention_backward_gqa(q, k, v, do, 0.8, causal)
+        np.testing.assert_allclose(o, ot.detach().numpy(), rtol=1e-10, atol=1e-12)
+        for name, t in (("dq", tq), ("dk", tk), ("dv", tv)):
+            np.testing.assert_allclose(out[name], t.grad.numpy(), rtol=1e-9, atol=1e-11)
 
 
 def test_real_oracle_passes_battery():
