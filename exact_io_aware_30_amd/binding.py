@@ -41,6 +41,10 @@ _SIG = {
     "fa_bwd_gqa": [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _i, _p],
     "fa_bwd_dkdv_gqa": [_p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _i, _p],
     "fa_bwd_dq_gqa": [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _i, _p],
+    "fa_fwd_ex": [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _i, _i, _p],
+    "fa_bwd_ex": [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _i, _i, _p],
+    "fa_bwd_dkdv_ex": [_p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _i, _i, _p],
+    "fa_bwd_dq_ex": [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _i, _i, _p],
     "fa_status_string": [_i],
     "fa_version": [],
 }
@@ -195,25 +199,83 @@ def fa_bwd_dq_gqa(q, k, v, do, lse, delta, dq, scale: float, causal: bool) -> No
                               _DT[q.dtype], _stream(q)), "fa_bwd_dq_gqa")
 
 
-def attention_forward(q, k, v, scale: float, causal: bool):
+def _window(window, causal):
+    """(left, right) for fa_*_ex: `window` on top of the causal flag."""
+    left, right = (-1, -1) if window is None else (int(window[0]), int(window[1]))
+    if left < -1 or right < -1:
+        raise ValueError("window bounds must be >= -1 (-1: no bound)")
+    if causal:
+        right = 0 if right < 0 else min(right, 0)
+    return left, right
+
+
+def fa_fwd_ex(q, k, v, o, lse, scale: float, window) -> None:
+    B, H, N, d = _bhnd(q, "q")
+    Hkv = _kv(q, ((k, "k"), (v, "v")))
+    _same(q, (o, "o"))
+    _rows(q, (lse, "lse"))
+    wl, wr = window
+    _check(_lib.fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, Hkv, N, d,
+                          float(scale), int(wl), int(wr), _DT[q.dtype], _stream(q)), "fa_fwd_ex")
+
+
+def fa_bwd_ex(q, k, v, do, lse, delta, dq, dk, dv, scale: float, window) -> None:
+    B, H, N, d = _bhnd(q, "q")
+    Hkv = _kv(q, ((k, "k"), (v, "v"), (dk, "dk"), (dv, "dv")))
+    _same(q, (do, "do"), (dq, "dq"))
+    _rows(q, (lse, "lse"), (delta, "delta"))
+    wl, wr = window
+    _check(_lib.fa_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                          delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, N, d,
+                          float(scale), int(wl), int(wr), _DT[q.dtype], _stream(q)), "fa_bwd_ex")
+
+
+def fa_bwd_dkdv_ex(q, k, v, do, lse, delta, dk, dv, scale: float, window) -> None:
+    B, H, N, d = _bhnd(q, "q")
+    Hkv = _kv(q, ((k, "k"), (v, "v"), (dk, "dk"), (dv, "dv")))
+    _same(q, (do, "do"))
+    _rows(q, (lse, "lse"), (delta, "delta"))
+    wl, wr = window
+    _check(_lib.fa_bwd_dkdv_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                               delta.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, N, d, float(scale),
+                               int(wl), int(wr), _DT[q.dtype], _stream(q)), "fa_bwd_dkdv_ex")
+
+
+def fa_bwd_dq_ex(q, k, v, do, lse, delta, dq, scale: float, window) -> None:
+    B, H, N, d = _bhnd(q, "q")
+    Hkv = _kv(q, ((k, "k"), (v, "v")))
+    _same(q, (do, "do"), (dq, "dq"))
+    _rows(q, (lse, "lse"), (delta, "delta"))
+    wl, wr = window
+    _check(_lib.fa_bwd_dq_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                             delta.data_ptr(), dq.data_ptr(), B, H, Hkv, N, d, float(scale), int(wl), int(wr),
+                             _DT[q.dtype], _stream(q)), "fa_bwd_dq_ex")
+
+
+def attention_forward(q, k, v, scale: float, causal: bool, window=None):
     """(o, lse) with o like q and lse float32 [B, H, N]; k and v may have
-    fewer heads than q (grouped-query attention)."""
+    fewer heads than q (grouped-query attention); window = (left, right)
+    keeps keys i - left .. i + right for query i (-1: no bound)."""
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
-    if k.dim() == 4 and k.shape[1] != q.shape[1]:
+    if window is not None:
+        fa_fwd_ex(q, k, v, o, lse, scale, _window(window, causal))
+    elif k.dim() == 4 and k.shape[1] != q.shape[1]:
         fa_fwd_gqa(q, k, v, o, lse, scale, causal)
     else:
         fa_fwd(q, k, v, o, lse, scale, causal)
     return o, lse
 
 
-def attention_backward(q, k, v, o, do, lse, scale: float, causal: bool):
+def attention_backward(q, k, v, o, do, lse, scale: float, causal: bool, window=None):
     """(dq, dk, dv, delta): the pre-pass then the two backward kernels; dk and
     dv are shaped like k and v."""
     delta = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     fa_bwd_preprocess(o, do, delta)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    if k.dim() == 4 and k.shape[1] != q.shape[1]:
+    if window is not None:
+        fa_bwd_ex(q, k, v, do, lse, delta, dq, dk, dv, scale, _window(window, causal))
+    elif k.dim() == 4 and k.shape[1] != q.shape[1]:
         fa_bwd_gqa(q, k, v, do, lse, delta, dq, dk, dv, scale, causal)
     else:
         fa_bwd(q, k, v, do, lse, delta, dq, dk, dv, scale, causal)

@@ -40,10 +40,18 @@ int check_common(int B, int H, int N, int d, fa_dtype dt) {
   return FA_OK;
 }
 
-int check_scale_mask(float scale, int causal) {
+int check_scale_window(float scale, int wl, int wr) {
   if (!(std::isfinite(scale) && scale > 0.f)) return FA_ERR_INVALID_ARG;
-  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (wl < -1 || wr < -1) return FA_ERR_INVALID_ARG;
   return FA_OK;
+}
+
+// The causal flag as a window: (unbounded, 0); the full mask: (unbounded, unbounded).
+bool causal_window(int causal, int* wl, int* wr) {
+  if (causal != 0 && causal != 1) return false;
+  *wl = -1;
+  *wr = causal ? 0 : -1;
+  return true;
 }
 
 // outs must not overlap each other or any of ins.
@@ -66,13 +74,13 @@ int check_heads(int H, int Hkv) {
 
 int check_bwd(const void* q, const void* k, const void* v, const void* dO, const float* lse, const float* delta,
               const void* dq, const void* dk, const void* dv, int B, int H, int Hkv, int N, int d, float scale,
-              int causal, fa_dtype dt, bool want_dq, bool want_dkdv) {
+              int wl, int wr, fa_dtype dt, bool want_dq, bool want_dkdv) {
   if (!q || !k || !v || !dO || !lse || !delta) return FA_ERR_INVALID_ARG;
   if ((want_dq && !dq) || (want_dkdv && (!dk || !dv))) return FA_ERR_INVALID_ARG;
   int rc = check_common(B, H, N, d, dt);
   if (rc) return rc;
   if ((rc = check_heads(H, Hkv))) return rc;
-  if ((rc = check_scale_mask(scale, causal))) return rc;
+  if ((rc = check_scale_window(scale, wl, wr))) return rc;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) || !aligned16(lse) || !aligned16(delta))
     return FA_ERR_ALIGNMENT;
   if ((want_dq && !aligned16(dq)) || (want_dkdv && (!aligned16(dk) || !aligned16(dv)))) return FA_ERR_ALIGNMENT;
@@ -92,29 +100,95 @@ int check_bwd(const void* q, const void* k, const void* v, const void* dO, const
 
 fa::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* dO, const float* lse,
                      const float* delta, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d,
-                     float scale, int causal, fa_dtype dt) {
-  return fa::BwdArgs{q, k, v, dO, lse, delta, dq, dk, dv, B, H, N, d, Hkv, scale, causal == 1, dt == FA_BF16};
+                     float scale, int wl, int wr, fa_dtype dt) {
+  return fa::BwdArgs{q, k, v, dO, lse, delta, dq, dk, dv, B, H, N, d, Hkv, scale, wl, wr, dt == FA_BF16};
 }
 
 }  // namespace
 
 extern "C" {
 
-int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N,
-               int d, float scale, int causal, fa_dtype dt, void* stream) {
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N, int d,
+              float scale, int window_left, int window_right, fa_dtype dt, void* stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
   int rc = check_common(B, H, N, d, dt);
   if (rc) return rc;
   if ((rc = check_heads(H, Hkv))) return rc;
-  if ((rc = check_scale_mask(scale, causal))) return rc;
+  if ((rc = check_scale_window(scale, window_left, window_right))) return rc;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGNMENT;
   const long long tb = static_cast<long long>(B) * H * N * d * 2, rb = static_cast<long long>(B) * H * N * 4;
   const long long kvb = static_cast<long long>(B) * Hkv * N * d * 2;
   const Range ins[3] = {range_of(q, tb), range_of(k, kvb), range_of(v, kvb)};
   const Range outs[2] = {range_of(o, tb), range_of(lse, rb)};
   if ((rc = check_alias(outs, 2, ins, 3))) return rc;
-  const fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, Hkv, scale, causal == 1, dt == FA_BF16};
+  const fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, Hkv, scale, window_left, window_right, dt == FA_BF16};
   return hip_status(fa::launch_fwd(a, static_cast<hipStream_t>(stream)));
+}
+
+int fa_bwd_dkdv_ex(const void* q, const void* k, const void* v, const void* dO, const float* lse, const float* delta,
+                   void* dk, void* dv, int B, int H, int Hkv, int N, int d, float scale, int window_left,
+                   int window_right, fa_dtype dt, void* stream) {
+  const int rc = check_bwd(q, k, v, dO, lse, delta, nullptr, dk, dv, B, H, Hkv, N, d, scale, window_left,
+                           window_right, dt, false, true);
+  if (rc) return rc;
+  const fa::BwdArgs a =
+      bwd_args(q, k, v, dO, lse, delta, nullptr, dk, dv, B, H, Hkv, N, d, scale, window_left, window_right, dt);
+  return hip_status(fa::launch_bwd_dkdv(a, static_cast<hipStream_t>(stream)));
+}
+
+int fa_bwd_dq_ex(const void* q, const void* k, const void* v, const void* dO, const float* lse, const float* delta,
+                 void* dq, int B, int H, int Hkv, int N, int d, float scale, int window_left, int window_right,
+                 fa_dtype dt, void* stream) {
+  const int rc = check_bwd(q, k, v, dO, lse, delta, dq, nullptr, nullptr, B, H, Hkv, N, d, scale, window_left,
+                           window_right, dt, true, false);
+  if (rc) return rc;
+  const fa::BwdArgs a =
+      bwd_args(q, k, v, dO, lse, delta, dq, nullptr, nullptr, B, H, Hkv, N, d, scale, window_left, window_right, dt);
+  return hip_status(fa::launch_bwd_dq(a, static_cast<hipStream_t>(stream)));
+}
+
+int fa_bwd_ex(const void* q, const void* k, const void* v, const void* dO, const float* lse, const float* delta,
+              void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d, float scale, int window_left,
+              int window_right, fa_dtype dt, void* stream) {
+  int rc = check_bwd(q, k, v, dO, lse, delta, dq, dk, dv, B, H, Hkv, N, d, scale, window_left, window_right, dt,
+                     true, true);
+  if (rc) return rc;
+  const fa::BwdArgs a =
+      bwd_args(q, k, v, dO, lse, delta, dq, dk, dv, B, H, Hkv, N, d, scale, window_left, window_right, dt);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((rc = hip_status(fa::launch_bwd_dkdv(a, st)))) return rc;
+  return hip_status(fa::launch_bwd_dq(a, st));
+}
+
+int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N,
+               int d, float scale, int causal, fa_dtype dt, void* stream) {
+  int wl, wr;
+  if (!causal_window(causal, &wl, &wr)) return FA_ERR_INVALID_ARG;
+  return fa_fwd_ex(q, k, v, o, lse, B, H, Hkv, N, d, scale, wl, wr, dt, stream);
+}
+
+int fa_bwd_dkdv_gqa(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                    const float* delta, void* dk, void* dv, int B, int H, int Hkv, int N, int d, float scale,
+                    int causal, fa_dtype dt, void* stream) {
+  int wl, wr;
+  if (!causal_window(causal, &wl, &wr)) return FA_ERR_INVALID_ARG;
+  return fa_bwd_dkdv_ex(q, k, v, dO, lse, delta, dk, dv, B, H, Hkv, N, d, scale, wl, wr, dt, stream);
+}
+
+int fa_bwd_dq_gqa(const void* q, const void* k, const void* v, const void* dO, const float* lse, const float* delta,
+                  void* dq, int B, int H, int Hkv, int N, int d, float scale, int causal, fa_dtype dt,
+                  void* stream) {
+  int wl, wr;
+  if (!causal_window(causal, &wl, &wr)) return FA_ERR_INVALID_ARG;
+  return fa_bwd_dq_ex(q, k, v, dO, lse, delta, dq, B, H, Hkv, N, d, scale, wl, wr, dt, stream);
+}
+
+int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* dO, const float* lse, const float* delta,
+               void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d, float scale, int causal,
+               fa_dtype dt, void* stream) {
+  int wl, wr;
+  if (!causal_window(causal, &wl, &wr)) return FA_ERR_INVALID_ARG;
+  return fa_bwd_ex(q, k, v, dO, lse, delta, dq, dk, dv, B, H, Hkv, N, d, scale, wl, wr, dt, stream);
 }
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
@@ -134,37 +208,6 @@ int fa_bwd_preprocess(const void* o, const void* dO, float* delta, int B, int H,
   if ((rc = check_alias(outs, 1, ins, 2))) return rc;
   const fa::PreArgs a{o, dO, delta, B, H, N, d, dt == FA_BF16};
   return hip_status(fa::launch_preprocess(a, static_cast<hipStream_t>(stream)));
-}
-
-int fa_bwd_dkdv_gqa(const void* q, const void* k, const void* v, const void* dO, const float* lse,
-                    const float* delta, void* dk, void* dv, int B, int H, int Hkv, int N, int d, float scale,
-                    int causal, fa_dtype dt, void* stream) {
-  const int rc =
-      check_bwd(q, k, v, dO, lse, delta, nullptr, dk, dv, B, H, Hkv, N, d, scale, causal, dt, false, true);
-  if (rc) return rc;
-  const fa::BwdArgs a = bwd_args(q, k, v, dO, lse, delta, nullptr, dk, dv, B, H, Hkv, N, d, scale, causal, dt);
-  return hip_status(fa::launch_bwd_dkdv(a, static_cast<hipStream_t>(stream)));
-}
-
-int fa_bwd_dq_gqa(const void* q, const void* k, const void* v, const void* dO, const float* lse, const float* delta,
-                  void* dq, int B, int H, int Hkv, int N, int d, float scale, int causal, fa_dtype dt,
-                  void* stream) {
-  const int rc =
-      check_bwd(q, k, v, dO, lse, delta, dq, nullptr, nullptr, B, H, Hkv, N, d, scale, causal, dt, true, false);
-  if (rc) return rc;
-  const fa::BwdArgs a = bwd_args(q, k, v, dO, lse, delta, dq, nullptr, nullptr, B, H, Hkv, N, d, scale, causal, dt);
-  return hip_status(fa::launch_bwd_dq(a, static_cast<hipStream_t>(stream)));
-}
-
-int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* dO, const float* lse, const float* delta,
-               void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d, float scale, int causal,
-               fa_dtype dt, void* stream) {
-  int rc = check_bwd(q, k, v, dO, lse, delta, dq, dk, dv, B, H, Hkv, N, d, scale, causal, dt, true, true);
-  if (rc) return rc;
-  const fa::BwdArgs a = bwd_args(q, k, v, dO, lse, delta, dq, dk, dv, B, H, Hkv, N, d, scale, causal, dt);
-  const hipStream_t st = static_cast<hipStream_t>(stream);
-  if ((rc = hip_status(fa::launch_bwd_dkdv(a, st)))) return rc;
-  return hip_status(fa::launch_bwd_dq(a, st));
 }
 
 int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse, const float* delta,
@@ -187,7 +230,7 @@ const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
     case FA_ERR_INVALID_ARG:
-      return "invalid argument (null pointer, size < 1, bad dtype, mask or scale, or H not a multiple of Hkv)";
+      return "invalid argument (null pointer, size < 1, bad dtype, mask, window or scale, or H not a multiple of Hkv)";
     case FA_ERR_UNSUPPORTED: return "unsupported (head dim not 32/64/128, or sizes beyond the library limits)";
     case FA_ERR_ALIGNMENT: return "a pointer is not 16-byte aligned";
     case FA_ERR_HIP: return "the HIP runtime refused a kernel launch";
@@ -196,6 +239,6 @@ const char* fa_status_string(int status) {
   }
 }
 
-int fa_version(void) { return 200; }
+int fa_version(void) { return 300; }
 
 }  // extern "C"

@@ -139,19 +139,26 @@ __device__ __forceinline__ void dkdv_scores(const lds_char* qt, const lds_char* 
   prio_mfma_end();
 }
 
-// Phase 2 (VALU): mask (only when `edge`: the tile crosses the diagonal of
-// the wave's keys), P = 2^(S c - L log2 e), dS = P (dP - D), packed into
-// MFMA operands.  st holds the tile's L (st[0..63]) and D (st[64..127]).
+// Phase 2 (VALU): mask (only when `edge`: the tile crosses an edge of the
+// window of some of the wave's keys), P = 2^(S c - L log2 e),
+// dS = P (dP - D), packed into MFMA operands.  st holds the tile's L
+// (st[0..63]) and D (st[64..127]).
 template <class T, int NA>
 __device__ __forceinline__ void dkdv_probs(f32x16* s, f32x16* dp, const float* st, u32x4* pf, u32x4* dsf, bool edge,
-                                           int i0, int krow, float c, int lane) {
+                                           int i0, int krow, Win win, float c, int lane) {
   const int h = lane >> 5;
   if (edge) {
+    // Query i sees the lane's key iff krow - right <= i <= krow + left;
+    // compared as offsets 32a + 8(r/4) + r%4 from i0 + 4h.
+    const int rlo = (win.right < 0 ? kUnbounded : krow - win.right) - i0 - 4 * h;
+    const int rhi = (win.left < 0 ? (1 << 30) : krow + win.left) - i0 - 4 * h;
 #pragma unroll
     for (int a = 0; a < NA; ++a)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (krow > i0 + 32 * a + 8 * (r >> 2) + 4 * h + (r & 3)) s[a][r] = -INFINITY;
+      for (int r = 0; r < 16; ++r) {
+        const int off = 32 * a + 8 * (r >> 2) + (r & 3);
+        if ((win.right >= 0 && off < rlo) || (win.left >= 0 && off > rhi)) s[a][r] = -INFINITY;
+      }
   }
 #pragma unroll
   for (int a = 0; a < NA; ++a)
@@ -199,11 +206,11 @@ __device__ __forceinline__ void dkdv_accum(const lds_char* qt, const lds_char* d
 template <class T, int D, int NA, class VOp>
 __device__ __forceinline__ void dkdv_tile(const lds_char* qt, const lds_char* dot, const float* st, const u32x4* kf,
                                           const VOp& vop, f32x16* dka, f32x16* dva, bool edge, int i0, int krow,
-                                          float c, int lane) {
+                                          Win win, float c, int lane) {
   f32x16 s[NA], dp[NA];
   u32x4 pf[2 * NA], dsf[2 * NA];
   dkdv_scores<T, D, NA>(qt, dot, kf, vop, s, dp, lane);
-  dkdv_probs<T, NA>(s, dp, st, pf, dsf, edge, i0, krow, c, lane);
+  dkdv_probs<T, NA>(s, dp, st, pf, dsf, edge, i0, krow, win, c, lane);
   dkdv_accum<T, D, NA>(qt, dot, pf, dsf, dka, dva, lane);
 }
 
@@ -223,11 +230,11 @@ __device__ __forceinline__ void dkdv_issue(lds_char* b, int i0, const DmaTile<Dk
 // One ring step on query tile t, held in ring buffer IDX = t % S (a
 // compile-time index, so LDS operand addresses are register + immediate):
 // wait and barrier, DMA of tile t + S - 1, then the math.
-template <class T, int D, bool CAUSAL, int IDX, class VOp>
+template <class T, int D, bool MASK, int IDX, class VOp>
 __device__ __forceinline__ void dkdv_step(lds_char* lds, int t, int nt, int i_start,
                                           const DmaTile<Dkdv<D>::kTile, D, kBwdWaves>& dma, Rsrc rq, Rsrc rdo, Rsrc rl,
                                           Rsrc rd, const u32x4* kf, const VOp& vop, f32x16* dka, f32x16* dva,
-                                          int wk0, int krow, float c, int w, int lane) {
+                                          int wk0, int krow, Win win, float c, int w, int lane) {
   constexpr int S = Dkdv<D>::kStages, BMQ = Dkdv<D>::kTile, TILE = BMQ * D * 2, BUF = 2 * TILE + 2 * kStatsRows * 4;
   constexpr int PT = 2 * DmaTile<Dkdv<D>::kTile, D, kBwdWaves>::PER;  // per tile; waves 0, 1 add an L or D dword
   if (w < 2)
@@ -237,10 +244,12 @@ __device__ __forceinline__ void dkdv_step(lds_char* lds, int t, int nt, int i_st
   const int i0 = i_start + t * BMQ;
   if (t + S - 1 < nt) dkdv_issue<D>(lds + ((IDX + S - 1) % S) * BUF, i0 + (S - 1) * BMQ, dma, rq, rdo, rl, rd, w, lane);
   __builtin_amdgcn_sched_barrier(0);
-  if (CAUSAL && i0 + BMQ - 1 < wk0) return;  // every query of the tile precedes every key of the wave
+  // No query of the tile sees any key of the wave.
+  if (MASK && (i0 + BMQ <= win.query_lo(wk0) || i0 >= win.query_hi(wk0 + 31, 1 << 30))) return;
   const lds_char* cur = lds + IDX * BUF;
   const float* st = (const float*)(cur + 2 * TILE);
-  dkdv_tile<T, D, BMQ / 32>(cur, cur + TILE, st, kf, vop, dka, dva, CAUSAL && i0 < wk0 + 31, i0, krow, c, lane);
+  const bool edge = MASK && !win.all_visible(i0, i0 + BMQ - 1, wk0, wk0 + 31);
+  dkdv_tile<T, D, BMQ / 32>(cur, cur + TILE, st, kf, vop, dka, dva, edge, i0, krow, win, c, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -252,19 +261,20 @@ __device__ __forceinline__ void dkdv_step(lds_char* lds, int t, int nt, int i_st
 //   S = Q K^T, dP = dO V^T          (lane = key, registers = queries)
 //   P = 2^(S c - L2), dS = P (dP - D)
 //   dV^T += dO^T P, dK^T += Q^T dS  (A operands by transposed LDS reads)
-// Under the causal mask query tiles start at the block's first key, and only
-// tiles that cross the diagonal are masked.
+// With a window (the causal mask is one) the query tiles cover only the
+// queries that see some key of the block, and only tiles that cross an edge
+// of a key's window are masked.
 // ---------------------------------------------------------------------------
 // The ring loop over query tiles, once per query head of the key/value
 // head's group (G = 1 without grouping: the gradients of a shared K and V
 // are the sums over the heads that read them), and the final store of dK
 // and dV.  The first head's first tiles were issued by the caller.
-template <class T, int D, bool CAUSAL, class VOp>
+template <class T, int D, bool MASK, class VOp>
 __device__ __forceinline__ void dkdv_run(lds_char* lds, int nt, int i_start, const DmaTile<Dkdv<D>::kTile, D, kBwdWaves>& dma,
                                          const void* qp, const void* dop, const float* lsep, const float* deltap,
                                          int bh0, int G, int N, const u32x4* kf, const VOp& vop,
                                          __amdgpu_buffer_rsrc_t rdk, __amdgpu_buffer_rsrc_t rdv, int wk0, int krow,
-                                         float c, float scale, int w, int lane) {
+                                         Win win, float c, float scale, int w, int lane) {
   constexpr int S = Dkdv<D>::kStages, NB = D / 32, BMQ = Dkdv<D>::kTile;
   constexpr int BUF = 2 * BMQ * D * 2 + 2 * kStatsRows * 4;
   const uint32_t bytes = (uint32_t)N * D * 2;
@@ -286,18 +296,19 @@ __device__ __forceinline__ void dkdv_run(lds_char* lds, int nt, int i_start, con
       if (S > 3 && nt > 2) dkdv_issue<D>(lds + (2 % S) * BUF, i_start + 2 * BMQ, dma, rq, rdo, rl, rd, w, lane);
     }
     for (int t = 0; t < nt; t += S) {
-      dkdv_step<T, D, CAUSAL, 0>(lds, t, nt, i_start, dma, rq, rdo, rl, rd, kf, vop, dka, dva, wk0, krow, c, w, lane);
+      dkdv_step<T, D, MASK, 0>(lds, t, nt, i_start, dma, rq, rdo, rl, rd, kf, vop, dka, dva, wk0, krow, win, c, w,
+                               lane);
       if (t + 1 < nt)
-        dkdv_step<T, D, CAUSAL, 1>(lds, t + 1, nt, i_start, dma, rq, rdo, rl, rd, kf, vop, dka, dva, wk0, krow, c, w,
-                                   lane);
+        dkdv_step<T, D, MASK, 1>(lds, t + 1, nt, i_start, dma, rq, rdo, rl, rd, kf, vop, dka, dva, wk0, krow, win, c,
+                                 w, lane);
       if constexpr (S > 2)
         if (t + 2 < nt)
-          dkdv_step<T, D, CAUSAL, 2 % S>(lds, t + 2, nt, i_start, dma, rq, rdo, rl, rd, kf, vop, dka, dva, wk0, krow,
-                                         c, w, lane);
+          dkdv_step<T, D, MASK, 2 % S>(lds, t + 2, nt, i_start, dma, rq, rdo, rl, rd, kf, vop, dka, dva, wk0, krow,
+                                       win, c, w, lane);
       if constexpr (S > 3)
         if (t + 3 < nt)
-          dkdv_step<T, D, CAUSAL, 3 % S>(lds, t + 3, nt, i_start, dma, rq, rdo, rl, rd, kf, vop, dka, dva, wk0, krow,
-                                         c, w, lane);
+          dkdv_step<T, D, MASK, 3 % S>(lds, t + 3, nt, i_start, dma, rq, rdo, rl, rd, kf, vop, dka, dva, wk0, krow,
+                                       win, c, w, lane);
     }
   }
   store_rows<T, D>(rdk, krow, dka, scale, lane);
@@ -306,11 +317,15 @@ __device__ __forceinline__ void dkdv_run(lds_char* lds, int nt, int i_start, con
 
 // Grid: key blocks x key/value heads (BHkv = B * H / G of them); the query
 // heads of key/value head hkv of batch b are b H + hkv G .. + G - 1.
-template <class T, int D, bool CAUSAL>
+template <class T, int D, int MODE>
 __global__ __launch_bounds__(64 * kBwdWaves, Dkdv<D>::kOcc) void dkdv_kernel(
     const void* __restrict__ qp, const void* __restrict__ kp, const void* __restrict__ vp,
     const void* __restrict__ dop, const float* __restrict__ lsep, const float* __restrict__ deltap,
-    void* __restrict__ dkp, void* __restrict__ dvp, int N, int BHkv, int H, int G, float c, float scale) {
+    void* __restrict__ dkp, void* __restrict__ dvp, int N, int BHkv, int H, int G, Win win_in, float c, float scale) {
+  // MODE 0: no window (full mask); 1: the causal window (-1, 0), a
+  // compile-time constant so that every window test folds; 2: any window.
+  constexpr bool MASK = MODE != 0;
+  const Win win = MODE == 1 ? Win{-1, 0} : win_in;
   constexpr int NW = kBwdWaves, BNK = 32 * NW, BMQ = Dkdv<D>::kTile, NKK = D / 16;
   constexpr int TILE = BMQ * D * 2;
   constexpr int S = Dkdv<D>::kStages;
@@ -334,8 +349,9 @@ __global__ __launch_bounds__(64 * kBwdWaves, Dkdv<D>::kOcc) void dkdv_kernel(
   const auto rdk = make_rsrc((char*)dkp + headkv, bytes);
   const auto rdv = make_rsrc((char*)dvp + headkv, bytes);
 
-  const int i_start = CAUSAL ? k0 : 0;
-  const int nt = (N - i_start + BMQ - 1) / BMQ;
+  // Query rows i_start .. i_end - 1 hold every query that sees a key of the block.
+  const int i_start = MASK ? win.query_lo(k0) : 0, i_end = MASK ? win.query_hi(k0 + BNK - 1, N) : N;
+  const int nt = (i_end - i_start + BMQ - 1) / BMQ;
   DmaTile<BMQ, D, NW> dma;
   dma.init(w, lane);
   {
@@ -377,20 +393,21 @@ __global__ __launch_bounds__(64 * kBwdWaves, Dkdv<D>::kOcc) void dkdv_kernel(
     if (S > 3 && nt > 2) dkdv_issue<D>(lds + (2 % S) * BUF, i_start + 2 * BMQ, dma, rq, rdo, rl, rd, w, lane);
   }
   if constexpr (VL)
-    dkdv_run<T, D, CAUSAL>(lds, nt, i_start, dma, qp, dop, lsep, deltap, bh0, G, N, kf, VLds<D>{vt, 32 * w}, rdk,
-                           rdv, wk0, krow, c, scale, w, lane);
+    dkdv_run<T, D, MASK>(lds, nt, i_start, dma, qp, dop, lsep, deltap, bh0, G, N, kf, VLds<D>{vt, 32 * w}, rdk,
+                         rdv, wk0, krow, win, c, scale, w, lane);
   else
-    dkdv_run<T, D, CAUSAL>(lds, nt, i_start, dma, qp, dop, lsep, deltap, bh0, G, N, kf, VRegs{vf}, rdk, rdv, wk0,
-                           krow, c, scale, w, lane);
+    dkdv_run<T, D, MASK>(lds, nt, i_start, dma, qp, dop, lsep, deltap, bh0, G, N, kf, VRegs{vf}, rdk, rdv, wk0,
+                         krow, win, c, scale, w, lane);
 }
 
-// One key tile of the dQ kernel for one wave (`edge`: the tile crosses the
-// causal diagonal of this wave's queries or the end of N).  One code path
-// for every tile, so the accumulator registers need no copies at merges.
-template <class T, int D, bool CAUSAL>
+// One key tile of the dQ kernel for one wave (`edge`: the tile crosses an
+// edge of the window of some of the wave's queries, or the end of N).  One
+// code path for every tile, so the accumulator registers need no copies at
+// merges.
+template <class T, int D, bool MASK>
 __device__ __forceinline__ void dq_tile(const lds_char* kt, const lds_char* vt, const u32x4* qf, const u32x4* dof,
-                                        f32x16* dqa, float l2, float dd, bool edge, int j0, int qrow, int N, float c,
-                                        int lane) {
+                                        f32x16* dqa, float l2, float dd, bool edge, int j0, int qrow, int N, Win win,
+                                        float c, int lane) {
   constexpr int NKK = D / 16, NB = D / 32;
   const int h = lane >> 5;
   f32x16 s[2], dp[2];
@@ -407,12 +424,13 @@ __device__ __forceinline__ void dq_tile(const lds_char* kt, const lds_char* vt, 
   sched_mfma_lds<4 * NKK, 1, 6>();
   prio_mfma_end();
   if (edge) {
+    const int klo = MASK ? win.lo(qrow) : kUnbounded, khi = MASK ? win.hi(qrow, N) : N - 1;
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = j0 + 32 * a + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (key >= N || (CAUSAL && key > qrow)) s[a][r] = -INFINITY;
+        if (key > khi || (MASK && win.left >= 0 && key < klo)) s[a][r] = -INFINITY;
       }
   }
 #pragma unroll
@@ -445,19 +463,20 @@ __device__ __forceinline__ void dq_issue(lds_char* lds, int t, const DmaTile<kBw
 }
 
 // One ring step on key tile t, held in ring buffer IDX = t % S.
-template <class T, int D, bool CAUSAL, int IDX>
-__device__ __forceinline__ void dq_step(lds_char* lds, int t, int nt, const DmaTile<kBwdTile, D, kBwdWaves>& dma,
+template <class T, int D, bool MASK, int IDX>
+__device__ __forceinline__ void dq_step(lds_char* lds, int t, int nt, int tb, const DmaTile<kBwdTile, D, kBwdWaves>& dma,
                                         Rsrc rk, Rsrc rv, const u32x4* qf, const u32x4* dof, f32x16* dqa, float l2,
-                                        float dd, int wq0, int qrow, int N, float c, int w, int lane) {
+                                        float dd, int wq0, int qrow, int N, Win win, float c, int w, int lane) {
   constexpr int S = kBwdStages, BN = kBwdTile, TILE = BN * D * 2;
   ring_wait<S, 2 * DmaTile<kBwdTile, D, kBwdWaves>::PER>(t, nt);
-  if (t + S - 1 < nt) dq_issue<D, (IDX + S - 1) % S>(lds, t + S - 1, dma, rk, rv, w);
+  if (t + S - 1 < nt) dq_issue<D, (IDX + S - 1) % S>(lds, tb + t + S - 1, dma, rk, rv, w);
   __builtin_amdgcn_sched_barrier(0);
-  const int j0 = t * BN;
-  if (CAUSAL && j0 > wq0 + 31) return;  // every key of the tile follows every query of the wave
+  const int j0 = (tb + t) * BN;
+  // No key of the tile is visible to any query of the wave.
+  if (MASK && (j0 + BN <= win.key_lo(wq0) || j0 >= win.key_hi(wq0 + 31, N))) return;
   const lds_char* cur = lds + IDX * 2 * TILE;
-  const bool edge = (j0 + BN > N) || (CAUSAL && j0 + BN - 1 > wq0);
-  dq_tile<T, D, CAUSAL>(cur, cur + TILE, qf, dof, dqa, l2, dd, edge, j0, qrow, N, c, lane);
+  const bool edge = (j0 + BN > N) || (MASK && !win.all_visible(wq0, wq0 + 31, j0, j0 + BN - 1));
+  dq_tile<T, D, MASK>(cur, cur + TILE, qf, dof, dqa, l2, dd, edge, j0, qrow, N, win, c, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -469,12 +488,16 @@ __device__ __forceinline__ void dq_step(lds_char* lds, int t, int nt, const DmaT
 //   P = 2^(S c - L2), dS = P (dP - D)
 //   dQ^T += K^T dS^T             (A operand by transposed LDS reads)
 // ---------------------------------------------------------------------------
-template <class T, int D, bool CAUSAL>
+template <class T, int D, int MODE>
 __global__ __launch_bounds__(64 * kBwdWaves, 2) void dq_kernel(const void* __restrict__ qp, const void* __restrict__ kp,
                                                             const void* __restrict__ vp, const void* __restrict__ dop,
                                                             const float* __restrict__ lsep,
                                                             const float* __restrict__ deltap, void* __restrict__ dqp,
-                                                            int N, int BH, int nqb, int H, int G, float c, float scale) {
+                                                            int N, int BH, int nqb, int H, int G, Win win_in, float c, float scale) {
+  // MODE 0: no window (full mask); 1: the causal window (-1, 0), a
+  // compile-time constant so that every window test folds; 2: any window.
+  constexpr bool MASK = MODE != 0;
+  const Win win = MODE == 1 ? Win{-1, 0} : win_in;
   constexpr int NW = kBwdWaves, BM = 32 * NW, BN = kBwdTile, NKK = D / 16, NB = D / 32;
   constexpr int S = kBwdStages, TILE = BN * D * 2;
   __shared__ __attribute__((aligned(16))) char smem[S * 2 * TILE];
@@ -483,7 +506,7 @@ __global__ __launch_bounds__(64 * kBwdWaves, 2) void dq_kernel(const void* __res
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, known uniform
   const int x = blockIdx.x;
-  const int qb = CAUSAL ? (nqb - 1 - x / BH) : (x / BH);
+  const int qb = MASK ? (nqb - 1 - x / BH) : (x / BH);
   const int bh = x % BH;
   const int q0 = qb * BM;
   const size_t head = (size_t)bh * N * D * 2;
@@ -496,11 +519,12 @@ __global__ __launch_bounds__(64 * kBwdWaves, 2) void dq_kernel(const void* __res
   const Rsrc rk = make_rsrc_words((const char*)kp + headkv, bytes);
   const Rsrc rv = make_rsrc_words((const char*)vp + headkv, bytes);
 
-  const int kend = CAUSAL ? min(N, q0 + BM) : N;
-  const int nt = (kend + BN - 1) / BN;
+  // Key tiles tb .. tb + nt - 1 hold every key visible to the block.
+  const int kbeg = MASK ? win.key_lo(q0) : 0, kend = MASK ? win.key_hi(q0 + BM - 1, N) : N;
+  const int tb = kbeg / BN, nt = (kend + BN - 1) / BN - tb;
   DmaTile<BN, D, NW> dma;
   dma.init(w, lane);
-  dq_issue<D, 0>(lds, 0, dma, rk, rv, w);
+  dq_issue<D, 0>(lds, tb, dma, rk, rv, w);
 
   const int wq0 = q0 + 32 * w;
   const int qrow = wq0 + (lane & 31);
@@ -520,21 +544,24 @@ __global__ __launch_bounds__(64 * kBwdWaves, 2) void dq_kernel(const void* __res
   }
   land(l2);
   land(dd);
-  if (S > 2 && nt > 1) dq_issue<D, 1 % S>(lds, 1, dma, rk, rv, w);
-  if (S > 3 && nt > 2) dq_issue<D, 2 % S>(lds, 2, dma, rk, rv, w);
+  if (S > 2 && nt > 1) dq_issue<D, 1 % S>(lds, tb + 1, dma, rk, rv, w);
+  if (S > 3 && nt > 2) dq_issue<D, 2 % S>(lds, tb + 2, dma, rk, rv, w);
   f32x16 dqa[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) dqa[b] = (f32x16){};
 
   for (int t = 0; t < nt; t += S) {
-    dq_step<T, D, CAUSAL, 0>(lds, t, nt, dma, rk, rv, qf, dof, dqa, l2, dd, wq0, qrow, N, c, w, lane);
-    if (t + 1 < nt) dq_step<T, D, CAUSAL, 1>(lds, t + 1, nt, dma, rk, rv, qf, dof, dqa, l2, dd, wq0, qrow, N, c, w, lane);
+    dq_step<T, D, MASK, 0>(lds, t, nt, tb, dma, rk, rv, qf, dof, dqa, l2, dd, wq0, qrow, N, win, c, w, lane);
+    if (t + 1 < nt)
+      dq_step<T, D, MASK, 1>(lds, t + 1, nt, tb, dma, rk, rv, qf, dof, dqa, l2, dd, wq0, qrow, N, win, c, w, lane);
     if constexpr (S > 2)
       if (t + 2 < nt)
-        dq_step<T, D, CAUSAL, 2 % S>(lds, t + 2, nt, dma, rk, rv, qf, dof, dqa, l2, dd, wq0, qrow, N, c, w, lane);
+        dq_step<T, D, MASK, 2 % S>(lds, t + 2, nt, tb, dma, rk, rv, qf, dof, dqa, l2, dd, wq0, qrow, N, win, c, w,
+                                   lane);
     if constexpr (S > 3)
       if (t + 3 < nt)
-        dq_step<T, D, CAUSAL, 3 % S>(lds, t + 3, nt, dma, rk, rv, qf, dof, dqa, l2, dd, wq0, qrow, N, c, w, lane);
+        dq_step<T, D, MASK, 3 % S>(lds, t + 3, nt, tb, dma, rk, rv, qf, dof, dqa, l2, dd, wq0, qrow, N, win, c, w,
+                                   lane);
   }
   store_rows<T, D>(rdq, qrow, dqa, scale, lane);
 }
@@ -564,31 +591,39 @@ hipError_t launch_preprocess(const PreArgs& a, hipStream_t st) {
   return a.bf16 ? launch_pre_e<bf16_tag>(a, st) : launch_pre_e<f16_tag>(a, st);
 }
 
-template <class T, int D, bool CAUSAL>
+template <class T, int D, int MODE>
 static hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t st) {
   const int BHkv = a.B * a.Hkv;
   const int nkb = (a.N + 127) / 128;
-  hipLaunchKernelGGL((dkdv_kernel<T, D, CAUSAL>), dim3(nkb * BHkv), dim3(256), 0, st, a.q, a.k, a.v, a.dO, a.lse,
-                     a.delta, a.dk, a.dv, a.N, BHkv, a.H, a.H / a.Hkv, a.scale * kLog2e, a.scale);
+  hipLaunchKernelGGL((dkdv_kernel<T, D, MODE>), dim3(nkb * BHkv), dim3(256), 0, st, a.q, a.k, a.v, a.dO, a.lse,
+                     a.delta, a.dk, a.dv, a.N, BHkv, a.H, a.H / a.Hkv, Win{a.wl, a.wr}, a.scale * kLog2e, a.scale);
   return hipGetLastError();
 }
 
-template <class T, int D, bool CAUSAL>
+template <class T, int D, int MODE>
 static hipError_t launch_dq_t(const BwdArgs& a, hipStream_t st) {
   const int BH = a.B * a.H;
   const int nqb = (a.N + 127) / 128;
-  hipLaunchKernelGGL((dq_kernel<T, D, CAUSAL>), dim3(nqb * BH), dim3(256), 0, st, a.q, a.k, a.v, a.dO, a.lse,
-                     a.delta, a.dq, a.N, BH, nqb, a.H, a.H / a.Hkv, a.scale * kLog2e, a.scale);
+  hipLaunchKernelGGL((dq_kernel<T, D, MODE>), dim3(nqb * BH), dim3(256), 0, st, a.q, a.k, a.v, a.dO, a.lse,
+                     a.delta, a.dq, a.N, BH, nqb, a.H, a.H / a.Hkv, Win{a.wl, a.wr}, a.scale * kLog2e, a.scale);
   return hipGetLastError();
 }
 
 template <class T, int D>
 static hipError_t launch_dkdv_d(const BwdArgs& a, hipStream_t st) {
-  return a.causal ? launch_dkdv_t<T, D, true>(a, st) : launch_dkdv_t<T, D, false>(a, st);
+  switch (win_mode(a.wl, a.wr)) {
+    case 0: return launch_dkdv_t<T, D, 0>(a, st);
+    case 1: return launch_dkdv_t<T, D, 1>(a, st);
+    default: return launch_dkdv_t<T, D, 2>(a, st);
+  }
 }
 template <class T, int D>
 static hipError_t launch_dq_d(const BwdArgs& a, hipStream_t st) {
-  return a.causal ? launch_dq_t<T, D, true>(a, st) : launch_dq_t<T, D, false>(a, st);
+  switch (win_mode(a.wl, a.wr)) {
+    case 0: return launch_dq_t<T, D, 0>(a, st);
+    case 1: return launch_dq_t<T, D, 1>(a, st);
+    default: return launch_dq_t<T, D, 2>(a, st);
+  }
 }
 
 template <class T>

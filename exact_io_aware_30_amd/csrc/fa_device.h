@@ -77,6 +77,35 @@ struct Elem<f16_tag> {
 };
 
 // ---------------------------------------------------------------------------
+// Attention window: key j is visible to query i iff i - left <= j <= i + right,
+// a negative bound meaning unbounded.  The causal mask is the window
+// (left, right) = (-1, 0); kernels compiled without a window (the full mask)
+// skip every window test.  Every row sees its own key (the window contains
+// the diagonal), so no row is ever fully masked.
+// ---------------------------------------------------------------------------
+constexpr int kUnbounded = -(1 << 30);  // lower key bound standing for "none"
+
+// Kernel mask mode for a window (wl, wr): 0 none (full mask), 1 causal, 2 other.
+inline int win_mode(int wl, int wr) { return (wl < 0 && wr < 0) ? 0 : (wl < 0 && wr == 0) ? 1 : 2; }
+
+struct Win {
+  int left, right;
+  // Keys visible to some query of [qlo, qhi]: [key_lo, key_hi), within [0, N).
+  __device__ __forceinline__ int key_lo(int qlo) const { return left < 0 ? 0 : max(0, qlo - left); }
+  __device__ __forceinline__ int key_hi(int qhi, int N) const { return right < 0 ? N : min(N, qhi + right + 1); }
+  // Queries that see some key of [klo, khi]: [query_lo, query_hi), within [0, N).
+  __device__ __forceinline__ int query_lo(int klo) const { return right < 0 ? 0 : max(0, klo - right); }
+  __device__ __forceinline__ int query_hi(int khi, int N) const { return left < 0 ? N : min(N, khi + left + 1); }
+  // Every query of [qlo, qhi] sees every key of [klo, khi].
+  __device__ __forceinline__ bool all_visible(int qlo, int qhi, int klo, int khi) const {
+    return (left < 0 || qhi - left <= klo) && (right < 0 || khi <= qlo + right);
+  }
+  // Visible keys of query i: [lo(i), hi(i, N)] (inclusive; lo may be kUnbounded).
+  __device__ __forceinline__ int lo(int i) const { return left < 0 ? kUnbounded : i - left; }
+  __device__ __forceinline__ int hi(int i, int N) const { return right < 0 ? N - 1 : min(N - 1, i + right); }
+};
+
+// ---------------------------------------------------------------------------
 // Buffer resources: a head slice [N, D] addressed with byte offsets.  Loads
 // past num_records return zero and stores past it are dropped, which is how
 // the ragged tail (rows >= N) is zero-filled on load and never written.

@@ -64,12 +64,13 @@ __device__ __forceinline__ void fwd_prio_end() {
 }
 
 // One key tile for one wave: S^T, mask (only when `edge`: the tile crosses
-// the diagonal or the end of N), online-softmax update, PV.  One code path
-// for every tile, so the accumulator registers need no copies at merges.
-template <class T, int D, bool CAUSAL>
+// an edge of the window or the end of N), online-softmax update, PV.  One
+// code path for every tile, so the accumulator registers need no copies at
+// merges.
+template <class T, int D, bool MASK>
 __device__ __forceinline__ void fwd_tile(const lds_char* kt, const lds_char* vt, const u32x4* qf, f32x16* acc,
-                                         float& mref, float& l, bool edge, int j0, int qrow, int N, float c,
-                                         int lane) {
+                                         float& mref, float& l, bool edge, int j0, int qrow, int N, Win win,
+                                         float c, int lane) {
   constexpr int NKK = D / 16, NB = D / 32, NA = kFwdNA;
   const int h = lane >> 5;
   f32x16 s[NA];
@@ -83,12 +84,13 @@ __device__ __forceinline__ void fwd_tile(const lds_char* kt, const lds_char* vt,
   sched_mfma_lds<NA * NKK, 1, (NA * NKK < 6 ? NA * NKK : 6)>();
   fwd_prio_end();
   if (edge) {
+    const int klo = MASK ? win.lo(qrow) : kUnbounded, khi = MASK ? win.hi(qrow, N) : N - 1;
 #pragma unroll
     for (int a = 0; a < NA; ++a)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = j0 + 32 * a + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (key >= N || (CAUSAL && key > qrow)) s[a][r] = -INFINITY;
+        if (key > khi || (MASK && win.left >= 0 && key < klo)) s[a][r] = -INFINITY;
       }
   }
   float mx = s[0][0];
@@ -99,18 +101,21 @@ __device__ __forceinline__ void fwd_tile(const lds_char* kt, const lds_char* vt,
   const float mxc = max_with_partner(mx) * c;  // row max in base-2 units
   if (__builtin_amdgcn_ballot_w64(mxc > mref + kRescaleSlack)) {
     const float mnew = fmaxf(mref, mxc);
-    const float alpha = exp2_fast(mref - mnew);  // 0 on the first tile (mref = -inf)
+    // 0 on a row's first visible tile (mref = -inf); rows with nothing
+    // visible yet keep l = 0, acc = 0.
+    const float alpha = mnew == -INFINITY ? 1.f : exp2_fast(mref - mnew);
     mref = mnew;
     l *= alpha;
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[b] *= alpha;
   }
   float rs = 0.f;
+  const float mr = mref == -INFINITY ? 0.f : mref;  // all of a row masked so far: p = 0
 #pragma unroll
   for (int a = 0; a < NA; ++a)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float p = exp2_fast(__builtin_fmaf(s[a][r], c, -mref));
+      const float p = exp2_fast(__builtin_fmaf(s[a][r], c, -mr));
       s[a][r] = p;
       rs += p;
     }
@@ -141,19 +146,20 @@ __device__ __forceinline__ void fwd_issue(lds_char* lds, int t, const DmaTile<kF
 // index, so that every LDS operand address is a register plus an immediate):
 // wait and barrier, DMA of tile t + S - 1 into the buffer tile t - 1 used,
 // then the math.
-template <class T, int D, bool CAUSAL, int IDX>
-__device__ __forceinline__ void fwd_step(lds_char* lds, int t, int nt, const DmaTile<kFwdBN, D, kFwdWaves>& dma,
+template <class T, int D, bool MASK, int IDX>
+__device__ __forceinline__ void fwd_step(lds_char* lds, int t, int nt, int tb, const DmaTile<kFwdBN, D, kFwdWaves>& dma,
                                          Rsrc rk, Rsrc rv, const u32x4* qf, f32x16* acc, float& mref, float& l,
-                                         int wq0, int qrow, int N, float c, int w, int lane) {
+                                         int wq0, int qrow, int N, Win win, float c, int w, int lane) {
   constexpr int S = kFwdStages, BN = kFwdBN, TILE = BN * D * 2;
   ring_wait<S, 2 * DmaTile<kFwdBN, D, kFwdWaves>::PER>(t, nt);
-  if (t + S - 1 < nt) fwd_issue<D, (IDX + S - 1) % S>(lds, t + S - 1, dma, rk, rv, w);
+  if (t + S - 1 < nt) fwd_issue<D, (IDX + S - 1) % S>(lds, tb + t + S - 1, dma, rk, rv, w);
   __builtin_amdgcn_sched_barrier(0);
-  const int j0 = t * BN;
-  if (CAUSAL && j0 > wq0 + 31) return;  // every key of the tile follows every query of the wave
+  const int j0 = (tb + t) * BN;
+  // No key of the tile is visible to any query of the wave.
+  if (MASK && (j0 + BN <= win.key_lo(wq0) || j0 >= win.key_hi(wq0 + 31, N))) return;
   const lds_char* cur = lds + IDX * 2 * TILE;
-  const bool edge = (j0 + BN > N) || (CAUSAL && j0 + BN - 1 > wq0);
-  fwd_tile<T, D, CAUSAL>(cur, cur + TILE, qf, acc, mref, l, edge, j0, qrow, N, c, lane);
+  const bool edge = (j0 + BN > N) || (MASK && !win.all_visible(wq0, wq0 + 31, j0, j0 + BN - 1));
+  fwd_tile<T, D, MASK>(cur, cur + TILE, qf, acc, mref, l, edge, j0, qrow, N, win, c, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -188,20 +194,23 @@ __device__ __forceinline__ void fwd_scores(const lds_char* kt, const u32x4* qf, 
     for (int a = 0; a < NA; ++a) s[a] = Elem<T>::mma(lds_rows_operand<D>(kt, 32 * a, kk, lane), qf[kk], s[a]);
 }
 
-// Keys past N, and under the causal mask keys after the lane's query, to
-// -inf: key j0 + 32a + 8(r/4) + 4h + r%4 is dropped when it exceeds
-// lim = min(query, N - 1) (N - 1 without the mask), one compare per element
-// against lim - j0 - 4h.  The bound passes through an empty asm statement so
-// that the compares stay inside the caller's branch.
-template <bool CAUSAL>
-__device__ __forceinline__ void fwd_mask(f32x16* s, int j0, int qrow, int N, int lane) {
-  int rel = (CAUSAL ? min(qrow, N - 1) : N - 1) - j0 - 4 * (lane >> 5);
-  asm volatile("" : "+v"(rel));
+// Keys past N, and keys outside the lane's query window, to -inf: key
+// j0 + 32a + 8(r/4) + 4h + r%4 is dropped when it lies outside the query's
+// [lo, hi] (hi = N - 1 without a window), compared as offsets against
+// lo - j0 - 4h and hi - j0 - 4h.  The bounds pass through an empty asm
+// statement so that the compares stay inside the caller's branch.
+template <bool MASK>
+__device__ __forceinline__ void fwd_mask(f32x16* s, int j0, int qrow, int N, Win win, int lane) {
+  int rhi = (MASK ? win.hi(qrow, N) : N - 1) - j0 - 4 * (lane >> 5);
+  int rlo = (MASK ? win.lo(qrow) : kUnbounded) - j0 - 4 * (lane >> 5);
+  asm volatile("" : "+v"(rhi), "+v"(rlo));
 #pragma unroll
   for (int a = 0; a < kFwdNA; ++a)
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      if (32 * a + 8 * (r >> 2) + (r & 3) > rel) s[a][r] = -INFINITY;
+    for (int r = 0; r < 16; ++r) {
+      const int off = 32 * a + 8 * (r >> 2) + (r & 3);
+      if (off > rhi || (MASK && win.left >= 0 && off < rlo)) s[a][r] = -INFINITY;
+    }
 }
 
 // Row maximum of s in base-2 units (both lane halves).
@@ -220,38 +229,14 @@ template <int NB>
 __device__ __forceinline__ void fwd_rescale(float mxc, f32x16* acc, float& mref, float& l) {
   if (__builtin_amdgcn_ballot_w64(mxc > mref + kRescaleSlack)) {
     const float mnew = fmaxf(mref, mxc);
-    const float alpha = exp2_fast(mref - mnew);  // 0 on the first tile (mref = -inf)
+    // 0 on a row's first visible tile (mref = -inf); rows with nothing
+    // visible yet keep l = 0, acc = 0.
+    const float alpha = mnew == -INFINITY ? 1.f : exp2_fast(mref - mnew);
     mref = mnew;
     l *= alpha;
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[b] *= alpha;
   }
-}
-
-// p = 2^(s c - mref) packed into MFMA operands; l += row sum.
-template <class T>
-__device__ __forceinline__ void fwd_probs(const f32x16* s, u32x4* pf, float c, float mref, float& l) {
-  float rs = 0.f;
-  f32x16 p[kFwdNA];
-#pragma unroll
-  for (int a = 0; a < kFwdNA; ++a)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      p[a][r] = exp2_fast(__builtin_fmaf(s[a][r], c, -mref));
-      rs += p[a][r];
-    }
-  l += rs;
-#pragma unroll
-  for (int j = 0; j < 2 * kFwdNA; ++j) pf[j] = pack8<T>(p[j >> 1], j & 1);
-}
-
-template <class T, int D>
-__device__ __forceinline__ void fwd_pv(const lds_char* vt, const u32x4* pf, f32x16* acc, int lane) {
-  constexpr int NB = D / 32;
-#pragma unroll
-  for (int j = 0; j < 2 * kFwdNA; ++j)
-#pragma unroll
-    for (int b = 0; b < NB; ++b) acc[b] = Elem<T>::mma(lds_cols_operand<D>(vt, j, 32 * b, lane), pf[j], acc[b]);
 }
 
 // Ring layout of the pipelined kernel: the K tiles of all buffers first,
@@ -282,17 +267,17 @@ __device__ __forceinline__ void pipe_wait(int t, int nt) {
 // its share of VALU work and the LDS reads for a later MFMA, with
 // scheduling fences between the groups so that the compiler keeps this
 // order (a wave issues VALU work while its own MFMAs execute).
-template <class T, int D, bool CAUSAL, int IDX>
-__device__ __forceinline__ void fwd_pipe_step(lds_char* lds, int t, int nt, int ntw,
+template <class T, int D, bool MASK, int IDX>
+__device__ __forceinline__ void fwd_pipe_step(lds_char* lds, int t, int nt, int ntw, int tb,
                                               const DmaTile<kFwdBN, D, kFwdWaves>& dma, Rsrc rk, Rsrc rv,
                                               const u32x4* qf, f32x16* acc, f32x16* s_cur, f32x16* s_nxt,
-                                              float& mref, float& l, int wq0, int qrow, int N, float c, int w,
-                                              int lane) {
+                                              float& mref, float& l, int wq0, int qrow, int N, Win win, float c,
+                                              int w, int lane) {
   constexpr int S = kPipeStages, BN = kFwdBN, TILE = BN * D * 2, NB = D / 32, NKK = D / 16, NA = kFwdNA;
   pipe_wait<2 * DmaTile<kFwdBN, D, kFwdWaves>::PER>(t, nt);
-  if (t + S - 1 < nt) fwd_pipe_issue<D, (IDX + S - 1) % S>(lds, t + S - 1, dma, rk, rv, w);
+  if (t + S - 1 < nt) fwd_pipe_issue<D, (IDX + S - 1) % S>(lds, tb + t + S - 1, dma, rk, rv, w);
   __builtin_amdgcn_sched_barrier(0);
-  if (t >= ntw) return;  // every key from tile t on follows every query of the wave
+  if (t >= ntw) return;  // no key from tile t on is visible to any query of the wave
   // Tile bases made opaque per step, so that the compiler does not hoist a
   // full set of per-buffer, per-lane addresses out of the loop.
   uint32_t vb = (uint32_t)(uintptr_t)lds + (S + IDX) * TILE, kb = (uint32_t)(uintptr_t)lds + ((IDX + 1) % S) * TILE;
@@ -308,6 +293,7 @@ __device__ __forceinline__ void fwd_pipe_step(lds_char* lds, int t, int nt, int 
     constexpr int NM = NA * NKK, E = 16 * NA / NM, PRE = NM < 3 ? NM : 3;
     u32x4 kop[NM];
     float rs = 0.f;
+    const float mr = mref == -INFINITY ? 0.f : mref;  // all of a row masked so far: p = 0
     u32x4 pf[2 * NA];
 #pragma unroll
     for (int i = 0; i < PRE; ++i) kop[i] = lds_rows_operand<D>(knxt, 32 * (i % NA), i / NA, lane);
@@ -321,7 +307,7 @@ __device__ __forceinline__ void fwd_pipe_step(lds_char* lds, int t, int nt, int 
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const int x = i * E + e, a = x / 16, r = x % 16;
-        s_cur[a][r] = exp2_fast(__builtin_fmaf(s_cur[a][r], c, -mref));  // P in place
+        s_cur[a][r] = exp2_fast(__builtin_fmaf(s_cur[a][r], c, -mr));  // P in place
         rs += s_cur[a][r];
         if (r % 8 == 7) pf[x / 8] = pack8<T>(s_cur[a], (r / 8));
       }
@@ -335,8 +321,9 @@ __device__ __forceinline__ void fwd_pipe_step(lds_char* lds, int t, int nt, int 
     for (int j = 0; j < 2 * NA; ++j) land(pf[j]);
     land(l);
 
-    const int j1 = (t + 1) * BN;
-    if ((j1 + BN > N) || (CAUSAL && j1 + BN - 1 > wq0)) fwd_mask<CAUSAL>(s_nxt, j1, qrow, N, lane);
+    const int j1 = (tb + t + 1) * BN;
+    if ((j1 + BN > N) || (MASK && !win.all_visible(wq0, wq0 + 31, j1, j1 + BN - 1)))
+      fwd_mask<MASK>(s_nxt, j1, qrow, N, win, lane);
     __builtin_amdgcn_sched_barrier(0);
 
     // Run 2: O^T += V(t)^T P(t)^T, MFMA i = (j = i / NB, b = i % NB), and the
@@ -363,12 +350,17 @@ __device__ __forceinline__ void fwd_pipe_step(lds_char* lds, int t, int nt, int 
   }
 }
 
-template <class T, int D, bool CAUSAL>
+template <class T, int D, int MODE>
 __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_pipe_kernel(const void* __restrict__ qp,
                                                                      const void* __restrict__ kp,
                                                                      const void* __restrict__ vp,
                                                                      void* __restrict__ op, float* __restrict__ lsep,
-                                                                     int N, int BH, int nqb, int H, int G, float c) {
+                                                                     int N, int BH, int nqb, int H, int G, Win win_in,
+                                                                     float c) {
+  // MODE 0: no window (full mask); 1: the causal window (-1, 0), a
+  // compile-time constant so that every window test folds; 2: any window.
+  constexpr bool MASK = MODE != 0;
+  const Win win = MODE == 1 ? Win{-1, 0} : win_in;
   constexpr int NW = kFwdWaves, S = kPipeStages, BM = 32 * NW, BN = kFwdBN, NKK = D / 16, NB = D / 32;
   constexpr int TILE = BN * D * 2, BUF = 2 * TILE;
   using Dma = DmaTile<BN, D, NW>;
@@ -384,7 +376,7 @@ __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_pipe_kernel(const void*
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, known uniform
   const int x = blockIdx.x;
-  const int qb = CAUSAL ? (nqb - 1 - x / BH) : (x / BH);
+  const int qb = MASK ? (nqb - 1 - x / BH) : (x / BH);
   const int bh = x % BH;
   const int q0 = qb * BM;
   const size_t head = (size_t)bh * N * D * 2;
@@ -397,15 +389,16 @@ __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_pipe_kernel(const void*
   const Rsrc rk = make_rsrc_words((const char*)kp + headkv, bytes);
   const Rsrc rv = make_rsrc_words((const char*)vp + headkv, bytes);
 
-  const int kend = CAUSAL ? min(N, q0 + BM) : N;
-  const int nt = (kend + BN - 1) / BN;
+  // Key tiles tb .. tb + nt - 1 hold every key visible to the block.
+  const int kbeg = MASK ? win.key_lo(q0) : 0, kend = MASK ? win.key_hi(q0 + BM - 1, N) : N;
+  const int tb = kbeg / BN, nt = (kend + BN - 1) / BN - tb;
   const int wq0 = q0 + 32 * w;  // first query of this wave
-  // Tiles this wave computes on: under the causal mask those with a key at
-  // or before its last query.
-  const int ntw = CAUSAL ? min(nt, (wq0 + 31) / BN + 1) : nt;
+  // This wave computes tiles 0 .. ntw - 1 of the block's (those past its
+  // last visible key are skipped; leading tiles it cannot see are masked).
+  const int ntw = MASK ? min(nt, (win.key_hi(wq0 + 31, N) + BN - 1) / BN - tb) : nt;
   Dma dma;
   dma.init(w, lane);
-  fwd_pipe_issue<D, 0>(lds, 0, dma, rk, rv, w);
+  fwd_pipe_issue<D, 0>(lds, tb, dma, rk, rv, w);
 
   const int qrow = wq0 + (lane & 31);  // this lane's query
   u32x4 qf[NKK];
@@ -415,8 +408,8 @@ __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_pipe_kernel(const void*
   // compiler tracks may be pending inside the loop.
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) land(qf[kk]);
-  if (nt > 1) fwd_pipe_issue<D, 1>(lds, 1, dma, rk, rv, w);
-  if (nt > 2) fwd_pipe_issue<D, 2>(lds, 2, dma, rk, rv, w);
+  if (nt > 1) fwd_pipe_issue<D, 1>(lds, tb + 1, dma, rk, rv, w);
+  if (nt > 2) fwd_pipe_issue<D, 2>(lds, tb + 2, dma, rk, rv, w);
   // Tile 0 landed (waited above); tiles 1 and 2 may be in flight.
   dma_wait_barrier<63>();
 
@@ -425,20 +418,25 @@ __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_pipe_kernel(const void*
   for (int b = 0; b < NB; ++b) acc[b] = (f32x16){};
   float mref = -INFINITY, l = 0.f;  // reference max (base 2) and this lane's part of the row sum
   fwd_scores<T, D>(lds, qf, sa, lane);
-  if (BN > N || (CAUSAL && BN - 1 > wq0)) fwd_mask<CAUSAL>(sa, 0, qrow, N, lane);
+  {
+    const int j0 = tb * BN;
+    if (j0 + BN > N || (MASK && !win.all_visible(wq0, wq0 + 31, j0, j0 + BN - 1)))
+      fwd_mask<MASK>(sa, j0, qrow, N, win, lane);
+  }
   fwd_rescale<NB>(fwd_rowmax(sa, c), acc, mref, l);
 
   for (int t = 0; t < nt; t += 4) {
-    fwd_pipe_step<T, D, CAUSAL, 0>(lds, t, nt, ntw, dma, rk, rv, qf, acc, sa, sb, mref, l, wq0, qrow, N, c, w, lane);
+    fwd_pipe_step<T, D, MASK, 0>(lds, t, nt, ntw, tb, dma, rk, rv, qf, acc, sa, sb, mref, l, wq0, qrow, N, win, c, w,
+                                  lane);
     if (t + 1 < nt)
-      fwd_pipe_step<T, D, CAUSAL, 1>(lds, t + 1, nt, ntw, dma, rk, rv, qf, acc, sb, sa, mref, l, wq0, qrow, N, c, w,
-                                     lane);
+      fwd_pipe_step<T, D, MASK, 1>(lds, t + 1, nt, ntw, tb, dma, rk, rv, qf, acc, sb, sa, mref, l, wq0, qrow, N, win,
+                                    c, w, lane);
     if (t + 2 < nt)
-      fwd_pipe_step<T, D, CAUSAL, 2>(lds, t + 2, nt, ntw, dma, rk, rv, qf, acc, sa, sb, mref, l, wq0, qrow, N, c, w,
-                                     lane);
+      fwd_pipe_step<T, D, MASK, 2>(lds, t + 2, nt, ntw, tb, dma, rk, rv, qf, acc, sa, sb, mref, l, wq0, qrow, N, win,
+                                    c, w, lane);
     if (t + 3 < nt)
-      fwd_pipe_step<T, D, CAUSAL, 3>(lds, t + 3, nt, ntw, dma, rk, rv, qf, acc, sb, sa, mref, l, wq0, qrow, N, c, w,
-                                     lane);
+      fwd_pipe_step<T, D, MASK, 3>(lds, t + 3, nt, ntw, tb, dma, rk, rv, qf, acc, sb, sa, mref, l, wq0, qrow, N, win,
+                                    c, w, lane);
   }
 
   const float lt = sum_with_partner(l);
@@ -446,12 +444,16 @@ __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_pipe_kernel(const void*
   if (h == 0 && qrow < N) lsep[(size_t)bh * N + qrow] = (mref + log2_fast(lt)) * kLn2;
 }
 
-template <class T, int D, bool CAUSAL>
+template <class T, int D, int MODE>
 __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_kernel(const void* __restrict__ qp,
                                                                 const void* __restrict__ kp,
                                                                 const void* __restrict__ vp, void* __restrict__ op,
                                                                 float* __restrict__ lsep, int N, int BH, int nqb,
-                                                                int H, int G, float c) {
+                                                                int H, int G, Win win_in, float c) {
+  // MODE 0: no window (full mask); 1: the causal window (-1, 0), a
+  // compile-time constant so that every window test folds; 2: any window.
+  constexpr bool MASK = MODE != 0;
+  const Win win = MODE == 1 ? Win{-1, 0} : win_in;
   constexpr int NW = kFwdWaves, S = kFwdStages, BM = 32 * NW, BN = kFwdBN, NKK = D / 16, NB = D / 32;
   constexpr int TILE = BN * D * 2, BUF = 2 * TILE;
   using Dma = DmaTile<BN, D, NW>;
@@ -461,7 +463,7 @@ __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_kernel(const void* __re
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, known uniform
   const int x = blockIdx.x;
-  const int qb = CAUSAL ? (nqb - 1 - x / BH) : (x / BH);
+  const int qb = MASK ? (nqb - 1 - x / BH) : (x / BH);
   const int bh = x % BH;
   const int q0 = qb * BM;
   const size_t head = (size_t)bh * N * D * 2;
@@ -474,11 +476,12 @@ __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_kernel(const void* __re
   const Rsrc rk = make_rsrc_words((const char*)kp + headkv, bytes);
   const Rsrc rv = make_rsrc_words((const char*)vp + headkv, bytes);
 
-  const int kend = CAUSAL ? min(N, q0 + BM) : N;
-  const int nt = (kend + BN - 1) / BN;
+  // Key tiles tb .. tb + nt - 1 hold every key visible to the block.
+  const int kbeg = MASK ? win.key_lo(q0) : 0, kend = MASK ? win.key_hi(q0 + BM - 1, N) : N;
+  const int tb = kbeg / BN, nt = (kend + BN - 1) / BN - tb;
   Dma dma;
   dma.init(w, lane);
-  fwd_issue<D, 0>(lds, 0, dma, rk, rv, w);
+  fwd_issue<D, 0>(lds, tb, dma, rk, rv, w);
 
   const int qrow = q0 + 32 * w + (lane & 31);  // this lane's query
   u32x4 qf[NKK];
@@ -488,8 +491,8 @@ __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_kernel(const void* __re
   // compiler tracks may be pending inside the loop.
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) land(qf[kk]);
-  if (S > 2 && nt > 1) fwd_issue<D, 1 % S>(lds, 1, dma, rk, rv, w);
-  if (S > 3 && nt > 2) fwd_issue<D, 2 % S>(lds, 2, dma, rk, rv, w);
+  if (S > 2 && nt > 1) fwd_issue<D, 1 % S>(lds, tb + 1, dma, rk, rv, w);
+  if (S > 3 && nt > 2) fwd_issue<D, 2 % S>(lds, tb + 2, dma, rk, rv, w);
 
   f32x16 acc[NB];
 #pragma unroll
@@ -498,14 +501,15 @@ __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_kernel(const void* __re
   const int wq0 = q0 + 32 * w;      // first query of this wave
 
   for (int t = 0; t < nt; t += S) {
-    fwd_step<T, D, CAUSAL, 0>(lds, t, nt, dma, rk, rv, qf, acc, mref, l, wq0, qrow, N, c, w, lane);
-    if (t + 1 < nt) fwd_step<T, D, CAUSAL, 1>(lds, t + 1, nt, dma, rk, rv, qf, acc, mref, l, wq0, qrow, N, c, w, lane);
+    fwd_step<T, D, MASK, 0>(lds, t, nt, tb, dma, rk, rv, qf, acc, mref, l, wq0, qrow, N, win, c, w, lane);
+    if (t + 1 < nt)
+      fwd_step<T, D, MASK, 1>(lds, t + 1, nt, tb, dma, rk, rv, qf, acc, mref, l, wq0, qrow, N, win, c, w, lane);
     if constexpr (S > 2)
       if (t + 2 < nt)
-        fwd_step<T, D, CAUSAL, 2 % S>(lds, t + 2, nt, dma, rk, rv, qf, acc, mref, l, wq0, qrow, N, c, w, lane);
+        fwd_step<T, D, MASK, 2 % S>(lds, t + 2, nt, tb, dma, rk, rv, qf, acc, mref, l, wq0, qrow, N, win, c, w, lane);
     if constexpr (S > 3)
       if (t + 3 < nt)
-        fwd_step<T, D, CAUSAL, 3 % S>(lds, t + 3, nt, dma, rk, rv, qf, acc, mref, l, wq0, qrow, N, c, w, lane);
+        fwd_step<T, D, MASK, 3 % S>(lds, t + 3, nt, tb, dma, rk, rv, qf, acc, mref, l, wq0, qrow, N, win, c, w, lane);
   }
 
   const float lt = sum_with_partner(l);
@@ -513,23 +517,28 @@ __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_kernel(const void* __re
   if (h == 0 && qrow < N) lsep[(size_t)bh * N + qrow] = (mref + log2_fast(lt)) * kLn2;
 }
 
-template <class T, int D, bool CAUSAL>
+template <class T, int D, int MODE>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   const int BH = a.B * a.H;
   const int BM = 32 * kFwdWaves;
   const int nqb = (a.N + BM - 1) / BM;
+  const Win win{a.wl, a.wr};
   if constexpr (kFwdPipelined<D>)
-    hipLaunchKernelGGL((fwd_pipe_kernel<T, D, CAUSAL>), dim3(nqb * BH), dim3(64 * kFwdWaves), 0, st, a.q, a.k, a.v,
-                       a.o, a.lse, a.N, BH, nqb, a.H, a.H / a.Hkv, a.scale * kLog2e);
+    hipLaunchKernelGGL((fwd_pipe_kernel<T, D, MODE>), dim3(nqb * BH), dim3(64 * kFwdWaves), 0, st, a.q, a.k, a.v,
+                       a.o, a.lse, a.N, BH, nqb, a.H, a.H / a.Hkv, win, a.scale * kLog2e);
   else
-    hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL>), dim3(nqb * BH), dim3(64 * kFwdWaves), 0, st, a.q, a.k, a.v, a.o,
-                       a.lse, a.N, BH, nqb, a.H, a.H / a.Hkv, a.scale * kLog2e);
+    hipLaunchKernelGGL((fwd_kernel<T, D, MODE>), dim3(nqb * BH), dim3(64 * kFwdWaves), 0, st, a.q, a.k, a.v, a.o,
+                       a.lse, a.N, BH, nqb, a.H, a.H / a.Hkv, win, a.scale * kLog2e);
   return hipGetLastError();
 }
 
 template <class T, int D>
 static hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t st) {
-  return a.causal ? launch_fwd_t<T, D, true>(a, st) : launch_fwd_t<T, D, false>(a, st);
+  switch (win_mode(a.wl, a.wr)) {
+    case 0: return launch_fwd_t<T, D, 0>(a, st);
+    case 1: return launch_fwd_t<T, D, 1>(a, st);
+    default: return launch_fwd_t<T, D, 2>(a, st);
+  }
 }
 
 template <class T>

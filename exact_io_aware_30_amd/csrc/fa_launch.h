@@ -13,7 +13,8 @@ struct FwdArgs {
   int B, H, N, d;
   int Hkv;  // key/value heads; H is a multiple of Hkv
   float scale;
-  bool causal, bf16;
+  int wl, wr;  // window: key j visible to query i iff i - wl <= j <= i + wr (negative: unbounded)
+  bool bf16;
 };
 
 struct PreArgs {
@@ -30,7 +31,8 @@ struct BwdArgs {
   int B, H, N, d;
   int Hkv;  // key/value heads; H is a multiple of Hkv
   float scale;
-  bool causal, bf16;
+  int wl, wr;  // window, as in FwdArgs
+  bool bf16;
 };
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st);

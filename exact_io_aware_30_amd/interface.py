@@ -10,7 +10,8 @@ module.  This module provides the same three names on top of
 * ``FlashAttnFunction`` -- forward calls ``fa_fwd`` and saves q, k, v, o and
   the row log-sum-exp L; backward calls ``fa_bwd_preprocess`` then
   ``fa_bwd`` (P is rebuilt from L, never stored).
-* ``flash_attn(q, k, v, causal=False, softmax_scale=None)`` -- the function
+* ``flash_attn(q, k, v, causal=False, softmax_scale=None, window_size=(-1, -1))``
+  -- the function
   form; inputs are made contiguous, the scale defaults to 1/sqrt(D).  k and
   v may carry fewer heads than q (Hkv dividing H): grouped-query attention,
   query head h reading key/value head h / (H / Hkv).
@@ -56,29 +57,34 @@ class FlashAttnFunction(torch.autograd.Function):
     """Exact attention whose backward rebuilds P from the saved L."""
 
     @staticmethod
-    def forward(ctx, q, k, v, causal: bool, scale: float):
+    def forward(ctx, q, k, v, causal: bool, scale: float, window=None):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
-        o, lse = binding.attention_forward(q, k, v, scale, causal)
+        o, lse = binding.attention_forward(q, k, v, scale, causal, window)
         ctx.save_for_backward(q, k, v, o, lse)
-        ctx.causal, ctx.scale = bool(causal), float(scale)
+        ctx.causal, ctx.scale, ctx.window = bool(causal), float(scale), window
         return o
 
     @staticmethod
     def backward(ctx, do):
         q, k, v, o, lse = ctx.saved_tensors
         dq, dk, dv, _ = binding.attention_backward(q, k, v, o, do.contiguous().to(o.dtype), lse, ctx.scale,
-                                                   ctx.causal)
-        return dq, dk, dv, None, None
+                                                   ctx.causal, ctx.window)
+        return dq, dk, dv, None, None, None
 
 
-def flash_attn(q, k, v, causal: bool = False, softmax_scale: float | None = None):
-    """softmax(q k^T * scale [+ causal mask]) v for q (B, H, N, D) and k, v
-    (B, Hkv, N, D), Hkv dividing H."""
+def flash_attn(q, k, v, causal: bool = False, softmax_scale: float | None = None, window_size=(-1, -1)):
+    """softmax(q k^T * scale [+ mask]) v for q (B, H, N, D) and k, v
+    (B, Hkv, N, D), Hkv dividing H.  window_size = (left, right) keeps keys
+    i - left .. i + right for query i (-1: no bound), on top of `causal`."""
     _check_inputs(q, k, v)
     scale = 1.0 / math.sqrt(q.shape[-1]) if softmax_scale is None else float(softmax_scale)
     if not (math.isfinite(scale) and scale > 0):
         raise ValueError("softmax_scale must be finite and positive")
-    return FlashAttnFunction.apply(q, k, v, bool(causal), scale)
+    left, right = (int(window_size[0]), int(window_size[1]))
+    if left < -1 or right < -1:
+        raise ValueError("window_size bounds must be >= -1 (-1: no bound)")
+    window = None if (left, right) == (-1, -1) else (left, right)
+    return FlashAttnFunction.apply(q, k, v, bool(causal), scale, window)
 
 
 class FlashSelfAttention(torch.nn.Module):

@@ -48,7 +48,7 @@ typedef enum { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
 
 enum {
   FA_OK = 0,
-  FA_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, bad mask/scale/dtype, bad Hkv */
+  FA_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, bad mask/window/scale/dtype, bad Hkv */
   FA_ERR_UNSUPPORTED = -2, /* head dim not in {32,64,128}, or sizes beyond the limits above */
   FA_ERR_ALIGNMENT = -3,   /* a pointer is not 16-byte aligned */
   FA_ERR_HIP = -4,         /* the HIP runtime refused a launch */
@@ -142,6 +142,33 @@ int fa_bwd_dq_gqa(const void* q, const void* k, const void* v, const void* dO,
                   const float* lse, const float* delta, void* dq, int B,
                   int H, int Hkv, int N, int d, float scale, int causal,
                   fa_dtype dt, void* stream);
+
+/*
+ * Windowed forms (sliding-window or local attention; "flash-attn-triton"
+ * docs, "Scope", lists sliding windows as not yet done there): key j is
+ * visible to query i iff i - window_left <= j <= i + window_right, -1 meaning
+ * no bound on that side.  (-1, 0) is the causal mask, (-1, -1) the full one;
+ * every window contains the diagonal, so no row is ever fully masked.
+ * Grouped heads as in the _gqa forms (Hkv = H for plain attention).
+ * window_left or window_right below -1 returns FA_ERR_INVALID_ARG; everything
+ * else as above.  lse and delta are over each query's visible keys.
+ */
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+              int B, int H, int Hkv, int N, int d, float scale,
+              int window_left, int window_right, fa_dtype dt, void* stream);
+int fa_bwd_ex(const void* q, const void* k, const void* v, const void* dO,
+              const float* lse, const float* delta, void* dq, void* dk,
+              void* dv, int B, int H, int Hkv, int N, int d, float scale,
+              int window_left, int window_right, fa_dtype dt, void* stream);
+int fa_bwd_dkdv_ex(const void* q, const void* k, const void* v,
+                   const void* dO, const float* lse, const float* delta,
+                   void* dk, void* dv, int B, int H, int Hkv, int N, int d,
+                   float scale, int window_left, int window_right,
+                   fa_dtype dt, void* stream);
+int fa_bwd_dq_ex(const void* q, const void* k, const void* v, const void* dO,
+                 const float* lse, const float* delta, void* dq, int B, int H,
+                 int Hkv, int N, int d, float scale, int window_left,
+                 int window_right, fa_dtype dt, void* stream);
 
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* fa_status_string(int status);

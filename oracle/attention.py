@@ -30,8 +30,13 @@ gradient of the forward above, derived by the chain rule):
     dQ = scale * dS K,  dK = scale * dS^T Q
 
 A row with no visible key (cannot arise for causal with equal query and key
-lengths, or for the full mask, but handled) has P = 0, O = 0, L = -inf and
-contributes nothing to any gradient.
+lengths, for the full mask or for a window that contains the diagonal, but
+handled) has P = 0, O = 0, L = -inf and contributes nothing to any gradient.
+
+Sliding windows (flash-attn-triton docs, "Scope", lists them as not yet done
+there): ``window=(left, right)`` keeps key j for query i iff
+i - left <= j <= i + right, a bound of -1 meaning none on that side; it
+applies on top of ``causal``.
 
 Row blocking (``row_block``) only bounds memory: each block of query rows sees
 its full key range, so every row's softmax is still one-shot.  Under the
@@ -56,13 +61,22 @@ def _check_shapes(*ts):
             raise ValueError("shape mismatch")
 
 
-def _scores(qh, kh, scale, causal, r0, r1, nk):
+def _scores(qh, kh, scale, causal, r0, r1, nk, window=None):
     """Scaled scores of query rows [r0, r1) against keys [0, nk), masked."""
     s = scale * (qh[r0:r1] @ kh[:nk].T)
     if causal:
         i = np.arange(r0, r1)[:, None]
         j = np.arange(nk)[None, :]
         s = np.where(j > i, -np.inf, s)
+    if window is not None:
+        # key j visible to query i iff i - left <= j <= i + right (-1: no bound)
+        left, right = window
+        i = np.arange(r0, r1)[:, None]
+        j = np.arange(nk)[None, :]
+        if left >= 0:
+            s = np.where(j < i - left, -np.inf, s)
+        if right >= 0:
+            s = np.where(j > i + right, -np.inf, s)
     return s
 
 
@@ -77,12 +91,18 @@ def _probs(s):
     return p, L
 
 
-def _key_extent(causal, r1, n):
-    return min(r1, n) if causal else n
+def _key_extent(causal, r1, n, window=None):
+    """Keys past this one are masked for every row before r1."""
+    nk = min(r1, n) if causal else n
+    if window is not None and window[1] >= 0:
+        nk = min(nk, r1 + window[1])
+    return nk
 
 
-def attention_forward(q, k, v, scale, causal, row_block=None):
-    """O [B,H,N,d] and L [B,H,N] of exact softmax attention."""
+def attention_forward(q, k, v, scale, causal, row_block=None, window=None):
+    """O [B,H,N,d] and L [B,H,N] of exact softmax attention.  ``window``
+    (left, right) further restricts query i to keys i - left .. i + right
+    (-1: no bound on that side)."""
     q, k, v = _as64(q), _as64(k), _as64(v)
     _check_shapes(q, k, v)
     B, H, N, _ = q.shape
@@ -93,8 +113,8 @@ def attention_forward(q, k, v, scale, causal, row_block=None):
         for h in range(H):
             for r0 in range(0, N, rb):
                 r1 = min(N, r0 + rb)
-                nk = _key_extent(causal, r1, N)
-                p, L[b, h, r0:r1] = _probs(_scores(q[b, h], k[b, h], scale, causal, r0, r1, nk))
+                nk = _key_extent(causal, r1, N, window)
+                p, L[b, h, r0:r1] = _probs(_scores(q[b, h], k[b, h], scale, causal, r0, r1, nk, window))
                 o[b, h, r0:r1] = p @ v[b, h, :nk]
     return o, L
 
@@ -104,7 +124,7 @@ def delta_rowsum(o, do):
     return np.sum(_as64(o) * _as64(do), axis=-1)
 
 
-def attention_backward(q, k, v, do, scale, causal, row_block=None):
+def attention_backward(q, k, v, do, scale, causal, row_block=None, window=None):
     """Gradients of sum(dO o O) with respect to Q, K, V.
 
     Returns a dict with dq, dk, dv ([B,H,N,d]), and the forward quantities the
@@ -123,8 +143,8 @@ def attention_backward(q, k, v, do, scale, causal, row_block=None):
             qh, kh, vh, doh = q[b, h], k[b, h], v[b, h], do[b, h]
             for r0 in range(0, N, rb):
                 r1 = min(N, r0 + rb)
-                nk = _key_extent(causal, r1, N)
-                p, lse = _probs(_scores(qh, kh, scale, causal, r0, r1, nk))
+                nk = _key_extent(causal, r1, N, window)
+                p, lse = _probs(_scores(qh, kh, scale, causal, r0, r1, nk, window))
                 ob = p @ vh[:nk]
                 dob = doh[r0:r1]
                 out["dv"][b, h, :nk] += p.T @ dob
@@ -155,19 +175,19 @@ def _group(q, k):
     return H // Hkv
 
 
-def attention_forward_gqa(q, k, v, scale, causal, row_block=None):
+def attention_forward_gqa(q, k, v, scale, causal, row_block=None, window=None):
     """(O [B,H,N,d], L [B,H,N]) for q [B,H,N,d] and k, v [B,Hkv,N,d]."""
     G = _group(q, k)
     return attention_forward(q, np.repeat(_as64(k), G, axis=1), np.repeat(_as64(v), G, axis=1), scale, causal,
-                             row_block)
+                             row_block, window)
 
 
-def attention_backward_gqa(q, k, v, do, scale, causal, row_block=None):
+def attention_backward_gqa(q, k, v, do, scale, causal, row_block=None, window=None):
     """attention_backward for grouped heads: dk and dv [B,Hkv,N,d] sum the
     gradients of the G query heads that read each key/value head."""
     G = _group(q, k)
     out = attention_backward(q, np.repeat(_as64(k), G, axis=1), np.repeat(_as64(v), G, axis=1), do, scale,
-                             causal, row_block)
+                             causal, row_block, window)
     B, Hkv, N, d = k.shape
     for name in ("dk", "dv"):
         out[name] = out[name].reshape(B, Hkv, G, N, d).sum(axis=2)

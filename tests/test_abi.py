@@ -33,6 +33,7 @@ def test_header_functions_are_exported():
     names = declared_functions()
     assert names == sorted(["fa_fwd", "fa_bwd_preprocess", "fa_bwd", "fa_bwd_dkdv", "fa_bwd_dq",
                             "fa_fwd_gqa", "fa_bwd_gqa", "fa_bwd_dkdv_gqa", "fa_bwd_dq_gqa",
+                            "fa_fwd_ex", "fa_bwd_ex", "fa_bwd_dkdv_ex", "fa_bwd_dq_ex",
                             "fa_status_string", "fa_version"])
     out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (fa_\w+)$", out, flags=re.M))
@@ -173,6 +174,21 @@ def test_gqa_rejects(p):
     # dk [1,1,64,64] is 8 KiB: placed 4 KiB into v (8 KiB) it overlaps
     assert b("fa_bwd_dkdv_gqa", dk=p[2] + 4096) == ALIAS
     assert b("fa_bwd_gqa", dq=p[0] + 8192) == ALIAS  # q is 16 KiB with H = 2
+
+
+def test_window_rejects(p):
+    # fa_fwd_ex(q, k, v, o, lse, B, H, Hkv, N, d, scale, wl, wr, dt, stream)
+    f = lambda wl, wr, Hkv=1: lib.fa_fwd_ex(p[0], p[1], p[2], p[3], p[4], 1, 1, Hkv, 64, 64, 0.125, wl, wr, 1,  # noqa
+                                            None)
+    assert f(-2, 0) == INVALID
+    assert f(0, -5) == INVALID
+    assert f(3, 3, Hkv=0) == INVALID
+    g = lambda wl, wr: lib.fa_bwd_ex(*p[:9], 1, 1, 1, 64, 64, 0.125, wl, wr, 1, None)  # noqa: E731
+    assert g(-3, 1) == INVALID
+    assert lib.fa_bwd_dkdv_ex(*p[:6], p[7], p[8], 1, 1, 1, 64, 64, 0.125, 2, -9, 1, None) == INVALID
+    assert lib.fa_bwd_dq_ex(*p[:7], 1, 1, 1, 64, 64, 0.125, -4, 0, 1, None) == INVALID
+    # the causal flag of the older entry points must be 0 or 1
+    assert lib.fa_fwd_gqa(*p[:5], 1, 1, 1, 64, 64, 0.125, 2, 1, None) == INVALID
 
 
 def test_binding_rejects_host_tensors():

@@ -440,3 +440,88 @@ def test_gqa_gradients_match_central_differences(causal):
             xm[idx] -= h
             g[idx] = (f(*[xp if x is t else t for t in (k, v)]) - f(*[xm if x is t else t for t in (k, v)])) / (2 * h)
         assert np.max(np.abs(g - out[name])) / np.max(np.abs(g)) <= 1e-7, name
+
+
+# --------------------------------------------------------------------------
+# Sliding windows (flash-attn-triton docs, "Scope")
+# --------------------------------------------------------------------------
+
+def _torch_window_mask(N, window, causal):
+    i = torch.arange(N)[:, None]
+    j = torch.arange(N)[None, :]
+    ok = torch.ones(N, N, dtype=torch.bool)
+    if causal:
+        ok &= j <= i
+    left, right = window
+    if left >= 0:
+        ok &= j >= i - left
+    if right >= 0:
+        ok &= j <= i + right
+    return ok
+
+
+@pytest.mark.parametrize("window,causal", [((3, 2), False), ((5, -1), False), ((-1, 4), False), ((7, 0), False),
+                                           ((4, -1), True), ((0, 6), False)])
+def test_window_against_torch_fp64(window, causal):
+    B, H, N, d = 2, 2, 29, 8
+    q, k, v, do = (rand((B, H, N, d), 120 + i) for i in range(4))
+    scale = 0.45
+    ok = _torch_window_mask(N, window, causal)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    s = ((tq @ tk.transpose(-1, -2)) * scale).masked_fill(~ok, float("-inf"))
+    lse_t = torch.logsumexp(s, dim=-1)
+    o_t = torch.softmax(s, dim=-1) @ tv
+    o_t.backward(torch.tensor(do))
+    sdpa = torch.nn.functional.scaled_dot_product_attention(torch.tensor(q), torch.tensor(k), torch.tensor(v),
+                                                            attn_mask=ok, scale=scale)
+    out = attention_backward(q, k, v, do, scale, causal, window=window)
+    o, L = attention_forward(q, k, v, scale, causal, window=window, row_block=7)
+
+    def rel(a, b):
+        return np.max(np.abs(a - b)) / np.max(np.abs(b))
+
+    assert rel(o, sdpa.numpy()) <= 1e-12
+    assert rel(out["o"], o_t.detach().numpy()) <= 1e-12
+    assert rel(L, lse_t.detach().numpy()) <= 1e-12
+    for name, t in (("dq", tq), ("dk", tk), ("dv", tv)):
+        assert rel(out[name], t.grad.numpy()) <= 1e-12, name
+
+
+def test_window_special_cases():
+    B, H, N, d = 1, 2, 17, 5
+    q, k, v, do = (rand((B, H, N, d), 140 + i) for i in range(4))
+    plain_c = attention_backward(q, k, v, do, 0.6, True)
+    plain_f = attention_backward(q, k, v, do, 0.6, False)
+    # (-1, 0) is the causal mask and (-1, -1) the full one, bit for bit
+    for ref, window in ((plain_c, (-1, 0)), (plain_f, (-1, -1)), (plain_f, (N - 1, N - 1))):
+        got = attention_backward(q, k, v, do, 0.6, False, window=window)
+        for name in ("o", "lse", "dq", "dk", "dv"):
+            np.testing.assert_allclose(got[name], ref[name], rtol=1e-14, atol=1e-14)
+    # (0, 0): each query sees only its own key, so O = V, L = scale q.k,
+    # dV = dO and dQ = dK = 0 (a softmax over one element is constant)
+    one = attention_backward(q, k, v, do, 0.6, False, window=(0, 0))
+    np.testing.assert_allclose(one["o"], v, rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(one["lse"], 0.6 * np.sum(q * k, axis=-1), rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(one["dv"], do, rtol=1e-14, atol=1e-14)
+    assert np.max(np.abs(one["dq"])) == 0 and np.max(np.abs(one["dk"])) == 0
+
+
+@pytest.mark.parametrize("window", [(2, 1), (1, -1)])
+def test_window_gradients_match_central_differences(window):
+    rng = np.random.default_rng(77 + window[0])
+    q, k, v, do = (rng.standard_normal((1, 1, 6, 3)) for _ in range(4))
+    out = attention_backward(q, k, v, do, 0.9, False, window=window)
+    h = 1e-6
+
+    def f(qq, kk, vv):
+        o, _ = attention_forward(qq, kk, vv, 0.9, False, window=window)
+        return float(np.sum(do * o))
+
+    for name, x in (("dq", q), ("dk", k), ("dv", v)):
+        g = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            g[idx] = (f(*[xp if x is t else t for t in (q, k, v)]) - f(*[xm if x is t else t for t in (q, k, v)])) / (2 * h)
+        assert np.max(np.abs(g - out[name])) / np.max(np.abs(g)) <= 1e-7, name

@@ -32,6 +32,9 @@ MUTANTS = {
     "transposed_p_in_bwd_pv": ("ob = p @ vh[:nk]", "ob = p.T @ vh[:nk]"),
     "transposed_p_in_fwd_pv": ("o[b, h, r0:r1] = p @ v[b, h, :nk]", "o[b, h, r0:r1] = p.T @ v[b, h, :nk]"),
     "delta_wrong_axis": ("dsum = np.sum(p * dp, axis=1)", "dsum = np.sum(p * dp, axis=0)"),
+    # sliding window: the left bound must keep key i - left
+    "window_left_off_by_one": ("s = np.where(j < i - left, -np.inf, s)", "s = np.where(j <= i - left, -np.inf, s)"),
+    "window_extent_too_short": ("nk = min(nk, r1 + window[1])", "nk = min(nk, r1 + window[1] - 1)"),
     # grouped-query attention: query head h must read key/value head h // G
     "gqa_heads_interleaved": ("return attention_forward(q, np.repeat(_as64(k), G, axis=1), np.repeat(_as64(v), G, axis=1)",
                               "return attention_forward(q, np.tile(_as64(k), (1, G, 1, 1)), "
@@ -92,6 +95,21 @@ def pin_battery(m):
         np.testing.assert_allclose(out["o"], ot.detach().numpy(), rtol=1e-10, atol=1e-12)
         np.testing.assert_allclose(out["delta"], out["delta_o"], rtol=1e-10, atol=1e-12)
         assert np.max(np.abs(out["dk"].sum(axis=2))) <= 1e-10
+    # a sliding window against torch fp64 with the same boolean mask
+    N, d = 9, 3
+    q, k, v, do = (rng.standard_normal((1, 1, N, d)) for _ in range(4))
+    i_, j_ = torch.arange(N)[:, None], torch.arange(N)[None, :]
+    ok = (j_ >= i_ - 2) & (j_ <= i_ + 1)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    s = ((tq @ tk.transpose(-1, -2)) * 0.7).masked_fill(~ok, float("-inf"))
+    ot = torch.softmax(s, -1) @ tv
+    ot.backward(torch.tensor(do))
+    out = m.attention_backward(q, k, v, do, 0.7, False, window=(2, 1), row_block=3)
+    o, L = m.attention_forward(q, k, v, 0.7, False, window=(2, 1), row_block=2)
+    np.testing.assert_allclose(o, ot.detach().numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(L, torch.logsumexp(s, -1).detach().numpy(), rtol=1e-10, atol=1e-12)
+    for name, t in (("dq", tq), ("dk", tk), ("dv", tv)):
+        np.testing.assert_allclose(out[name], t.grad.numpy(), rtol=1e-9, atol=1e-11)
     # grouped-query forms against torch fp64 through repeat_interleave
     for causal in (False, True):
         H, Hkv, N, d = 4, 2, 5, 3
