@@ -45,6 +45,8 @@ _SIG = {
     "fa_bwd_ex": [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _i, _i, _p],
     "fa_bwd_dkdv_ex": [_p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _i, _i, _p],
     "fa_bwd_dq_ex": [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _i, _i, _p],
+    "fa_fwd_varlen": [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _i, _i, _p],
+    "fa_bwd_varlen": [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _i, _i, _p],
     "fa_status_string": [_i],
     "fa_version": [],
 }
@@ -279,4 +281,68 @@ def attention_backward(q, k, v, o, do, lse, scale: float, causal: bool, window=N
         fa_bwd_gqa(q, k, v, do, lse, delta, dq, dk, dv, scale, causal)
     else:
         fa_bwd(q, k, v, do, lse, delta, dq, dk, dv, scale, causal)
+    return dq, dk, dv, delta
+
+
+# ---------------------------------------------------------------------------
+# Packed variable-length batches: q, o, do, dq [H, T, d]; k, v, dk, dv
+# [Hkv, T, d]; lse, delta [H, T]; cu_seqlens int32 [B + 1] on the GPU.
+# ---------------------------------------------------------------------------
+def _packed(q, kv_pairs, q_pairs, rows, cu_seqlens):
+    if q.dim() != 3 or not q.is_cuda or not q.is_contiguous() or q.dtype not in _DT:
+        raise ValueError("q must be a contiguous [H, T, d] float16/bfloat16 GPU tensor")
+    H, T, d = q.shape
+    Hkv = kv_pairs[0][0].shape[0] if kv_pairs[0][0].dim() == 3 else -1
+    for t, name in kv_pairs:
+        if t.dim() != 3 or t.shape != (Hkv, T, d) or t.dtype != q.dtype or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [Hkv, T, d] GPU tensor of q's dtype")
+    if Hkv < 1 or H % Hkv:
+        raise ValueError(f"the query heads ({H}) must be a multiple of the key/value heads ({Hkv})")
+    for t, name in q_pairs:
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must match q")
+    for t, name in rows:
+        if t.shape != (H, T) or t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 [H, T] GPU tensor")
+    if (cu_seqlens.dim() != 1 or cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda
+            or not cu_seqlens.is_contiguous() or cu_seqlens.numel() < 2):
+        raise ValueError("cu_seqlens must be a contiguous int32 [B + 1] GPU tensor")
+    return H, Hkv, T, d, cu_seqlens.numel() - 1
+
+
+def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, max_seqlen: int, scale: float, window) -> None:
+    H, Hkv, T, d, B = _packed(q, ((k, "k"), (v, "v")), ((o, "o"),), ((lse, "lse"),), cu_seqlens)
+    wl, wr = window
+    _check(_lib.fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                              cu_seqlens.data_ptr(), B, int(max_seqlen), T, H, Hkv, d, float(scale), int(wl), int(wr),
+                              _DT[q.dtype], _stream(q)), "fa_fwd_varlen")
+
+
+def fa_bwd_varlen(q, k, v, do, lse, delta, dq, dk, dv, cu_seqlens, max_seqlen: int, scale: float, window) -> None:
+    H, Hkv, T, d, B = _packed(q, ((k, "k"), (v, "v"), (dk, "dk"), (dv, "dv")), ((do, "do"), (dq, "dq")),
+                              ((lse, "lse"), (delta, "delta")), cu_seqlens)
+    wl, wr = window
+    _check(_lib.fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                              delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), cu_seqlens.data_ptr(), B,
+                              int(max_seqlen), T, H, Hkv, d, float(scale), int(wl), int(wr), _DT[q.dtype],
+                              _stream(q)), "fa_bwd_varlen")
+
+
+def attention_forward_varlen(q, k, v, cu_seqlens, max_seqlen: int, scale: float, causal: bool, window=None):
+    """(o [H, T, d], lse [H, T]) for packed sequences."""
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, max_seqlen, scale, _window(window, causal))
+    return o, lse
+
+
+def attention_backward_varlen(q, k, v, o, do, lse, cu_seqlens, max_seqlen: int, scale: float, causal: bool,
+                              window=None):
+    """(dq, dk, dv, delta) for packed sequences: the pre-pass over [1, H, T, d]
+    views, then the two backward kernels."""
+    H, T, d = q.shape
+    delta = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    fa_bwd_preprocess(o.view(1, H, T, d), do.view(1, H, T, d), delta.view(1, H, T))
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fa_bwd_varlen(q, k, v, do, lse, delta, dq, dk, dv, cu_seqlens, max_seqlen, scale, _window(window, causal))
     return dq, dk, dv, delta

@@ -104,9 +104,64 @@ fa::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* dO
   return fa::BwdArgs{q, k, v, dO, lse, delta, dq, dk, dv, B, H, N, d, Hkv, scale, wl, wr, dt == FA_BF16};
 }
 
+// Packed variable-length batches: q, o, dO, dq [H, T, d]; k, v, dk, dv
+// [Hkv, T, d]; lse, delta [H, T]; sequence b at rows cu[b] .. cu[b+1] - 1.
+int check_varlen(const int* cu, int B, int max_seqlen, int T, int H, int Hkv, int d, fa_dtype dt, float scale,
+                 int wl, int wr) {
+  if (!cu || B < 1 || max_seqlen < 1 || T < 1) return FA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(cu) & 3u) != 0) return FA_ERR_ALIGNMENT;
+  int rc = check_common(B, H, max_seqlen, d, dt);  // per-sequence limits as for a batch of max_seqlen
+  if (rc) return rc;
+  if ((rc = check_heads(H, Hkv))) return rc;
+  return check_scale_window(scale, wl, wr);
+}
+
 }  // namespace
 
 extern "C" {
+
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int* cu_seqlens, int B,
+                  int max_seqlen, int T, int H, int Hkv, int d, float scale, int window_left, int window_right,
+                  fa_dtype dt, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  int rc = check_varlen(cu_seqlens, B, max_seqlen, T, H, Hkv, d, dt, scale, window_left, window_right);
+  if (rc) return rc;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGNMENT;
+  const long long tb = static_cast<long long>(H) * T * d * 2, rb = static_cast<long long>(H) * T * 4;
+  const long long kvb = static_cast<long long>(Hkv) * T * d * 2;
+  const Range ins[3] = {range_of(q, tb), range_of(k, kvb), range_of(v, kvb)};
+  const Range outs[2] = {range_of(o, tb), range_of(lse, rb)};
+  if ((rc = check_alias(outs, 2, ins, 3))) return rc;
+  fa::FwdArgs a{q, k, v, o, lse, B, H, max_seqlen, d, Hkv, scale, window_left, window_right, dt == FA_BF16};
+  a.cu = cu_seqlens;
+  a.T = T;
+  return hip_status(fa::launch_fwd(a, static_cast<hipStream_t>(stream)));
+}
+
+int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* dO, const float* lse, const float* delta,
+                  void* dq, void* dk, void* dv, const int* cu_seqlens, int B, int max_seqlen, int T, int H, int Hkv,
+                  int d, float scale, int window_left, int window_right, fa_dtype dt, void* stream) {
+  if (!q || !k || !v || !dO || !lse || !delta || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
+  int rc = check_varlen(cu_seqlens, B, max_seqlen, T, H, Hkv, d, dt, scale, window_left, window_right);
+  if (rc) return rc;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) || !aligned16(lse) || !aligned16(delta) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return FA_ERR_ALIGNMENT;
+  const long long tb = static_cast<long long>(H) * T * d * 2, rb = static_cast<long long>(H) * T * 4;
+  const long long kvb = static_cast<long long>(Hkv) * T * d * 2;
+  const Range ins[6] = {range_of(q, tb), range_of(k, kvb), range_of(v, kvb), range_of(dO, tb), range_of(lse, rb),
+                        range_of(delta, rb)};
+  const Range outs[3] = {range_of(dq, tb), range_of(dk, kvb), range_of(dv, kvb)};
+  if ((rc = check_alias(outs, 3, ins, 6))) return rc;
+  fa::BwdArgs a = bwd_args(q, k, v, dO, lse, delta, dq, dk, dv, B, H, Hkv, max_seqlen, d, scale, window_left,
+                           window_right, dt);
+  a.cu = cu_seqlens;
+  a.T = T;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((rc = hip_status(fa::launch_bwd_dkdv(a, st)))) return rc;
+  return hip_status(fa::launch_bwd_dq(a, st));
+}
+
 
 int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N, int d,
               float scale, int window_left, int window_right, fa_dtype dt, void* stream) {
@@ -239,6 +294,6 @@ const char* fa_status_string(int status) {
   }
 }
 
-int fa_version(void) { return 300; }
+int fa_version(void) { return 400; }
 
 }  // extern "C"

@@ -272,7 +272,7 @@ __device__ __forceinline__ void dkdv_step(lds_char* lds, int t, int nt, int i_st
 template <class T, int D, bool MASK, class VOp>
 __device__ __forceinline__ void dkdv_run(lds_char* lds, int nt, int i_start, const DmaTile<Dkdv<D>::kTile, D, kBwdWaves>& dma,
                                          const void* qp, const void* dop, const float* lsep, const float* deltap,
-                                         int bh0, int G, int N, const u32x4* kf, const VOp& vop,
+                                         const Geom& geo, int b, int hk, int N, const u32x4* kf, const VOp& vop,
                                          __amdgpu_buffer_rsrc_t rdk, __amdgpu_buffer_rsrc_t rdv, int wk0, int krow,
                                          Win win, float c, float scale, int w, int lane) {
   constexpr int S = Dkdv<D>::kStages, NB = D / 32, BMQ = Dkdv<D>::kTile;
@@ -281,13 +281,15 @@ __device__ __forceinline__ void dkdv_run(lds_char* lds, int nt, int i_start, con
   f32x16 dka[NB], dva[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) dka[b] = dva[b] = (f32x16){};
-  for (int g = 0; g < G; ++g) {
-    const int bh = bh0 + g;
-    const size_t head = (size_t)bh * N * D * 2;
+  for (int g = 0; g < geo.G; ++g) {
+    long qr0, kvr0;
+    int len;
+    geo.slice(b, hk * geo.G + g, qr0, kvr0, len);
+    const size_t head = (size_t)qr0 * D * 2;
     const Rsrc rq = make_rsrc_words((const char*)qp + head, bytes);
     const Rsrc rdo = make_rsrc_words((const char*)dop + head, bytes);
-    const Rsrc rl = make_rsrc_words(lsep + (size_t)bh * N, (uint32_t)N * 4);
-    const Rsrc rd = make_rsrc_words(deltap + (size_t)bh * N, (uint32_t)N * 4);
+    const Rsrc rl = make_rsrc_words(lsep + qr0, (uint32_t)N * 4);
+    const Rsrc rd = make_rsrc_words(deltap + qr0, (uint32_t)N * 4);
     if (g > 0) {
       // Every wave is done with the previous head's ring before it refills.
       dma_wait_barrier<0>();
@@ -316,12 +318,12 @@ __device__ __forceinline__ void dkdv_run(lds_char* lds, int nt, int i_start, con
 }
 
 // Grid: key blocks x key/value heads (BHkv = B * H / G of them); the query
-// heads of key/value head hkv of batch b are b H + hkv G .. + G - 1.
+// heads of key/value head hk are hk G .. hk G + G - 1 of the same batch.
 template <class T, int D, int MODE>
 __global__ __launch_bounds__(64 * kBwdWaves, Dkdv<D>::kOcc) void dkdv_kernel(
     const void* __restrict__ qp, const void* __restrict__ kp, const void* __restrict__ vp,
     const void* __restrict__ dop, const float* __restrict__ lsep, const float* __restrict__ deltap,
-    void* __restrict__ dkp, void* __restrict__ dvp, int N, int BHkv, int H, int G, Win win_in, float c, float scale) {
+    void* __restrict__ dkp, void* __restrict__ dvp, Geom geo, int BHkv, Win win_in, float c, float scale) {
   // MODE 0: no window (full mask); 1: the causal window (-1, 0), a
   // compile-time constant so that every window test folds; 2: any window.
   constexpr bool MASK = MODE != 0;
@@ -339,11 +341,15 @@ __global__ __launch_bounds__(64 * kBwdWaves, Dkdv<D>::kOcc) void dkdv_kernel(
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, known uniform
   const int x = blockIdx.x;
   const int kb = x / BHkv, bhkv = x % BHkv;
-  const int Hkv = H / G;
-  const int bh0 = (bhkv / Hkv) * H + (bhkv % Hkv) * G;  // first query head of the group
+  const int Hkv = geo.H / geo.G;
+  const int b = bhkv / Hkv, hk = bhkv % Hkv;
   const int k0 = kb * BNK;
-  const size_t headkv = (size_t)bhkv * N * D * 2;
-  const size_t head0 = (size_t)bh0 * N * D * 2;
+  long qr0, kvr0;  // the group's first query head, and the key/value head
+  int N;
+  geo.slice(b, hk * geo.G, qr0, kvr0, N);
+  if (k0 >= N) return;  // past the end of a shorter packed sequence (the whole workgroup)
+  const size_t headkv = (size_t)kvr0 * D * 2;
+  const size_t head0 = (size_t)qr0 * D * 2;
   const uint32_t bytes = (uint32_t)N * D * 2;
   const auto rk = make_rsrc((const char*)kp + headkv, bytes);
   const auto rdk = make_rsrc((char*)dkp + headkv, bytes);
@@ -357,8 +363,8 @@ __global__ __launch_bounds__(64 * kBwdWaves, Dkdv<D>::kOcc) void dkdv_kernel(
   {
     const Rsrc rq = make_rsrc_words((const char*)qp + head0, bytes);
     const Rsrc rdo = make_rsrc_words((const char*)dop + head0, bytes);
-    const Rsrc rl = make_rsrc_words(lsep + (size_t)bh0 * N, (uint32_t)N * 4);
-    const Rsrc rd = make_rsrc_words(deltap + (size_t)bh0 * N, (uint32_t)N * 4);
+    const Rsrc rl = make_rsrc_words(lsep + qr0, (uint32_t)N * 4);
+    const Rsrc rd = make_rsrc_words(deltap + qr0, (uint32_t)N * 4);
     dkdv_issue<D>(lds, i_start, dma, rq, rdo, rl, rd, w, lane);
   }
   lds_char* const vt = lds + S * BUF;
@@ -387,17 +393,17 @@ __global__ __launch_bounds__(64 * kBwdWaves, Dkdv<D>::kOcc) void dkdv_kernel(
   {
     const Rsrc rq = make_rsrc_words((const char*)qp + head0, bytes);
     const Rsrc rdo = make_rsrc_words((const char*)dop + head0, bytes);
-    const Rsrc rl = make_rsrc_words(lsep + (size_t)bh0 * N, (uint32_t)N * 4);
-    const Rsrc rd = make_rsrc_words(deltap + (size_t)bh0 * N, (uint32_t)N * 4);
+    const Rsrc rl = make_rsrc_words(lsep + qr0, (uint32_t)N * 4);
+    const Rsrc rd = make_rsrc_words(deltap + qr0, (uint32_t)N * 4);
     if (S > 2 && nt > 1) dkdv_issue<D>(lds + (1 % S) * BUF, i_start + BMQ, dma, rq, rdo, rl, rd, w, lane);
     if (S > 3 && nt > 2) dkdv_issue<D>(lds + (2 % S) * BUF, i_start + 2 * BMQ, dma, rq, rdo, rl, rd, w, lane);
   }
   if constexpr (VL)
-    dkdv_run<T, D, MASK>(lds, nt, i_start, dma, qp, dop, lsep, deltap, bh0, G, N, kf, VLds<D>{vt, 32 * w}, rdk,
-                         rdv, wk0, krow, win, c, scale, w, lane);
+    dkdv_run<T, D, MASK>(lds, nt, i_start, dma, qp, dop, lsep, deltap, geo, b, hk, N, kf, VLds<D>{vt, 32 * w},
+                         rdk, rdv, wk0, krow, win, c, scale, w, lane);
   else
-    dkdv_run<T, D, MASK>(lds, nt, i_start, dma, qp, dop, lsep, deltap, bh0, G, N, kf, VRegs{vf}, rdk, rdv, wk0,
-                         krow, win, c, scale, w, lane);
+    dkdv_run<T, D, MASK>(lds, nt, i_start, dma, qp, dop, lsep, deltap, geo, b, hk, N, kf, VRegs{vf}, rdk, rdv,
+                         wk0, krow, win, c, scale, w, lane);
 }
 
 // One key tile of the dQ kernel for one wave (`edge`: the tile crosses an
@@ -493,7 +499,8 @@ __global__ __launch_bounds__(64 * kBwdWaves, 2) void dq_kernel(const void* __res
                                                             const void* __restrict__ vp, const void* __restrict__ dop,
                                                             const float* __restrict__ lsep,
                                                             const float* __restrict__ deltap, void* __restrict__ dqp,
-                                                            int N, int BH, int nqb, int H, int G, Win win_in, float c, float scale) {
+                                                            Geom geo, int BH, int nqb, Win win_in, float c,
+                                                            float scale) {
   // MODE 0: no window (full mask); 1: the causal window (-1, 0), a
   // compile-time constant so that every window test folds; 2: any window.
   constexpr bool MASK = MODE != 0;
@@ -509,9 +516,12 @@ __global__ __launch_bounds__(64 * kBwdWaves, 2) void dq_kernel(const void* __res
   const int qb = MASK ? (nqb - 1 - x / BH) : (x / BH);
   const int bh = x % BH;
   const int q0 = qb * BM;
-  const size_t head = (size_t)bh * N * D * 2;
-  // K and V of the group (see the forward kernel).
-  const size_t headkv = (size_t)((bh / H) * (H / G) + (bh % H) / G) * N * D * 2;
+  // This (batch, head) slice: query head h reads key/value head h / G.
+  long qr0, kvr0;
+  int N;
+  geo.slice(bh / geo.H, bh % geo.H, qr0, kvr0, N);
+  if (q0 >= N) return;  // past the end of a shorter packed sequence (the whole workgroup)
+  const size_t head = (size_t)qr0 * D * 2, headkv = (size_t)kvr0 * D * 2;
   const uint32_t bytes = (uint32_t)N * D * 2;
   const auto rq = make_rsrc((const char*)qp + head, bytes);
   const auto rdo = make_rsrc((const char*)dop + head, bytes);
@@ -534,8 +544,8 @@ __global__ __launch_bounds__(64 * kBwdWaves, 2) void dq_kernel(const void* __res
     qf[kk] = bload16(rq, (uint32_t)((qrow * D + 16 * kk + 8 * h) * 2));
     dof[kk] = bload16(rdo, (uint32_t)((qrow * D + 16 * kk + 8 * h) * 2));
   }
-  const float l2 = qrow < N ? lsep[(size_t)bh * N + qrow] * kLog2e : INFINITY;
-  const float dd = qrow < N ? deltap[(size_t)bh * N + qrow] : 0.f;
+  const float l2 = qrow < N ? lsep[(size_t)qr0 + qrow] * kLog2e : INFINITY;
+  const float dd = qrow < N ? deltap[(size_t)qr0 + qrow] : 0.f;
   // Q, dO, L, D (and with them tile 0) land before the ring starts.
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
@@ -595,8 +605,9 @@ template <class T, int D, int MODE>
 static hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t st) {
   const int BHkv = a.B * a.Hkv;
   const int nkb = (a.N + 127) / 128;
+  const Geom geo{a.N, a.H, a.H / a.Hkv, a.cu, a.T};
   hipLaunchKernelGGL((dkdv_kernel<T, D, MODE>), dim3(nkb * BHkv), dim3(256), 0, st, a.q, a.k, a.v, a.dO, a.lse,
-                     a.delta, a.dk, a.dv, a.N, BHkv, a.H, a.H / a.Hkv, Win{a.wl, a.wr}, a.scale * kLog2e, a.scale);
+                     a.delta, a.dk, a.dv, geo, BHkv, Win{a.wl, a.wr}, a.scale * kLog2e, a.scale);
   return hipGetLastError();
 }
 
@@ -604,8 +615,9 @@ template <class T, int D, int MODE>
 static hipError_t launch_dq_t(const BwdArgs& a, hipStream_t st) {
   const int BH = a.B * a.H;
   const int nqb = (a.N + 127) / 128;
+  const Geom geo{a.N, a.H, a.H / a.Hkv, a.cu, a.T};
   hipLaunchKernelGGL((dq_kernel<T, D, MODE>), dim3(nqb * BH), dim3(256), 0, st, a.q, a.k, a.v, a.dO, a.lse,
-                     a.delta, a.dq, a.N, BH, nqb, a.H, a.H / a.Hkv, Win{a.wl, a.wr}, a.scale * kLog2e, a.scale);
+                     a.delta, a.dq, geo, BH, nqb, Win{a.wl, a.wr}, a.scale * kLog2e, a.scale);
   return hipGetLastError();
 }
 

@@ -77,6 +77,35 @@ struct Elem<f16_tag> {
 };
 
 // ---------------------------------------------------------------------------
+// Where the (batch b, query head h) slice of each tensor lives, in rows of d
+// elements.  Batched tensors: Q, O, dO, dQ [B, H, N, d]; K, V, dK, dV
+// [B, H/G, N, d]; L, D [B, H, N].  Packed variable-length tensors (cu not
+// null): [H, T, d], [H/G, T, d] and [H, T], sequence b at rows cu[b] ..
+// cu[b+1] - 1 of every head.  Offsets read from cu are clamped to [0, T], so
+// malformed offsets cannot address rows outside the tensors.
+// ---------------------------------------------------------------------------
+struct Geom {
+  int N;          // batched: rows per sequence; packed: the longest sequence
+  int H, G;       // query heads; query heads per key/value head
+  const int* cu;  // packed: B + 1 row offsets in device memory; batched: null
+  int T;          // packed: total rows
+  // First row of the slice in the query-side tensors (and L, D), first row
+  // in the key/value-side tensors, and its number of rows.
+  __device__ __forceinline__ void slice(int b, int h, long& qrow0, long& kvrow0, int& len) const {
+    if (cu) {
+      const int s = min(max(cu[b], 0), T), e = min(max(cu[b + 1], s), T);
+      qrow0 = (long)h * T + s;
+      kvrow0 = (long)(h / G) * T + s;
+      len = e - s;
+    } else {
+      qrow0 = ((long)b * H + h) * N;
+      kvrow0 = ((long)b * (H / G) + h / G) * N;
+      len = N;
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
 // Attention window: key j is visible to query i iff i - left <= j <= i + right,
 // a negative bound meaning unbounded.  The causal mask is the window
 // (left, right) = (-1, 0); kernels compiled without a window (the full mask)

@@ -355,8 +355,7 @@ __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_pipe_kernel(const void*
                                                                      const void* __restrict__ kp,
                                                                      const void* __restrict__ vp,
                                                                      void* __restrict__ op, float* __restrict__ lsep,
-                                                                     int N, int BH, int nqb, int H, int G, Win win_in,
-                                                                     float c) {
+                                                                     Geom geo, int BH, int nqb, Win win_in, float c) {
   // MODE 0: no window (full mask); 1: the causal window (-1, 0), a
   // compile-time constant so that every window test folds; 2: any window.
   constexpr bool MASK = MODE != 0;
@@ -379,10 +378,12 @@ __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_pipe_kernel(const void*
   const int qb = MASK ? (nqb - 1 - x / BH) : (x / BH);
   const int bh = x % BH;
   const int q0 = qb * BM;
-  const size_t head = (size_t)bh * N * D * 2;
-  // K and V of the group: query head h of batch b reads key/value head
-  // b (H / G) + h / G (G = 1 without grouping).
-  const size_t headkv = (size_t)((bh / H) * (H / G) + (bh % H) / G) * N * D * 2;
+  // This (batch, head) slice: query head h reads key/value head h / G.
+  long qr0, kvr0;
+  int N;
+  geo.slice(bh / geo.H, bh % geo.H, qr0, kvr0, N);
+  if (q0 >= N) return;  // past the end of a shorter packed sequence (the whole workgroup)
+  const size_t head = (size_t)qr0 * D * 2, headkv = (size_t)kvr0 * D * 2;
   const uint32_t bytes = (uint32_t)N * D * 2;
   const auto rq = make_rsrc((const char*)qp + head, bytes);
   const auto ro = make_rsrc((char*)op + head, bytes);
@@ -441,15 +442,15 @@ __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_pipe_kernel(const void*
 
   const float lt = sum_with_partner(l);
   store_rows<T, D>(ro, qrow, acc, 1.0f / lt, lane);
-  if (h == 0 && qrow < N) lsep[(size_t)bh * N + qrow] = (mref + log2_fast(lt)) * kLn2;
+  if (h == 0 && qrow < N) lsep[(size_t)qr0 + qrow] = (mref + log2_fast(lt)) * kLn2;
 }
 
 template <class T, int D, int MODE>
 __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_kernel(const void* __restrict__ qp,
                                                                 const void* __restrict__ kp,
                                                                 const void* __restrict__ vp, void* __restrict__ op,
-                                                                float* __restrict__ lsep, int N, int BH, int nqb,
-                                                                int H, int G, Win win_in, float c) {
+                                                                float* __restrict__ lsep, Geom geo, int BH, int nqb,
+                                                                Win win_in, float c) {
   // MODE 0: no window (full mask); 1: the causal window (-1, 0), a
   // compile-time constant so that every window test folds; 2: any window.
   constexpr bool MASK = MODE != 0;
@@ -466,10 +467,12 @@ __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_kernel(const void* __re
   const int qb = MASK ? (nqb - 1 - x / BH) : (x / BH);
   const int bh = x % BH;
   const int q0 = qb * BM;
-  const size_t head = (size_t)bh * N * D * 2;
-  // K and V of the group: query head h of batch b reads key/value head
-  // b (H / G) + h / G (G = 1 without grouping).
-  const size_t headkv = (size_t)((bh / H) * (H / G) + (bh % H) / G) * N * D * 2;
+  // This (batch, head) slice: query head h reads key/value head h / G.
+  long qr0, kvr0;
+  int N;
+  geo.slice(bh / geo.H, bh % geo.H, qr0, kvr0, N);
+  if (q0 >= N) return;  // past the end of a shorter packed sequence (the whole workgroup)
+  const size_t head = (size_t)qr0 * D * 2, headkv = (size_t)kvr0 * D * 2;
   const uint32_t bytes = (uint32_t)N * D * 2;
   const auto rq = make_rsrc((const char*)qp + head, bytes);
   const auto ro = make_rsrc((char*)op + head, bytes);
@@ -514,21 +517,22 @@ __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_kernel(const void* __re
 
   const float lt = sum_with_partner(l);
   store_rows<T, D>(ro, qrow, acc, 1.0f / lt, lane);
-  if (h == 0 && qrow < N) lsep[(size_t)bh * N + qrow] = (mref + log2_fast(lt)) * kLn2;
+  if (h == 0 && qrow < N) lsep[(size_t)qr0 + qrow] = (mref + log2_fast(lt)) * kLn2;
 }
 
 template <class T, int D, int MODE>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   const int BH = a.B * a.H;
   const int BM = 32 * kFwdWaves;
-  const int nqb = (a.N + BM - 1) / BM;
+  const int nqb = (a.N + BM - 1) / BM;  // a.N: the longest sequence when packed
   const Win win{a.wl, a.wr};
+  const Geom geo{a.N, a.H, a.H / a.Hkv, a.cu, a.T};
   if constexpr (kFwdPipelined<D>)
     hipLaunchKernelGGL((fwd_pipe_kernel<T, D, MODE>), dim3(nqb * BH), dim3(64 * kFwdWaves), 0, st, a.q, a.k, a.v,
-                       a.o, a.lse, a.N, BH, nqb, a.H, a.H / a.Hkv, win, a.scale * kLog2e);
+                       a.o, a.lse, geo, BH, nqb, win, a.scale * kLog2e);
   else
     hipLaunchKernelGGL((fwd_kernel<T, D, MODE>), dim3(nqb * BH), dim3(64 * kFwdWaves), 0, st, a.q, a.k, a.v, a.o,
-                       a.lse, a.N, BH, nqb, a.H, a.H / a.Hkv, win, a.scale * kLog2e);
+                       a.lse, geo, BH, nqb, win, a.scale * kLog2e);
   return hipGetLastError();
 }
 

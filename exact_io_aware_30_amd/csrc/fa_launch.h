@@ -15,6 +15,8 @@ struct FwdArgs {
   float scale;
   int wl, wr;  // window: key j visible to query i iff i - wl <= j <= i + wr (negative: unbounded)
   bool bf16;
+  const int* cu = nullptr;  // packed variable-length: B + 1 device row offsets (N = longest sequence)
+  int T = 0;                // packed: total rows
 };
 
 struct PreArgs {
@@ -33,6 +35,8 @@ struct BwdArgs {
   float scale;
   int wl, wr;  // window, as in FwdArgs
   bool bf16;
+  const int* cu = nullptr;  // packed variable-length, as in FwdArgs
+  int T = 0;
 };
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st);

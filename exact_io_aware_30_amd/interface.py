@@ -15,6 +15,10 @@ module.  This module provides the same three names on top of
   form; inputs are made contiguous, the scale defaults to 1/sqrt(D).  k and
   v may carry fewer heads than q (Hkv dividing H): grouped-query attention,
   query head h reading key/value head h / (H / Hkv).
+* ``flash_attn_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False,
+  softmax_scale=None, window_size=(-1, -1))`` -- packed sequences: q (H, T, D),
+  k, v (Hkv, T, D), sequence b at rows cu_seqlens[b] .. cu_seqlens[b+1] - 1,
+  each attended on its own.
 * ``FlashSelfAttention(embed_dim, num_heads, causal=False, bias=True)`` --
   x (B, N, E) -> (B, N, E): one input projection to Q, K, V, attention
   through the kernels, one output projection.  The two projections are
@@ -85,6 +89,47 @@ def flash_attn(q, k, v, causal: bool = False, softmax_scale: float | None = None
         raise ValueError("window_size bounds must be >= -1 (-1: no bound)")
     window = None if (left, right) == (-1, -1) else (left, right)
     return FlashAttnFunction.apply(q, k, v, bool(causal), scale, window)
+
+
+class FlashAttnVarlenFunction(torch.autograd.Function):
+    """Exact attention over packed variable-length sequences."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, cu_seqlens, max_seqlen: int, causal: bool, scale: float, window=None):
+        q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        o, lse = binding.attention_forward_varlen(q, k, v, cu_seqlens, max_seqlen, scale, causal, window)
+        ctx.save_for_backward(q, k, v, o, lse, cu_seqlens)
+        ctx.args = (int(max_seqlen), bool(causal), float(scale), window)
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse, cu = ctx.saved_tensors
+        max_seqlen, causal, scale, window = ctx.args
+        dq, dk, dv, _ = binding.attention_backward_varlen(q, k, v, o, do.contiguous().to(o.dtype), lse, cu,
+                                                          max_seqlen, scale, causal, window)
+        return dq, dk, dv, None, None, None, None, None
+
+
+def flash_attn_varlen(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = False,
+                      softmax_scale: float | None = None, window_size=(-1, -1)):
+    """Attention over packed sequences: q (H, T, D), k and v (Hkv, T, D),
+    cu_seqlens int32 (B + 1,) on the GPU; every sequence attends on its own."""
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q must be (H, T, D) and k, v (Hkv, T, D)")
+    if q.shape[-1] not in HEAD_DIMS:
+        raise ValueError(f"head dimension must be one of {HEAD_DIMS}, got {q.shape[-1]}")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda and cu_seqlens.is_cuda):
+        raise ValueError("q, k, v and cu_seqlens must be GPU tensors: the attention runs only in the HIP kernels")
+    scale = 1.0 / math.sqrt(q.shape[-1]) if softmax_scale is None else float(softmax_scale)
+    if not (math.isfinite(scale) and scale > 0):
+        raise ValueError("softmax_scale must be finite and positive")
+    left, right = (int(window_size[0]), int(window_size[1]))
+    if left < -1 or right < -1:
+        raise ValueError("window_size bounds must be >= -1 (-1: no bound)")
+    window = None if (left, right) == (-1, -1) else (left, right)
+    return FlashAttnVarlenFunction.apply(q, k, v, cu_seqlens.to(torch.int32).contiguous(), int(max_seqlen),
+                                         bool(causal), scale, window)
 
 
 class FlashSelfAttention(torch.nn.Module):

@@ -170,6 +170,36 @@ int fa_bwd_dq_ex(const void* q, const void* k, const void* v, const void* dO,
                  int Hkv, int N, int d, float scale, int window_left,
                  int window_right, fa_dtype dt, void* stream);
 
+/*
+ * Variable-length batches (packed sequences; "flash-attn-triton" docs,
+ * "Scope", lists variable-length batches as not yet done there).  The B
+ * sequences are packed along the row axis of head-major tensors:
+ *   q, o, dO, dq   [H, T, d] of dt;  k, v, dk, dv  [Hkv, T, d] of dt;
+ *   lse, delta     [H, T] float32;
+ *   cu_seqlens     device pointer to B + 1 int32 row offsets: sequence b is
+ *                  rows cu_seqlens[b] .. cu_seqlens[b+1] - 1 of every head,
+ *                  cu_seqlens[0] = 0, nondecreasing, cu_seqlens[B] = T, every
+ *                  length <= max_seqlen.
+ * Each sequence is attended on its own (positions, windows and the causal
+ * mask are relative to its first row); the result equals the batched entry
+ * points applied to every sequence separately.  Offsets are read on the
+ * device and clamped to [0, T], so malformed offsets never address rows
+ * outside the tensors, but give unspecified results (so do lengths above
+ * max_seqlen); empty sequences are allowed.  Per-sequence size limits are
+ * those of a batch of max_seqlen rows.  The pre-pass is fa_bwd_preprocess
+ * with B = 1, H, N = T.  Null cu_seqlens, B, max_seqlen or T below 1 return
+ * FA_ERR_INVALID_ARG; a cu_seqlens not 4-byte aligned FA_ERR_ALIGNMENT.
+ */
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o,
+                  float* lse, const int* cu_seqlens, int B, int max_seqlen,
+                  int T, int H, int Hkv, int d, float scale, int window_left,
+                  int window_right, fa_dtype dt, void* stream);
+int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* dO,
+                  const float* lse, const float* delta, void* dq, void* dk,
+                  void* dv, const int* cu_seqlens, int B, int max_seqlen,
+                  int T, int H, int Hkv, int d, float scale, int window_left,
+                  int window_right, fa_dtype dt, void* stream);
+
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* fa_status_string(int status);
 

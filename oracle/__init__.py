@@ -16,7 +16,7 @@ the identity they rely on.
 
 Modules:
   attention  -- forward (O, L), backward (dQ, dK, dV, D), row/column samplers,
-                grouped-query forms
+                grouped-query, windowed and packed variable-length forms
   softmax    -- safe softmax, the Fig. 3 per-tile recurrence, merge of partials
 """
 
@@ -25,6 +25,7 @@ from .attention import (  # noqa: F401
     attention_backward,
     attention_forward_gqa,
     attention_backward_gqa,
+    attention_backward_varlen,
     delta_rowsum,
     forward_rows,
     dq_rows,

@@ -195,6 +195,31 @@ def attention_backward_gqa(q, k, v, do, scale, causal, row_block=None, window=No
 
 
 # ---------------------------------------------------------------------------
+# Packed variable-length batches (flash-attn-triton docs, "Scope", lists
+# variable-length batches as not yet done there): the B sequences sit along
+# the row axis of [H, T, d] tensors, sequence b at rows cu[b] .. cu[b+1] - 1,
+# and each is attended on its own -- by definition the plain attention of
+# every sequence separately.
+# ---------------------------------------------------------------------------
+def attention_backward_varlen(q, k, v, do, cu, scale, causal, window=None):
+    """Forward and backward quantities for packed sequences: q, do [H,T,d],
+    k, v [Hkv,T,d], cu the B + 1 row offsets.  Returns o, dq [H,T,d], dk, dv
+    [Hkv,T,d], lse, delta [H,T]."""
+    q, k, v, do = _as64(q), _as64(k), _as64(v), _as64(do)
+    H, T, d = q.shape
+    out = {"o": np.zeros_like(q), "dq": np.zeros_like(q), "dk": np.zeros_like(k), "dv": np.zeros_like(v),
+           "lse": np.zeros((H, T)), "delta": np.zeros((H, T))}
+    for s0, s1 in zip(cu[:-1], cu[1:]):
+        if s1 <= s0:
+            continue
+        r = attention_backward_gqa(q[None, :, s0:s1], k[None, :, s0:s1], v[None, :, s0:s1], do[None, :, s0:s1],
+                                   scale, causal, window=window)
+        for name in ("o", "dq", "dk", "dv", "lse", "delta"):
+            out[name][:, s0:s1] = r[name][0]
+    return out
+
+
+# ---------------------------------------------------------------------------
 # Samplers: the same definitions restricted to chosen rows or key columns of
 # one head, for sizes where the whole N x N matrix is too costly on the CPU.
 # ---------------------------------------------------------------------------

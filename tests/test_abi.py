@@ -34,6 +34,7 @@ def test_header_functions_are_exported():
     assert names == sorted(["fa_fwd", "fa_bwd_preprocess", "fa_bwd", "fa_bwd_dkdv", "fa_bwd_dq",
                             "fa_fwd_gqa", "fa_bwd_gqa", "fa_bwd_dkdv_gqa", "fa_bwd_dq_gqa",
                             "fa_fwd_ex", "fa_bwd_ex", "fa_bwd_dkdv_ex", "fa_bwd_dq_ex",
+                            "fa_fwd_varlen", "fa_bwd_varlen",
                             "fa_status_string", "fa_version"])
     out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (fa_\w+)$", out, flags=re.M))
@@ -189,6 +190,22 @@ def test_window_rejects(p):
     assert lib.fa_bwd_dq_ex(*p[:7], 1, 1, 1, 64, 64, 0.125, -4, 0, 1, None) == INVALID
     # the causal flag of the older entry points must be 0 or 1
     assert lib.fa_fwd_gqa(*p[:5], 1, 1, 1, 64, 64, 0.125, 2, 1, None) == INVALID
+
+
+def test_varlen_rejects(p):
+    # fa_fwd_varlen(q, k, v, o, lse, cu, B, max_seqlen, T, H, Hkv, d, scale, wl, wr, dt, stream)
+    def f(cu=None, B=2, mx=32, T=64, H=1, Hkv=1, d=64, wl=-1, wr=0):
+        return lib.fa_fwd_varlen(p[0], p[1], p[2], p[3], p[4], p[5] if cu is None else cu, B, mx, T, H, Hkv, d,
+                                 0.125, wl, wr, 1, None)
+    assert f(cu=0) == INVALID
+    assert f(B=0) == INVALID
+    assert f(mx=0) == INVALID
+    assert f(T=0) == INVALID
+    assert f(Hkv=3, H=2) == INVALID
+    assert f(d=48) == UNSUPPORTED
+    assert f(wl=-7) == INVALID
+    assert f(cu=p[5] + 2) == ALIGN
+    assert lib.fa_bwd_varlen(*p[:9], 0, 2, 32, 64, 1, 1, 64, 0.125, -1, 0, 1, None) == INVALID
 
 
 def test_binding_rejects_host_tensors():

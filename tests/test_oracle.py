@@ -525,3 +525,56 @@ def test_window_gradients_match_central_differences(window):
             xm[idx] -= h
             g[idx] = (f(*[xp if x is t else t for t in (q, k, v)]) - f(*[xm if x is t else t for t in (q, k, v)])) / (2 * h)
         assert np.max(np.abs(g - out[name])) / np.max(np.abs(g)) <= 1e-7, name
+
+
+# --------------------------------------------------------------------------
+# Packed variable-length batches (flash-attn-triton docs, "Scope")
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal,window", [(False, None), (True, None), (False, (3, 2)), (True, (4, -1))])
+def test_varlen_against_torch_block_diagonal(causal, window):
+    # the packed sequences attended as one long sequence under a
+    # block-diagonal mask (plus the causal mask / window within each block)
+    lens = [5, 1, 0, 9, 3]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(int)
+    T, H, Hkv, d = int(cu[-1]), 4, 2, 6
+    q, do = (rand((H, T, d), 160 + i) for i in range(2))
+    k, v = (rand((Hkv, T, d), 170 + i) for i in range(2))
+    seq = np.repeat(np.arange(len(lens)), lens)
+    pos = np.concatenate([np.arange(n) for n in lens])
+    i_, j_ = pos[:, None], pos[None, :]
+    ok = seq[:, None] == seq[None, :]
+    if causal:
+        ok &= j_ <= i_
+    if window is not None:
+        if window[0] >= 0:
+            ok &= j_ >= i_ - window[0]
+        if window[1] >= 0:
+            ok &= j_ <= i_ + window[1]
+    okt = torch.tensor(ok)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    s = ((tq @ tk.repeat_interleave(2, dim=0).transpose(-1, -2)) * 0.5).masked_fill(~okt, float("-inf"))
+    o_t = torch.softmax(s, dim=-1) @ tv.repeat_interleave(2, dim=0)
+    o_t.backward(torch.tensor(do))
+    out = oracle.attention_backward_varlen(q, k, v, do, cu, 0.5, causal, window)
+
+    def rel(a, b):
+        return np.max(np.abs(a - b)) / np.max(np.abs(b))
+
+    assert rel(out["o"], o_t.detach().numpy()) <= 1e-12
+    assert rel(out["lse"], torch.logsumexp(s, -1).detach().numpy()) <= 1e-12
+    for name, t in (("dq", tq), ("dk", tk), ("dv", tv)):
+        assert rel(out[name], t.grad.numpy()) <= 1e-12, name
+
+
+def test_varlen_equal_lengths_is_the_batched_layout():
+    B, H, N, d = 3, 2, 11, 4
+    q, k, v, do = (rand((B, H, N, d), 180 + i) for i in range(4))
+    packed = [x.transpose(1, 0, 2, 3).reshape(H, B * N, d) for x in (q, k, v, do)]
+    out = oracle.attention_backward_varlen(*packed, np.arange(0, B * N + 1, N), 0.7, True)
+    ref = attention_backward(q, k, v, do, 0.7, True)
+    for name in ("o", "dq", "dk", "dv"):
+        np.testing.assert_allclose(out[name], ref[name].transpose(1, 0, 2, 3).reshape(H, B * N, d),
+                                   rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(out["lse"], ref["lse"].transpose(1, 0, 2).reshape(H, B * N), rtol=1e-14,
+                               atol=1e-14)
