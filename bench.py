@@ -16,6 +16,18 @@ both halved under the causal mask.
     python bench.py --sweep     bf16 causal d=128, B=1, H=16, N = 1K .. 64K:
                                 one pass of each kernel per N (for hardware
                                 counters) and its time
+    python bench.py --compare   ordinary attention (library GEMMs, softmax,
+                                S and P in device memory) beside the tiled
+                                kernels on every workload: forward+backward
+                                time, peak device memory, exact traffic
+                                counts of both and, from the committed
+                                counter summary, the measured bytes
+    python bench.py --oom       bf16 causal d=128, B=1, H=16, N = 4K .. 128K:
+                                peak memory and time of both versions until
+                                ordinary attention runs out of memory
+    python bench.py --compare-step flash|ordinary --workload W
+                                one forward+backward step of one version
+                                (for hardware byte counters)
 
 Without --report or --sweep it prints one JSON line.  Besides the contract fields it carries
   roofline      the dominant kernel (longest average launch, timed with HIP
@@ -225,6 +237,247 @@ def sweep():
         torch.cuda.empty_cache()
 
 
+# --------------------------------------------------------------------------
+# Ordinary attention beside the tiled kernels: time, peak memory, the point
+# where it runs out of memory, and the exact traffic of both versions
+# ("flash-attn-triton" docs, "The argument", Table 2, "Work it out" / Fig. 2,
+# "Scope"; "What is FlashAttention?", "Why is it faster if it does the same
+# math?" and "What you will build")
+# --------------------------------------------------------------------------
+
+def ordinary_attention(q, k, v, do, scale, causal, mask=None):
+    """Ordinary attention forward and backward on the GPU from library GEMMs,
+    softmax and elementwise kernels: S = scale QK^T, the causal mask and
+    P = softmax(S) go through device memory, then O = PV; backward dV = P^T dO,
+    dP = dO V^T, dS = P o (dP - rowsum(P o dP)), dQ = scale dS K,
+    dK = scale dS^T Q.  q, k, v, do: contiguous (B, H, N, d).  Every batched
+    product takes contiguous operands (transposed N x d copies are made
+    explicitly).  ``mask``: the (N, N) bool array of hidden entries (key
+    after query), built by the caller.  Returns (o, dq, dk, dv)."""
+    import torch
+
+    B, H, N, d = q.shape
+    q3, k3, v3, do3 = (x.reshape(B * H, N, d) for x in (q, k, v, do))
+    kt = k3.transpose(1, 2).contiguous()
+    s = torch.empty(B * H, N, N, dtype=q.dtype, device=q.device).baddbmm_(q3, kt, beta=0.0, alpha=scale)
+    del kt
+    if causal:
+        s.masked_fill_(mask, float("-inf"))
+    p = torch.softmax(s, dim=-1)
+    del s
+    o = torch.bmm(p, v3)
+    dot = do3.transpose(1, 2).contiguous()
+    dv = torch.bmm(dot, p).transpose(1, 2).contiguous()
+    del dot
+    vt = v3.transpose(1, 2).contiguous()
+    dp = torch.bmm(do3, vt)
+    del vt
+    ds = torch.ops.aten._softmax_backward_data(dp, p, -1, p.dtype)
+    del dp, p
+    dq = torch.empty(B * H, N, d, dtype=q.dtype, device=q.device).baddbmm_(ds, k3, beta=0.0, alpha=scale)
+    qt = q3.transpose(1, 2).contiguous()
+    dk = torch.empty(B * H, d, N, dtype=q.dtype, device=q.device).baddbmm_(qt, ds, beta=0.0, alpha=scale)
+    dk = dk.transpose(1, 2).contiguous()
+    shape = (B, H, N, d)
+    return o.view(shape), dq.view(shape), dk.view(shape), dv.view(shape)
+
+
+def causal_mask(n, device):
+    """(N, N) bool, True where the key comes after the query; built on the
+    host and copied, so that building it launches no kernel."""
+    import torch
+
+    return torch.ones(n, n, dtype=torch.bool).triu_(1).to(device)
+
+
+def _flash_step(q, k, v, do, o, dq, dk, dv, lse, delta, scale, causal):
+    from exact_io_aware_30_amd import binding
+
+    binding.fa_fwd(q, k, v, o, lse, scale, causal)
+    binding.fa_bwd_preprocess(o, do, delta)
+    binding.fa_bwd(q, k, v, do, lse, delta, dq, dk, dv, scale, causal)
+
+
+def _peak_growth(fn):
+    """Device memory fn allocates at its peak beyond what was allocated before."""
+    import torch
+
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    fn()
+    torch.cuda.synchronize()
+    return torch.cuda.max_memory_allocated() - base
+
+
+def io_summary_bytes(path=os.path.join(ROOT, "profiles", "io_compare_counters.txt")):
+    """{(workload, version): (read bytes, written bytes)} measured by the
+    committed counter summary of one forward+backward step, or {}."""
+    out = {}
+    if not os.path.exists(path):
+        return out
+    for line in open(path):
+        m = re.match(r"^measured (\w+) (\w+): read (\d+) written (\d+)", line)
+        if m:
+            out[(m.group(1), m.group(2))] = (int(m.group(3)), int(m.group(4)))
+    return out
+
+
+COMPARE_WORKLOADS = ("tiny", "gpt2_medium", "ragged", "long", "batch1_64k")
+
+
+def compare():
+    """Both versions on every workload: forward+backward time, peak device
+    memory beyond inputs and outputs, and the exact traffic counts."""
+    import torch
+
+    from exact_io_aware_30_amd import workloads
+
+    dev = torch.device("cuda:0")
+    measured = io_summary_bytes()
+    rows = []
+    for name in COMPARE_WORKLOADS:
+        w = workloads.WORKLOADS[name]
+        q, k, v, do, o, dq, dk, dv, lse, delta = _inputs(w, dev)
+        e = q.element_size()
+        flash = lambda: _flash_step(q, k, v, do, o, dq, dk, dv, lse, delta, w.scale, w.causal)  # noqa: E731
+        reps = 5 if w.N * w.N * w.B * w.H > 1 << 33 else 20
+        mem_f = _peak_growth(flash)
+        t_f = _median_ms(flash, warmup=3, reps=reps)
+        run_ordinary = w.N * w.N <= ORDINARY_MAX_SLICE
+        if run_ordinary:
+            mask = causal_mask(w.N, dev) if w.causal else None
+            ordinary = lambda: ordinary_attention(q, k, v, do, w.scale, w.causal, mask)  # noqa: E731
+            # the comparator's peak includes the four outputs it returns, not its mask
+            mem_o = _peak_growth(ordinary) - 4 * w.elems * e + (mask.numel() if w.causal else 0)
+            t_o = _median_ms(ordinary, warmup=2, reps=reps)
+            od = ordinary()
+            torch.cuda.synchronize()
+            diff = max((a.float() - b.float()).abs().max().item() / max(b.float().abs().max().item(), 1e-30)
+                       for a, b in zip(od, (o, dq, dk, dv)))
+            del od, mask, ordinary
+        cnt_t = sum(r + x for r, x in workloads.io_count_tiled(w.B, w.H, w.N, w.d, e, w.causal).values())
+        cnt_o = sum(r + x for _, r, x in workloads.io_count_ordinary(w.B, w.H, w.N, w.d, e, w.causal))
+        alg = sum(workloads.algorithmic_bytes(w).values())
+        r = {"workload": w.describe(), "flash_fwd_bwd_ms": round(t_f[0], 4), "flash_peak_extra_bytes": int(mem_f),
+             "flash_count_bytes": cnt_t, "ordinary_count_bytes": cnt_o, "algorithmic_bytes": alg}
+        if run_ordinary:
+            r.update({"ordinary_fwd_bwd_ms": round(t_o[0], 4), "speedup": round(t_o[0] / t_f[0], 2),
+                      "ordinary_peak_extra_bytes": int(mem_o), "max_rel_diff_outputs": round(diff, 5)})
+        else:
+            r["ordinary"] = "not run: score matrix above 2^31 elements per slice"
+        for ver in ("flash", "ordinary"):
+            if (name, ver) in measured:
+                r[f"{ver}_measured_bytes"] = sum(measured[(name, ver)])
+        rows.append(r)
+        del q, k, v, do, o, dq, dk, dv, lse, delta
+        torch.cuda.empty_cache()
+    print("| workload | ordinary ms | tiled ms | speed-up | ordinary peak extra | tiled peak extra "
+          "| ordinary count | tiled count | ordinary measured | tiled measured |")
+    print("|---|---|---|---|---|---|---|---|---|---|")
+    gib = lambda x: f"{x / 2**30:.3f} GiB" if x is not None else "-"  # noqa: E731
+    for r in rows:
+        t_o = f"{r['ordinary_fwd_bwd_ms']:.3f}" if "ordinary_fwd_bwd_ms" in r else "not run"
+        sp = f"{r['speedup']}x" if "speedup" in r else "-"
+        print(f"| {r['workload'].split(':')[0]} | {t_o} | {r['flash_fwd_bwd_ms']:.3f} "
+              f"| {sp} | {gib(r.get('ordinary_peak_extra_bytes'))} | {gib(r['flash_peak_extra_bytes'])} "
+              f"| {gib(r['ordinary_count_bytes'])} | {gib(r['flash_count_bytes'])} "
+              f"| {gib(r.get('ordinary_measured_bytes'))} | {gib(r.get('flash_measured_bytes'))} |")
+    for r in rows:
+        print(json.dumps(r), flush=True)
+
+
+OOM_N = (4096, 8192, 16384, 32768, 65536, 131072)
+# Library GEMM and softmax calls are only made on score matrices of at most
+# 2^31 elements per (batch, head) slice.
+ORDINARY_MAX_SLICE = 1 << 31
+
+
+def _ordinary_fits(bh, n, dtype, device):
+    """Try to allocate what ordinary attention holds at its peak (four
+    N x N matrices per slice: P, dP, dS and the P o dP product torch's
+    softmax backward forms, plus the N x N mask) without launching anything.
+    Returns None if it fits, else the allocator's message."""
+    import torch
+
+    held = []
+    try:
+        for _ in range(4):
+            held.append(torch.empty(bh, n, n, dtype=dtype, device=device))
+        held.append(torch.empty(n, n, dtype=torch.bool, device=device))
+        return None
+    except torch.cuda.OutOfMemoryError as err:
+        return str(err).split("\n")[0][:200]
+    finally:
+        del held
+        torch.cuda.empty_cache()
+
+
+def oom():
+    """bf16 causal d=128, B=1, H=16, N doubling: peak device memory and time of
+    both versions until ordinary attention runs out of device memory (found by
+    allocating its peak working set, which launches nothing)."""
+    import torch
+
+    from exact_io_aware_30_amd import workloads
+
+    dev = torch.device("cuda:0")
+    total = torch.cuda.get_device_properties(0).total_memory
+    ordinary_ok = True
+    for n in OOM_N:
+        w = workloads.Workload(f"oom{n}", "bf16", 1, 16, n, 128, True, 1.0, 3000 + n // 1024)
+        q, k, v, do, o, dq, dk, dv, lse, delta = _inputs(w, dev)
+        e = q.element_size()
+        fp = workloads.footprint(w.B, w.H, n, w.d, e, total)
+        r = {"N": n, "B": 1, "H": 16, "d": 128, "device_bytes": total, "score_matrix_bytes": fp["score"],
+             "score_matrix_alone_runs_out_at_N": fp["n_max"]}
+        flash = lambda: _flash_step(q, k, v, do, o, dq, dk, dv, lse, delta, w.scale, w.causal)  # noqa: E731
+        r["flash_peak_extra_bytes"] = int(_peak_growth(flash))
+        r["flash_fwd_bwd_ms"] = round(_median_ms(flash, warmup=1, reps=3)[0], 3)
+        if not ordinary_ok:
+            r["ordinary"] = "not run (out of memory at a smaller N)"
+        elif n * n > ORDINARY_MAX_SLICE:
+            msg = _ordinary_fits(w.B * w.H, n, q.dtype, dev)
+            if msg is None:
+                r["ordinary"] = "fits, not run (score matrix above 2^31 elements per slice)"
+            else:
+                ordinary_ok = False
+                r["ordinary"] = "out of memory: " + msg
+        else:
+            mask = causal_mask(n, dev)
+            run = lambda: ordinary_attention(q, k, v, do, w.scale, True, mask)  # noqa: E731
+            try:
+                r["ordinary_peak_extra_bytes"] = int(_peak_growth(run) - 4 * w.elems * e + mask.numel())
+                r["ordinary_fwd_bwd_ms"] = round(_median_ms(run, warmup=1, reps=3)[0], 3)
+            except torch.cuda.OutOfMemoryError as err:
+                ordinary_ok = False
+                r["ordinary"] = "out of memory: " + str(err).split("\n")[0][:200]
+            del mask, run
+        print(json.dumps(r), flush=True)
+        del q, k, v, do, o, dq, dk, dv, lse, delta
+        torch.cuda.empty_cache()
+
+
+def compare_step(version, name):
+    """One forward+backward step of one version on one workload, nothing else
+    launched on the device (for hardware byte counters)."""
+    import torch
+
+    from exact_io_aware_30_amd import workloads
+
+    w = workloads.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    q, k, v, do, o, dq, dk, dv, lse, delta = _inputs(w, dev)
+    mask = causal_mask(w.N, dev) if w.causal else None
+    torch.cuda.synchronize()
+    if version == "flash":
+        _flash_step(q, k, v, do, o, dq, dk, dv, lse, delta, w.scale, w.causal)
+    else:
+        ordinary_attention(q, k, v, do, w.scale, w.causal, mask)
+    torch.cuda.synchronize()
+    print(json.dumps({"compare_step": version, "workload": w.describe()}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -234,6 +487,9 @@ def main():
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--report", action="store_true")
     ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--compare", action="store_true")
+    ap.add_argument("--oom", action="store_true")
+    ap.add_argument("--compare-step", choices=("flash", "ordinary"), default=None)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed steps, copy a buffer of this many MiB once (a kernel of known "
                          "traffic for scaling hardware byte counters)")
@@ -243,8 +499,13 @@ def main():
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
-    if args.report or args.sweep:
-        report() if args.report else sweep()
+    if args.compare_step:
+        compare_step(args.compare_step, args.workload)
+        if args.calib_copy_mib:
+            calib_copy(args.calib_copy_mib)
+        return
+    if args.report or args.sweep or args.compare or args.oom:
+        (report if args.report else sweep if args.sweep else compare if args.compare else oom)()
         if args.calib_copy_mib:
             calib_copy(args.calib_copy_mib)
         return

@@ -138,3 +138,114 @@ def footprint(B: int, H: int, N: int, d: int, elem_bytes: int, capacity_bytes: f
     if capacity_bytes is not None:
         res["n_max"] = int(math.isqrt(int(capacity_bytes // (B * H * elem_bytes))))
     return res
+
+
+# --------------------------------------------------------------------------
+# Exact memory-traffic counts of the two versions
+# ("flash-attn-triton" docs, "The argument" and Table 2; "What is
+# FlashAttention?", "What you will build", step 03)
+# --------------------------------------------------------------------------
+
+# Tile geometry of the HIP kernels, as they request rows from device memory:
+# forward: query blocks of 256 rows, key tiles of 64; dK/dV: key blocks of 128
+# rows, query tiles of 32 (64 at d = 32) with the L and D vectors fetched 64
+# entries per tile; dQ: query blocks of 128 rows, key tiles of 64.
+def kernel_tiles(d: int) -> dict:
+    return {"fwd_bm": 256, "fwd_bn": 64, "dkdv_bk": 128, "dkdv_bq": 64 if d == 32 else 32, "dkdv_stats": 64,
+            "dq_bm": 128, "dq_bn": 64}
+
+
+def _blocks(n: int, size: int):
+    import numpy as np
+
+    start = np.arange(0, n, size, dtype=np.int64)
+    return start, np.minimum(size, n - start)
+
+
+def _key_rows(n: int, q0, bm: int, bn: int, causal: bool):
+    """Key rows a query block starting at q0 loads: whole key tiles up to its
+    last visible key, the tile past row n - 1 clipped."""
+    import numpy as np
+
+    if not causal:
+        return np.full_like(q0, n)
+    kend = np.minimum(n, q0 + bm)
+    return np.minimum(n, -(-kend // bn) * bn)
+
+
+def io_count_tiled(B: int, H: int, N: int, d: int, e: int, causal: bool, tiles: dict | None = None) -> dict:
+    """Bytes each tiled kernel reads from and writes to device memory, counting
+    every tile load a workgroup issues (no cache): {kernel: (read, written)}.
+
+    Per (batch, head) slice of N rows:
+      fwd       Q, O and L once; K and V once per query block, up to the last
+                key tile the block sees (all N keys without the causal mask).
+      preprocess O and dO read, D written once.
+      dK/dV     K, V, dK, dV once; per key block, Q and dO from its first
+                visible query row to N, and L and D in 64-entry pieces, one
+                per query tile.
+      dQ        Q, dO, L, D and dQ once; K and V once per query block, as in
+                the forward.
+    Writes are linear in N: no N x N data is stored.
+    """
+    import numpy as np
+
+    t = dict(kernel_tiles(d) if tiles is None else tiles)
+    row = d * e
+    q0, rq = _blocks(N, t["fwd_bm"])
+    kv = _key_rows(N, q0, t["fwd_bm"], t["fwd_bn"], causal)
+    fwd = (int(rq.sum()) * row + 2 * int(kv.sum()) * row, N * (row + 4))
+    pre = (2 * N * row, 4 * N)
+    k0, rk = _blocks(N, t["dkdv_bk"])
+    i_start = k0 if causal else np.zeros_like(k0)
+    stats = 0
+    for s in i_start.tolist():
+        i0 = np.arange(s, N, t["dkdv_bq"], dtype=np.int64)
+        stats += int(np.minimum(t["dkdv_stats"], N - i0).sum())
+    dkdv = (2 * int(rk.sum()) * row + 2 * int((N - i_start).sum()) * row + 2 * 4 * stats, 2 * N * row)
+    q0, rq = _blocks(N, t["dq_bm"])
+    kv = _key_rows(N, q0, t["dq_bm"], t["dq_bn"], causal)
+    dq = (int(rq.sum()) * (2 * row + 8) + 2 * int(kv.sum()) * row, N * row)
+    bh = B * H
+    return {k: (bh * r, bh * w) for k, (r, w) in
+            (("fwd", fwd), ("bwd_preprocess", pre), ("bwd_dkdv", dkdv), ("bwd_dq", dq))}
+
+
+def io_count_ordinary(B: int, H: int, N: int, d: int, e: int, causal: bool, layout_copies: bool = True) -> list:
+    """Bytes each step of ordinary attention reads and writes, each operand
+    read once and each result written once: [(step, read, written)].
+
+    The score matrix S, the probabilities P and, backward, dP and dS are
+    N x N per (batch, head) and go through device memory.  With
+    ``layout_copies`` the list also holds the N x d transposed copies and
+    the causal mask pass the GPU comparator performs (the mask is one
+    N x N byte array, read once per slice); without them it is the plain
+    algorithm: S = scale QK^T written, read back by the softmax, P written
+    and read by PV; backward dV = P^T dO, dP = dO V^T, dS = P o (dP - D),
+    dQ = scale dS K, dK = scale dS^T Q.
+    """
+    nd, nn = N * d * e, N * N * e
+    steps = []
+    add = lambda name, r, w: steps.append((name, B * H * r, B * H * w))  # noqa: E731
+    if layout_copies:
+        add("K^T copy", nd, nd)
+    add("S = scale Q K^T", 2 * nd, nn)
+    if causal and layout_copies:
+        add("mask S", nn + N * N, nn)
+    add("P = softmax(S)", nn, nn)
+    add("O = P V", nn + nd, nd)
+    if layout_copies:
+        add("dO^T copy", nd, nd)
+    add("dV = P^T dO", nn + nd, nd)
+    if layout_copies:
+        add("dV transpose copy", nd, nd)
+        add("V^T copy", nd, nd)
+    add("dP = dO V^T", 2 * nd, nn)
+    add("dS = P o (dP - D)", 2 * nn, nn)
+    add("dQ = scale dS K", nn + nd, nd)
+    if layout_copies:
+        add("Q^T copy", nd, nd)
+    add("dK = scale dS^T Q", nn + nd, nd)
+    if layout_copies:
+        add("dK transpose copy", nd, nd)
+    return steps
