@@ -28,8 +28,10 @@ both halved under the causal mask.
     python bench.py --compare-step flash|ordinary --workload W
                                 one forward+backward step of one version
                                 (for hardware byte counters)
+    --results PATH              also write every JSON record the run prints
+                                to PATH as one JSON list (a results file)
 
-Without --report or --sweep it prints one JSON line.  Besides the contract fields it carries
+Without a mode option it prints one JSON line.  Besides the contract fields it carries
   roofline      the dominant kernel (longest average launch, timed with HIP
                 events on the launch stream over the timed region) against
                 the dense bf16 MFMA peak, plus its HBM traffic per launch
@@ -59,6 +61,15 @@ METRIC = "attention fwd+bwd TFLOP/s (bf16 causal N=8192 d=128) + % of MFMA peak"
 WORKLOAD = "long"
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_traffic_long.txt")
 LIBRARY = os.path.join(ROOT, "exact_io_aware_30_amd", "libfa_mi355x.so")
+
+
+RECORDS = []  # every JSON record printed, for --results
+
+
+def emit(record):
+    """Print one JSON record on its own line and keep it for --results."""
+    RECORDS.append(record)
+    print(json.dumps(record), flush=True)
 
 
 def library_hash():
@@ -203,7 +214,7 @@ def report():
               f"| {r['fwd_tflops']} | {r['bwd_tflops']} | {r['fwd_bwd_tflops']} | {100 * r['frac_mfma_peak']:.1f} "
               f"| {r['device_memory_growth_bytes']} B | {r['oracle_one_head_s']} s ({r['oracle_tflops']} TF/s) |")
     for r in rows:
-        print(json.dumps(r), flush=True)
+        emit(r)
 
 
 SWEEP_N = (1024, 2048, 4096, 8192, 16384, 32768, 65536)
@@ -230,9 +241,8 @@ def sweep():
                                 binding.fa_bwd_preprocess(o, do, delta),
                                 binding.fa_bwd(q, k, v, do, lse, delta, dq, dk, dv, w.scale, w.causal)),
                        warmup=2, reps=5)
-        print(json.dumps({"N": n, "B": 1, "H": 16, "d": 128, "fwd_bwd_ms": round(t[0], 4),
-                          "fwd_bwd_tflops": round(fb / t[0] / 1e9, 1),
-                          "algorithmic_bytes": workloads.algorithmic_bytes(w)}), flush=True)
+        emit({"N": n, "B": 1, "H": 16, "d": 128, "fwd_bwd_ms": round(t[0], 4),
+              "fwd_bwd_tflops": round(fb / t[0] / 1e9, 1), "algorithmic_bytes": workloads.algorithmic_bytes(w)})
         del q, k, v, do, o, dq, dk, dv, lse, delta
         torch.cuda.empty_cache()
 
@@ -384,7 +394,7 @@ def compare():
               f"| {gib(r['ordinary_count_bytes'])} | {gib(r['flash_count_bytes'])} "
               f"| {gib(r.get('ordinary_measured_bytes'))} | {gib(r.get('flash_measured_bytes'))} |")
     for r in rows:
-        print(json.dumps(r), flush=True)
+        emit(r)
 
 
 OOM_N = (4096, 8192, 16384, 32768, 65536, 131072)
@@ -453,7 +463,7 @@ def oom():
                 ordinary_ok = False
                 r["ordinary"] = "out of memory: " + str(err).split("\n")[0][:200]
             del mask, run
-        print(json.dumps(r), flush=True)
+        emit(r)
         del q, k, v, do, o, dq, dk, dv, lse, delta
         torch.cuda.empty_cache()
 
@@ -475,7 +485,7 @@ def compare_step(version, name):
     else:
         ordinary_attention(q, k, v, do, w.scale, w.causal, mask)
     torch.cuda.synchronize()
-    print(json.dumps({"compare_step": version, "workload": w.describe()}), flush=True)
+    emit({"compare_step": version, "workload": w.describe()})
 
 
 def main():
@@ -490,10 +500,21 @@ def main():
     ap.add_argument("--compare", action="store_true")
     ap.add_argument("--oom", action="store_true")
     ap.add_argument("--compare-step", choices=("flash", "ordinary"), default=None)
+    ap.add_argument("--results", default=None, help="also write every JSON record printed to this file "
+                                                    "(a JSON list)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed steps, copy a buffer of this many MiB once (a kernel of known "
                          "traffic for scaling hardware byte counters)")
     args = ap.parse_args()
+    try:
+        run(args)
+    finally:
+        if args.results and RECORDS:
+            with open(args.results, "w") as f:
+                json.dump(RECORDS, f, indent=1)
+
+
+def run(args):
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -605,7 +626,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
-    print(json.dumps(line), flush=True)
+    emit(line)
 
 
 if __name__ == "__main__":
