@@ -199,6 +199,34 @@ __device__ __forceinline__ u32x4 lds_cols_operand(const lds_char* tile, int kc, 
   return (u32x4){a.x, a.y, b.x, b.y};
 }
 
+// The same two operands through per-lane byte offsets computed once.  The
+// swizzle depends only on a row's index modulo 16, so moving the first row
+// by a multiple of 16 moves every lane's address by the same amount: a rows
+// operand of row block 32a is rows_offset(kk) + 32a * 2D bytes from the tile,
+// and a cols operand of row chunk kc is cols_offset(col0, half) + kc * 32D
+// bytes.  Kernels add the per-lane offsets to a tile base once per tile and
+// let the row-block terms fold into the read instructions' immediates.
+template <int D>
+__device__ __forceinline__ uint32_t rows_offset(int kk, int lane) {
+  return (uint32_t)Swz<D>::chunk(lane & 31, 2 * kk + (lane >> 5));
+}
+template <int D>
+__device__ __forceinline__ uint32_t cols_offset(int col0, int half, int lane) {
+  const int g = lane >> 4, t = lane & 15, h = lane >> 5;
+  return (uint32_t)Swz<D>::elem4(4 * h + (t >> 2) + 8 * half, col0 + 16 * (g & 1) + 4 * (t & 3));
+}
+// Reads at p + OFF (a compile-time byte offset).
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_read16_at(const lds_char* p) {
+  return *(const u32x4*)(p + OFF);
+}
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_cols_at(const lds_char* p0, const lds_char* p1) {
+  u32x2 a = ds_read_tr16(p0 + OFF);
+  u32x2 b = ds_read_tr16(p1 + OFF);
+  return (u32x4){a.x, a.y, b.x, b.y};
+}
+
 // ---------------------------------------------------------------------------
 // Global -> LDS copies without registers: buffer_load_dword{,x4} ... lds.  One
 // instruction moves 64 lanes x 4 or 16 bytes; lane l's bytes land at LDS

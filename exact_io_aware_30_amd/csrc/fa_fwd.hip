@@ -270,9 +270,9 @@ __device__ __forceinline__ void pipe_wait(int t, int nt) {
 template <class T, int D, bool MASK, int IDX>
 __device__ __forceinline__ void fwd_pipe_step(lds_char* lds, int t, int nt, int ntw, int tb,
                                               const DmaTile<kFwdBN, D, kFwdWaves>& dma, Rsrc rk, Rsrc rv,
-                                              const u32x4* qf, f32x16* acc, f32x16* s_cur, f32x16* s_nxt,
-                                              float& mref, float& l, int wq0, int qrow, int N, Win win, float c,
-                                              int w, int lane) {
+                                              const u32x4* qf, const uint32_t* koff, const uint32_t* voff,
+                                              f32x16* acc, f32x16* s_cur, f32x16* s_nxt, float& mref, float& l,
+                                              int wq0, int qrow, int N, Win win, float c, int w, int lane) {
   constexpr int S = kPipeStages, BN = kFwdBN, TILE = BN * D * 2, NB = D / 32, NKK = D / 16, NA = kFwdNA;
   pipe_wait<2 * DmaTile<kFwdBN, D, kFwdWaves>::PER>(t, nt);
   if (t + S - 1 < nt) fwd_pipe_issue<D, (IDX + S - 1) % S>(lds, tb + t + S - 1, dma, rk, rv, w);
@@ -282,8 +282,16 @@ __device__ __forceinline__ void fwd_pipe_step(lds_char* lds, int t, int nt, int 
   // full set of per-buffer, per-lane addresses out of the loop.
   uint32_t vb = (uint32_t)(uintptr_t)lds + (S + IDX) * TILE, kb = (uint32_t)(uintptr_t)lds + ((IDX + 1) % S) * TILE;
   asm volatile("" : "+v"(vb), "+v"(kb));
-  const lds_char* vcur = (const lds_char*)(uintptr_t)vb;
-  const lds_char* knxt = (const lds_char*)(uintptr_t)kb;
+  // Operand addresses of this step: one add per per-lane offset, the row
+  // blocks as immediates (32 rows of K are 64D bytes, 16 rows of V 32D).
+  const lds_char* kp[NKK];
+  const lds_char* vp[NB][2];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) kp[kk] = (const lds_char*)(uintptr_t)(kb + koff[kk]);
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int x = 0; x < 2; ++x) vp[b][x] = (const lds_char*)(uintptr_t)(vb + voff[2 * b + x]);
 
   // Run 1: S^T(t+1) = K(t+1) Q^T, MFMA i = (kk = i / NA, a = i % NA), and
   // p = 2^(S(t) c - mref), row sums and packing of tile t, E elements per
@@ -296,13 +304,13 @@ __device__ __forceinline__ void fwd_pipe_step(lds_char* lds, int t, int nt, int 
     const float mr = mref == -INFINITY ? 0.f : mref;  // all of a row masked so far: p = 0
     u32x4 pf[2 * NA];
 #pragma unroll
-    for (int i = 0; i < PRE; ++i) kop[i] = lds_rows_operand<D>(knxt, 32 * (i % NA), i / NA, lane);
+    for (int i = 0; i < PRE; ++i) kop[i] = *(const u32x4*)(kp[i / NA] + 64 * D * (i % NA));
 #pragma unroll
     for (int a = 0; a < NA; ++a) s_nxt[a] = (f32x16){};
     fwd_prio_begin();
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
-      if (i + PRE < NM) kop[i + PRE] = lds_rows_operand<D>(knxt, 32 * ((i + PRE) % NA), (i + PRE) / NA, lane);
+      if (i + PRE < NM) kop[i + PRE] = *(const u32x4*)(kp[(i + PRE) / NA] + 64 * D * ((i + PRE) % NA));
       s_nxt[i % NA] = Elem<T>::mma(kop[i], qf[i / NA], s_nxt[i % NA]);
 #pragma unroll
       for (int e = 0; e < E; ++e) {
@@ -331,12 +339,16 @@ __device__ __forceinline__ void fwd_pipe_step(lds_char* lds, int t, int nt, int 
     constexpr int NM2 = 2 * NA * NB, F = 16 * NA / NM2, PRE2 = NM2 < 2 ? NM2 : 2;
     u32x4 vop[NM2];
 #pragma unroll
-    for (int i = 0; i < PRE2; ++i) vop[i] = lds_cols_operand<D>(vcur, i / NB, 32 * (i % NB), lane);
+    for (int i = 0; i < PRE2; ++i)
+      vop[i] = lds_cols_at<0>(vp[i % NB][0] + 32 * D * (i / NB), vp[i % NB][1] + 32 * D * (i / NB));
     float mx = -INFINITY;
     fwd_prio_begin();
 #pragma unroll
     for (int i = 0; i < NM2; ++i) {
-      if (i + PRE2 < NM2) vop[i + PRE2] = lds_cols_operand<D>(vcur, (i + PRE2) / NB, 32 * ((i + PRE2) % NB), lane);
+      if (i + PRE2 < NM2) {
+        const int n = i + PRE2;
+        vop[n] = lds_cols_at<0>(vp[n % NB][0] + 32 * D * (n / NB), vp[n % NB][1] + 32 * D * (n / NB));
+      }
       acc[i % NB] = Elem<T>::mma(vop[i], pf[i / NB], acc[i % NB]);
 #pragma unroll
       for (int e = 0; e < F; ++e) {
@@ -405,6 +417,11 @@ __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_pipe_kernel(const void*
   u32x4 qf[NKK];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) qf[kk] = bload16(rq, (uint32_t)((qrow * D + 16 * kk + 8 * h) * 2));
+  uint32_t koff[NKK], voff[2 * NB];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) koff[kk] = rows_offset<D>(kk, lane);
+#pragma unroll
+  for (int x = 0; x < 2 * NB; ++x) voff[x] = cols_offset<D>(32 * (x / 2), x % 2, lane);
   // Q has landed (and with it tile 0) before the ring starts: no load the
   // compiler tracks may be pending inside the loop.
 #pragma unroll
@@ -427,16 +444,16 @@ __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_pipe_kernel(const void*
   fwd_rescale<NB>(fwd_rowmax(sa, c), acc, mref, l);
 
   for (int t = 0; t < nt; t += 4) {
-    fwd_pipe_step<T, D, MASK, 0>(lds, t, nt, ntw, tb, dma, rk, rv, qf, acc, sa, sb, mref, l, wq0, qrow, N, win, c, w,
+    fwd_pipe_step<T, D, MASK, 0>(lds, t, nt, ntw, tb, dma, rk, rv, qf, koff, voff, acc, sa, sb, mref, l, wq0, qrow, N, win, c, w,
                                   lane);
     if (t + 1 < nt)
-      fwd_pipe_step<T, D, MASK, 1>(lds, t + 1, nt, ntw, tb, dma, rk, rv, qf, acc, sb, sa, mref, l, wq0, qrow, N, win,
+      fwd_pipe_step<T, D, MASK, 1>(lds, t + 1, nt, ntw, tb, dma, rk, rv, qf, koff, voff, acc, sb, sa, mref, l, wq0, qrow, N, win,
                                     c, w, lane);
     if (t + 2 < nt)
-      fwd_pipe_step<T, D, MASK, 2>(lds, t + 2, nt, ntw, tb, dma, rk, rv, qf, acc, sa, sb, mref, l, wq0, qrow, N, win,
+      fwd_pipe_step<T, D, MASK, 2>(lds, t + 2, nt, ntw, tb, dma, rk, rv, qf, koff, voff, acc, sa, sb, mref, l, wq0, qrow, N, win,
                                     c, w, lane);
     if (t + 3 < nt)
-      fwd_pipe_step<T, D, MASK, 3>(lds, t + 3, nt, ntw, tb, dma, rk, rv, qf, acc, sb, sa, mref, l, wq0, qrow, N, win,
+      fwd_pipe_step<T, D, MASK, 3>(lds, t + 3, nt, ntw, tb, dma, rk, rv, qf, koff, voff, acc, sb, sa, mref, l, wq0, qrow, N, win,
                                     c, w, lane);
   }
 
