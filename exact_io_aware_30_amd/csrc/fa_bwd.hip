@@ -458,6 +458,120 @@ __device__ __forceinline__ void dq_tile(const lds_char* kt, const lds_char* vt, 
   prio_mfma_end();
 }
 
+// The same tile as three MFMA runs with the tile's VALU work written
+// between them in issue order (each MFMA followed by its share, fenced so
+// that the compiler keeps the order): S^T; dP^T with P = 2^(S c - L2) of two
+// elements per MFMA; dQ^T with dS = P (dP - D) formed one packed operand
+// ahead of the MFMAs that take it.  The MFMA pipe then runs while the wave's
+// own softmax work issues.
+// Used at d = 32 and 64 (10% and 5% faster dQ on the ragged fp16 d = 32 and
+// bf16 d = 64 workloads); at d = 128 it needs every register and gains
+// nothing.  FA_DQ_PIPE=0/1 forces one form for every head dimension.
+#ifdef FA_DQ_PIPE
+template <int D>
+constexpr bool kDqPipe = FA_DQ_PIPE != 0;
+#else
+template <int D>
+constexpr bool kDqPipe = D != 128;
+#endif
+// LDS operand reads run this many MFMAs ahead in the score runs and the dQ run.
+#ifdef FA_DQ_PIPE_PRE1
+template <int D>
+constexpr int kDqPipePre1 = FA_DQ_PIPE_PRE1;
+#else
+template <int D>
+constexpr int kDqPipePre1 = D == 64 ? 1 : 2;
+#endif
+#ifndef FA_DQ_PIPE_PRE3
+#define FA_DQ_PIPE_PRE3 1
+#endif
+template <class T, int D, bool MASK>
+__device__ __forceinline__ void dq_tile_pipe(const lds_char* kt, const lds_char* vt, const u32x4* qf,
+                                             const u32x4* dof, f32x16* dqa, float l2, float dd, bool edge, int j0,
+                                             int qrow, int N, Win win, float c, int lane) {
+  constexpr int NKK = D / 16, NB = D / 32, NM = 2 * NKK, NM3 = 4 * NB;
+  constexpr int E = 32 / NM, F = 32 / NM3;  // elements per MFMA in runs 2 and 3
+  constexpr int PRE = kDqPipePre1<D>, PRE3 = FA_DQ_PIPE_PRE3;
+  const int h = lane >> 5;
+  f32x16 s[2], dp[2];
+  u32x4 dsf[4];
+
+  // Run 1: S^T = K Q^T (MFMA i: kk = i / 2, a = i % 2).
+  {
+    u32x4 ko[NM];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) s[a] = dp[a] = (f32x16){};
+#pragma unroll
+    for (int i = 0; i < PRE; ++i) ko[i] = lds_rows_operand<D>(kt, 32 * (i % 2), i / 2, lane);
+    prio_mfma_begin();
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      if (i + PRE < NM) ko[i + PRE] = lds_rows_operand<D>(kt, 32 * ((i + PRE) % 2), (i + PRE) / 2, lane);
+      s[i % 2] = Elem<T>::mma(ko[i], qf[i / 2], s[i % 2]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    prio_mfma_end();
+  }
+  if (edge) {
+    const int klo = MASK ? win.lo(qrow) : kUnbounded, khi = MASK ? win.hi(qrow, N) : N - 1;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = j0 + 32 * a + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (key > khi || (MASK && win.left >= 0 && key < klo)) s[a][r] = -INFINITY;
+      }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // Run 2: dP^T = V dO^T, and P = 2^(S c - L2) of E elements after each MFMA.
+  {
+    u32x4 vo[NM];
+#pragma unroll
+    for (int i = 0; i < PRE; ++i) vo[i] = lds_rows_operand<D>(vt, 32 * (i % 2), i / 2, lane);
+    prio_mfma_begin();
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      if (i + PRE < NM) vo[i + PRE] = lds_rows_operand<D>(vt, 32 * ((i + PRE) % 2), (i + PRE) / 2, lane);
+      dp[i % 2] = Elem<T>::mma(vo[i], dof[i / 2], dp[i % 2]);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int x = i * E + e;
+        s[x / 16][x % 16] = exp2_fast(__builtin_fmaf(s[x / 16][x % 16], c, -l2));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    prio_mfma_end();
+  }
+
+  // Run 3: dQ^T += K^T dS^T (MFMA i: j = i / NB, b = i % NB).  dS operand j
+  // (elements 8j .. 8j + 7) is formed before the first MFMA, operand j + 1
+  // under the MFMAs of operand j, F elements after each.
+  {
+    auto ds_elem = [&](int x) {
+      dp[x / 16][x % 16] = s[x / 16][x % 16] * (dp[x / 16][x % 16] - dd);
+      if (x % 8 == 7) dsf[x / 8] = pack8<T>(dp[x / 16], (x % 16) / 8);
+    };
+#pragma unroll
+    for (int x = 0; x < 8; ++x) ds_elem(x);
+    u32x4 to[NM3];
+#pragma unroll
+    for (int i = 0; i < PRE3; ++i) to[i] = lds_cols_operand<D>(kt, i / NB, 32 * (i % NB), lane);
+    prio_mfma_begin();
+#pragma unroll
+    for (int i = 0; i < NM3; ++i) {
+      if (i + PRE3 < NM3) to[i + PRE3] = lds_cols_operand<D>(kt, (i + PRE3) / NB, 32 * ((i + PRE3) % NB), lane);
+      dqa[i % NB] = Elem<T>::mma(to[i], dsf[i / NB], dqa[i % NB]);
+      if (i / NB + 1 < 4) {
+#pragma unroll
+        for (int e = 0; e < F; ++e) ds_elem(8 * (i / NB + 1) + F * (i % NB) + e);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    prio_mfma_end();
+  }
+}
+
 // DMA of key tile t (K then V) into ring buffer IDX.
 template <int D, int IDX>
 __device__ __forceinline__ void dq_issue(lds_char* lds, int t, const DmaTile<kBwdTile, D, kBwdWaves>& dma, Rsrc rk,
@@ -482,7 +596,10 @@ __device__ __forceinline__ void dq_step(lds_char* lds, int t, int nt, int tb, co
   if (MASK && (j0 + BN <= win.key_lo(wq0) || j0 >= win.key_hi(wq0 + 31, N))) return;
   const lds_char* cur = lds + IDX * 2 * TILE;
   const bool edge = (j0 + BN > N) || (MASK && !win.all_visible(wq0, wq0 + 31, j0, j0 + BN - 1));
-  dq_tile<T, D, MASK>(cur, cur + TILE, qf, dof, dqa, l2, dd, edge, j0, qrow, N, win, c, lane);
+  if constexpr (kDqPipe<D>)
+    dq_tile_pipe<T, D, MASK>(cur, cur + TILE, qf, dof, dqa, l2, dd, edge, j0, qrow, N, win, c, lane);
+  else
+    dq_tile<T, D, MASK>(cur, cur + TILE, qf, dof, dqa, l2, dd, edge, j0, qrow, N, win, c, lane);
 }
 
 // ---------------------------------------------------------------------------
