@@ -171,6 +171,15 @@ __device__ __forceinline__ void fwd_step(lds_char* lds, int t, int nt, int tb, c
 // read while t+2 lands and t+3 is being issued into the buffer of t-1.
 // ---------------------------------------------------------------------------
 constexpr int kPipeStages = 4;
+// LDS operand reads run this many MFMAs ahead of their use in the QK^T and
+// PV runs.
+#ifndef FA_FWD_PIPE_PRE1
+#define FA_FWD_PIPE_PRE1 3
+#endif
+#ifndef FA_FWD_PIPE_PRE2
+#define FA_FWD_PIPE_PRE2 2
+#endif
+constexpr int kPipePre1 = FA_FWD_PIPE_PRE1, kPipePre2 = FA_FWD_PIPE_PRE2;
 // Used at d = 128, where a tile's VALU work fits under its MFMAs; at d = 64
 // and 32 (half and a quarter of the MFMAs per score) the plain kernel is
 // faster.  FA_FWD_PIPE=0/1 forces one form for every head dimension.
@@ -298,7 +307,7 @@ __device__ __forceinline__ void fwd_pipe_step(lds_char* lds, int t, int nt, int 
   // MFMA.  K of tile t+1 is read even past the wave's (or the sequence's)
   // last tile: the buffer is in bounds and such scores are masked below.
   {
-    constexpr int NM = NA * NKK, E = 16 * NA / NM, PRE = NM < 3 ? NM : 3;
+    constexpr int NM = NA * NKK, E = 16 * NA / NM, PRE = NM < kPipePre1 ? NM : kPipePre1;
     u32x4 kop[NM];
     float rs = 0.f;
     const float mr = mref == -INFINITY ? 0.f : mref;  // all of a row masked so far: p = 0
@@ -336,7 +345,7 @@ __device__ __forceinline__ void fwd_pipe_step(lds_char* lds, int t, int nt, int 
 
     // Run 2: O^T += V(t)^T P(t)^T, MFMA i = (j = i / NB, b = i % NB), and the
     // row maximum of S(t+1), F elements per MFMA.
-    constexpr int NM2 = 2 * NA * NB, F = 16 * NA / NM2, PRE2 = NM2 < 2 ? NM2 : 2;
+    constexpr int NM2 = 2 * NA * NB, F = 16 * NA / NM2, PRE2 = NM2 < kPipePre2 ? NM2 : kPipePre2;
     u32x4 vop[NM2];
 #pragma unroll
     for (int i = 0; i < PRE2; ++i)
