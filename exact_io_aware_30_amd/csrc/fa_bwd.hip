@@ -46,7 +46,22 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const void* __restrict_
   }
 }
 
-constexpr int kBwdWaves = 4, kBwdTile = 64, kBwdStages = FA_BWD_STAGES;
+constexpr int kBwdWaves = 4, kBwdStages = FA_BWD_STAGES;
+// dQ key tile rows and ring depth.
+#ifdef FA_DQ_TILE
+template <int D>
+constexpr int kDqTile = FA_DQ_TILE;
+#else
+template <int D>
+constexpr int kDqTile = 64;
+#endif
+#ifdef FA_DQ_STAGES
+template <int D>
+constexpr int kDqStages = FA_DQ_STAGES;
+#else
+template <int D>
+constexpr int kDqStages = kBwdStages;
+#endif
 // dK/dV kernel configuration per head dimension (chosen by measurement):
 // query tile rows (32 or 64), workgroups per CU the registers are limited
 // for, ring depth, MFMAs' worth of LDS operand reads kept in flight in the
@@ -410,29 +425,29 @@ __global__ __launch_bounds__(64 * kBwdWaves, Dkdv<D>::kOcc) void dkdv_kernel(
 // edge of the window of some of the wave's queries, or the end of N).  One
 // code path for every tile, so the accumulator registers need no copies at
 // merges.
-template <class T, int D, bool MASK>
+template <class T, int D, bool MASK, int NA>
 __device__ __forceinline__ void dq_tile(const lds_char* kt, const lds_char* vt, const u32x4* qf, const u32x4* dof,
                                         f32x16* dqa, float l2, float dd, bool edge, int j0, int qrow, int N, Win win,
                                         float c, int lane) {
   constexpr int NKK = D / 16, NB = D / 32;
   const int h = lane >> 5;
-  f32x16 s[2], dp[2];
+  f32x16 s[NA], dp[NA];
 #pragma unroll
-  for (int a = 0; a < 2; ++a) s[a] = dp[a] = (f32x16){};
+  for (int a = 0; a < NA; ++a) s[a] = dp[a] = (f32x16){};
   prio_mfma_begin();
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
+    for (int a = 0; a < NA; ++a) {
       s[a] = Elem<T>::mma(lds_rows_operand<D>(kt, 32 * a, kk, lane), qf[kk], s[a]);
       dp[a] = Elem<T>::mma(lds_rows_operand<D>(vt, 32 * a, kk, lane), dof[kk], dp[a]);
     }
-  sched_mfma_lds<4 * NKK, 1, 6>();
+  sched_mfma_lds<2 * NA * NKK, 1, 6>();
   prio_mfma_end();
   if (edge) {
     const int klo = MASK ? win.lo(qrow) : kUnbounded, khi = MASK ? win.hi(qrow, N) : N - 1;
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < NA; ++a)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = j0 + 32 * a + 8 * (r >> 2) + 4 * h + (r & 3);
@@ -440,21 +455,21 @@ __device__ __forceinline__ void dq_tile(const lds_char* kt, const lds_char* vt, 
       }
   }
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < NA; ++a)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float p = exp2_fast(__builtin_fmaf(s[a][r], c, -l2));
       dp[a][r] = p * (dp[a][r] - dd);
     }
-  u32x4 dsf[4];
+  u32x4 dsf[2 * NA];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) dsf[j] = pack8<T>(dp[j >> 1], j & 1);
+  for (int j = 0; j < 2 * NA; ++j) dsf[j] = pack8<T>(dp[j >> 1], j & 1);
   prio_mfma_begin();
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < 2 * NA; ++j)
 #pragma unroll
     for (int b = 0; b < NB; ++b) dqa[b] = Elem<T>::mma(lds_cols_operand<D>(kt, j, 32 * b, lane), dsf[j], dqa[b]);
-  sched_mfma_lds<4 * NB, 2, 3>();
+  sched_mfma_lds<2 * NA * NB, 2, 3>();
   prio_mfma_end();
 }
 
@@ -485,29 +500,29 @@ constexpr int kDqPipePre1 = D == 64 ? 1 : 2;
 #ifndef FA_DQ_PIPE_PRE3
 #define FA_DQ_PIPE_PRE3 1
 #endif
-template <class T, int D, bool MASK>
+template <class T, int D, bool MASK, int NA>
 __device__ __forceinline__ void dq_tile_pipe(const lds_char* kt, const lds_char* vt, const u32x4* qf,
                                              const u32x4* dof, f32x16* dqa, float l2, float dd, bool edge, int j0,
                                              int qrow, int N, Win win, float c, int lane) {
-  constexpr int NKK = D / 16, NB = D / 32, NM = 2 * NKK, NM3 = 4 * NB;
-  constexpr int E = 32 / NM, F = 32 / NM3;  // elements per MFMA in runs 2 and 3
+  constexpr int NKK = D / 16, NB = D / 32, NM = NA * NKK, NM3 = 2 * NA * NB;
+  constexpr int E = 16 * NA / NM, F = 16 * NA / NM3;  // elements per MFMA in runs 2 and 3
   constexpr int PRE = kDqPipePre1<D>, PRE3 = FA_DQ_PIPE_PRE3;
   const int h = lane >> 5;
-  f32x16 s[2], dp[2];
-  u32x4 dsf[4];
+  f32x16 s[NA], dp[NA];
+  u32x4 dsf[2 * NA];
 
-  // Run 1: S^T = K Q^T (MFMA i: kk = i / 2, a = i % 2).
+  // Run 1: S^T = K Q^T (MFMA i: kk = i / NA, a = i % NA).
   {
     u32x4 ko[NM];
 #pragma unroll
-    for (int a = 0; a < 2; ++a) s[a] = dp[a] = (f32x16){};
+    for (int a = 0; a < NA; ++a) s[a] = dp[a] = (f32x16){};
 #pragma unroll
-    for (int i = 0; i < PRE; ++i) ko[i] = lds_rows_operand<D>(kt, 32 * (i % 2), i / 2, lane);
+    for (int i = 0; i < PRE; ++i) ko[i] = lds_rows_operand<D>(kt, 32 * (i % NA), i / NA, lane);
     prio_mfma_begin();
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
-      if (i + PRE < NM) ko[i + PRE] = lds_rows_operand<D>(kt, 32 * ((i + PRE) % 2), (i + PRE) / 2, lane);
-      s[i % 2] = Elem<T>::mma(ko[i], qf[i / 2], s[i % 2]);
+      if (i + PRE < NM) ko[i + PRE] = lds_rows_operand<D>(kt, 32 * ((i + PRE) % NA), (i + PRE) / NA, lane);
+      s[i % NA] = Elem<T>::mma(ko[i], qf[i / NA], s[i % NA]);
       __builtin_amdgcn_sched_barrier(0);
     }
     prio_mfma_end();
@@ -515,7 +530,7 @@ __device__ __forceinline__ void dq_tile_pipe(const lds_char* kt, const lds_char*
   if (edge) {
     const int klo = MASK ? win.lo(qrow) : kUnbounded, khi = MASK ? win.hi(qrow, N) : N - 1;
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < NA; ++a)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = j0 + 32 * a + 8 * (r >> 2) + 4 * h + (r & 3);
@@ -528,12 +543,12 @@ __device__ __forceinline__ void dq_tile_pipe(const lds_char* kt, const lds_char*
   {
     u32x4 vo[NM];
 #pragma unroll
-    for (int i = 0; i < PRE; ++i) vo[i] = lds_rows_operand<D>(vt, 32 * (i % 2), i / 2, lane);
+    for (int i = 0; i < PRE; ++i) vo[i] = lds_rows_operand<D>(vt, 32 * (i % NA), i / NA, lane);
     prio_mfma_begin();
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
-      if (i + PRE < NM) vo[i + PRE] = lds_rows_operand<D>(vt, 32 * ((i + PRE) % 2), (i + PRE) / 2, lane);
-      dp[i % 2] = Elem<T>::mma(vo[i], dof[i / 2], dp[i % 2]);
+      if (i + PRE < NM) vo[i + PRE] = lds_rows_operand<D>(vt, 32 * ((i + PRE) % NA), (i + PRE) / NA, lane);
+      dp[i % NA] = Elem<T>::mma(vo[i], dof[i / NA], dp[i % NA]);
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const int x = i * E + e;
@@ -562,7 +577,7 @@ __device__ __forceinline__ void dq_tile_pipe(const lds_char* kt, const lds_char*
     for (int i = 0; i < NM3; ++i) {
       if (i + PRE3 < NM3) to[i + PRE3] = lds_cols_operand<D>(kt, (i + PRE3) / NB, 32 * ((i + PRE3) % NB), lane);
       dqa[i % NB] = Elem<T>::mma(to[i], dsf[i / NB], dqa[i % NB]);
-      if (i / NB + 1 < 4) {
+      if (i / NB + 1 < 2 * NA) {
 #pragma unroll
         for (int e = 0; e < F; ++e) ds_elem(8 * (i / NB + 1) + F * (i % NB) + e);
       }
@@ -574,21 +589,21 @@ __device__ __forceinline__ void dq_tile_pipe(const lds_char* kt, const lds_char*
 
 // DMA of key tile t (K then V) into ring buffer IDX.
 template <int D, int IDX>
-__device__ __forceinline__ void dq_issue(lds_char* lds, int t, const DmaTile<kBwdTile, D, kBwdWaves>& dma, Rsrc rk,
+__device__ __forceinline__ void dq_issue(lds_char* lds, int t, const DmaTile<kDqTile<D>, D, kBwdWaves>& dma, Rsrc rk,
                                          Rsrc rv, int w) {
-  constexpr int TILE = kBwdTile * D * 2;
+  constexpr int TILE = kDqTile<D> * D * 2;
   lds_char* b = lds + IDX * 2 * TILE;
-  dma.issue(rk, b, t * kBwdTile, w);
-  dma.issue(rv, b + TILE, t * kBwdTile, w);
+  dma.issue(rk, b, t * kDqTile<D>, w);
+  dma.issue(rv, b + TILE, t * kDqTile<D>, w);
 }
 
 // One ring step on key tile t, held in ring buffer IDX = t % S.
 template <class T, int D, bool MASK, int IDX>
-__device__ __forceinline__ void dq_step(lds_char* lds, int t, int nt, int tb, const DmaTile<kBwdTile, D, kBwdWaves>& dma,
+__device__ __forceinline__ void dq_step(lds_char* lds, int t, int nt, int tb, const DmaTile<kDqTile<D>, D, kBwdWaves>& dma,
                                         Rsrc rk, Rsrc rv, const u32x4* qf, const u32x4* dof, f32x16* dqa, float l2,
                                         float dd, int wq0, int qrow, int N, Win win, float c, int w, int lane) {
-  constexpr int S = kBwdStages, BN = kBwdTile, TILE = BN * D * 2;
-  ring_wait<S, 2 * DmaTile<kBwdTile, D, kBwdWaves>::PER>(t, nt);
+  constexpr int S = kDqStages<D>, BN = kDqTile<D>, TILE = BN * D * 2;
+  ring_wait<S, 2 * DmaTile<kDqTile<D>, D, kBwdWaves>::PER>(t, nt);
   if (t + S - 1 < nt) dq_issue<D, (IDX + S - 1) % S>(lds, tb + t + S - 1, dma, rk, rv, w);
   __builtin_amdgcn_sched_barrier(0);
   const int j0 = (tb + t) * BN;
@@ -597,9 +612,9 @@ __device__ __forceinline__ void dq_step(lds_char* lds, int t, int nt, int tb, co
   const lds_char* cur = lds + IDX * 2 * TILE;
   const bool edge = (j0 + BN > N) || (MASK && !win.all_visible(wq0, wq0 + 31, j0, j0 + BN - 1));
   if constexpr (kDqPipe<D>)
-    dq_tile_pipe<T, D, MASK>(cur, cur + TILE, qf, dof, dqa, l2, dd, edge, j0, qrow, N, win, c, lane);
+    dq_tile_pipe<T, D, MASK, BN / 32>(cur, cur + TILE, qf, dof, dqa, l2, dd, edge, j0, qrow, N, win, c, lane);
   else
-    dq_tile<T, D, MASK>(cur, cur + TILE, qf, dof, dqa, l2, dd, edge, j0, qrow, N, win, c, lane);
+    dq_tile<T, D, MASK, BN / 32>(cur, cur + TILE, qf, dof, dqa, l2, dd, edge, j0, qrow, N, win, c, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -622,8 +637,8 @@ __global__ __launch_bounds__(64 * kBwdWaves, 2) void dq_kernel(const void* __res
   // compile-time constant so that every window test folds; 2: any window.
   constexpr bool MASK = MODE != 0;
   const Win win = MODE == 1 ? Win{-1, 0} : win_in;
-  constexpr int NW = kBwdWaves, BM = 32 * NW, BN = kBwdTile, NKK = D / 16, NB = D / 32;
-  constexpr int S = kBwdStages, TILE = BN * D * 2;
+  constexpr int NW = kBwdWaves, BM = 32 * NW, BN = kDqTile<D>, NKK = D / 16, NB = D / 32;
+  constexpr int S = kDqStages<D>, TILE = BN * D * 2;
   __shared__ __attribute__((aligned(16))) char smem[S * 2 * TILE];
   lds_char* const lds = (lds_char*)smem;
 
