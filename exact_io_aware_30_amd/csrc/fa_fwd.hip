@@ -27,22 +27,34 @@
 #include "fa_launch.h"
 
 // Tile configuration (compile-time; defaults chosen by measurement).
-#ifndef FA_FWD_WAVES
-#define FA_FWD_WAVES 8
-#endif
+// FA_FWD_WAVES / FA_FWD_KEYBLOCKS, when defined, apply to every head
+// dimension.
 #ifndef FA_FWD_STAGES
 #define FA_FWD_STAGES 3
-#endif
-#ifndef FA_FWD_KEYBLOCKS
-#define FA_FWD_KEYBLOCKS 2
 #endif
 
 namespace fa {
 
-constexpr int kFwdWaves = FA_FWD_WAVES;    // waves per workgroup (32 query rows each)
-constexpr int kFwdStages = FA_FWD_STAGES;  // LDS ring depth
-constexpr int kFwdNA = FA_FWD_KEYBLOCKS;   // key tile = 32 * kFwdNA rows
-constexpr int kFwdBN = 32 * kFwdNA;
+// Per head dimension: waves per workgroup (32 query rows each), key tile of
+// 32 * kNA rows, LDS ring depth of the plain kernel.  At d = 32 a workgroup
+// of 4 waves with 32-key tiles (two workgroups per CU) is 12% faster than 8
+// waves with 64-key tiles; at d = 64 and 128 it is 4-9% slower on the large
+// workloads.
+template <int D>
+struct FwdCfg {
+#ifdef FA_FWD_WAVES
+  static constexpr int kWaves = FA_FWD_WAVES;
+#else
+  static constexpr int kWaves = D == 32 ? 4 : 8;
+#endif
+#ifdef FA_FWD_KEYBLOCKS
+  static constexpr int kNA = FA_FWD_KEYBLOCKS;
+#else
+  static constexpr int kNA = D == 32 ? 1 : 2;
+#endif
+  static constexpr int kBN = 32 * kNA;
+  static constexpr int kStages = FA_FWD_STAGES;
+};
 
 // Rescale threshold in base-2 units: the reference maximum used for the
 // exponentials is moved only when a row's maximum exceeds it by more than
@@ -71,7 +83,7 @@ template <class T, int D, bool MASK>
 __device__ __forceinline__ void fwd_tile(const lds_char* kt, const lds_char* vt, const u32x4* qf, f32x16* acc,
                                          float& mref, float& l, bool edge, int j0, int qrow, int N, Win win,
                                          float c, int lane) {
-  constexpr int NKK = D / 16, NB = D / 32, NA = kFwdNA;
+  constexpr int NKK = D / 16, NB = D / 32, NA = FwdCfg<D>::kNA;
   const int h = lane >> 5;
   f32x16 s[NA];
 #pragma unroll
@@ -128,18 +140,18 @@ __device__ __forceinline__ void fwd_tile(const lds_char* kt, const lds_char* vt,
   for (int j = 0; j < 2 * NA; ++j)
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[b] = Elem<T>::mma(lds_cols_operand<D>(vt, j, 32 * b, lane), pf[j], acc[b]);
-  sched_mfma_lds<2 * NA * NB, 2, 3>();
+  sched_mfma_lds<2 * NA * NB, 2, (2 * NA * NB < 3 ? 2 * NA * NB : 3)>();
   fwd_prio_end();
 }
 
 // DMA of key tile t (K then V) into ring buffer IDX.
 template <int D, int IDX>
-__device__ __forceinline__ void fwd_issue(lds_char* lds, int t, const DmaTile<kFwdBN, D, kFwdWaves>& dma, Rsrc rk,
+__device__ __forceinline__ void fwd_issue(lds_char* lds, int t, const DmaTile<FwdCfg<D>::kBN, D, FwdCfg<D>::kWaves>& dma, Rsrc rk,
                                           Rsrc rv, int w) {
-  constexpr int TILE = kFwdBN * D * 2;
+  constexpr int TILE = FwdCfg<D>::kBN * D * 2;
   lds_char* b = lds + IDX * 2 * TILE;
-  dma.issue(rk, b, t * kFwdBN, w);
-  dma.issue(rv, b + TILE, t * kFwdBN, w);
+  dma.issue(rk, b, t * FwdCfg<D>::kBN, w);
+  dma.issue(rv, b + TILE, t * FwdCfg<D>::kBN, w);
 }
 
 // Ring step on tile t, which sits in buffer IDX = t % S (a compile-time
@@ -147,11 +159,11 @@ __device__ __forceinline__ void fwd_issue(lds_char* lds, int t, const DmaTile<kF
 // wait and barrier, DMA of tile t + S - 1 into the buffer tile t - 1 used,
 // then the math.
 template <class T, int D, bool MASK, int IDX>
-__device__ __forceinline__ void fwd_step(lds_char* lds, int t, int nt, int tb, const DmaTile<kFwdBN, D, kFwdWaves>& dma,
+__device__ __forceinline__ void fwd_step(lds_char* lds, int t, int nt, int tb, const DmaTile<FwdCfg<D>::kBN, D, FwdCfg<D>::kWaves>& dma,
                                          Rsrc rk, Rsrc rv, const u32x4* qf, f32x16* acc, float& mref, float& l,
                                          int wq0, int qrow, int N, Win win, float c, int w, int lane) {
-  constexpr int S = kFwdStages, BN = kFwdBN, TILE = BN * D * 2;
-  ring_wait<S, 2 * DmaTile<kFwdBN, D, kFwdWaves>::PER>(t, nt);
+  constexpr int S = FwdCfg<D>::kStages, BN = FwdCfg<D>::kBN, TILE = BN * D * 2;
+  ring_wait<S, 2 * DmaTile<FwdCfg<D>::kBN, D, FwdCfg<D>::kWaves>::PER>(t, nt);
   if (t + S - 1 < nt) fwd_issue<D, (IDX + S - 1) % S>(lds, tb + t + S - 1, dma, rk, rv, w);
   __builtin_amdgcn_sched_barrier(0);
   const int j0 = (tb + t) * BN;
@@ -194,7 +206,7 @@ constexpr bool kFwdPipelined = D == 128;
 // S^T of one key tile into s (lane = query, registers = keys).
 template <class T, int D>
 __device__ __forceinline__ void fwd_scores(const lds_char* kt, const u32x4* qf, f32x16* s, int lane) {
-  constexpr int NKK = D / 16, NA = kFwdNA;
+  constexpr int NKK = D / 16, NA = FwdCfg<D>::kNA;
 #pragma unroll
   for (int a = 0; a < NA; ++a) s[a] = (f32x16){};
 #pragma unroll
@@ -208,13 +220,13 @@ __device__ __forceinline__ void fwd_scores(const lds_char* kt, const u32x4* qf, 
 // [lo, hi] (hi = N - 1 without a window), compared as offsets against
 // lo - j0 - 4h and hi - j0 - 4h.  The bounds pass through an empty asm
 // statement so that the compares stay inside the caller's branch.
-template <bool MASK>
+template <bool MASK, int NA>
 __device__ __forceinline__ void fwd_mask(f32x16* s, int j0, int qrow, int N, Win win, int lane) {
   int rhi = (MASK ? win.hi(qrow, N) : N - 1) - j0 - 4 * (lane >> 5);
   int rlo = (MASK ? win.lo(qrow) : kUnbounded) - j0 - 4 * (lane >> 5);
   asm volatile("" : "+v"(rhi), "+v"(rlo));
 #pragma unroll
-  for (int a = 0; a < kFwdNA; ++a)
+  for (int a = 0; a < NA; ++a)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int off = 32 * a + 8 * (r >> 2) + (r & 3);
@@ -223,10 +235,11 @@ __device__ __forceinline__ void fwd_mask(f32x16* s, int j0, int qrow, int N, Win
 }
 
 // Row maximum of s in base-2 units (both lane halves).
+template <int NA>
 __device__ __forceinline__ float fwd_rowmax(const f32x16* s, float c) {
   float mx = s[0][0];
 #pragma unroll
-  for (int a = 0; a < kFwdNA; ++a)
+  for (int a = 0; a < NA; ++a)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[a][r]);
   return max_with_partner(mx) * c;
@@ -252,11 +265,11 @@ __device__ __forceinline__ void fwd_rescale(float mxc, f32x16* acc, float& mref,
 // then the V tiles, so that within each half every buffer is an immediate
 // offset (under 64 KiB) from one base address.
 template <int D, int IDX>
-__device__ __forceinline__ void fwd_pipe_issue(lds_char* lds, int t, const DmaTile<kFwdBN, D, kFwdWaves>& dma,
+__device__ __forceinline__ void fwd_pipe_issue(lds_char* lds, int t, const DmaTile<FwdCfg<D>::kBN, D, FwdCfg<D>::kWaves>& dma,
                                                Rsrc rk, Rsrc rv, int w) {
-  constexpr int TILE = kFwdBN * D * 2;
-  dma.issue(rk, lds + IDX * TILE, t * kFwdBN, w);
-  dma.issue(rv, lds + (kPipeStages + IDX) * TILE, t * kFwdBN, w);
+  constexpr int TILE = FwdCfg<D>::kBN * D * 2;
+  dma.issue(rk, lds + IDX * TILE, t * FwdCfg<D>::kBN, w);
+  dma.issue(rv, lds + (kPipeStages + IDX) * TILE, t * FwdCfg<D>::kBN, w);
 }
 
 // Wait until tile t+1 has landed (tile t already has), allowing the DMA of
@@ -278,12 +291,12 @@ __device__ __forceinline__ void pipe_wait(int t, int nt) {
 // order (a wave issues VALU work while its own MFMAs execute).
 template <class T, int D, bool MASK, int IDX>
 __device__ __forceinline__ void fwd_pipe_step(lds_char* lds, int t, int nt, int ntw, int tb,
-                                              const DmaTile<kFwdBN, D, kFwdWaves>& dma, Rsrc rk, Rsrc rv,
+                                              const DmaTile<FwdCfg<D>::kBN, D, FwdCfg<D>::kWaves>& dma, Rsrc rk, Rsrc rv,
                                               const u32x4* qf, const uint32_t* koff, const uint32_t* voff,
                                               f32x16* acc, f32x16* s_cur, f32x16* s_nxt, float& mref, float& l,
                                               int wq0, int qrow, int N, Win win, float c, int w, int lane) {
-  constexpr int S = kPipeStages, BN = kFwdBN, TILE = BN * D * 2, NB = D / 32, NKK = D / 16, NA = kFwdNA;
-  pipe_wait<2 * DmaTile<kFwdBN, D, kFwdWaves>::PER>(t, nt);
+  constexpr int S = kPipeStages, BN = FwdCfg<D>::kBN, TILE = BN * D * 2, NB = D / 32, NKK = D / 16, NA = FwdCfg<D>::kNA;
+  pipe_wait<2 * DmaTile<FwdCfg<D>::kBN, D, FwdCfg<D>::kWaves>::PER>(t, nt);
   if (t + S - 1 < nt) fwd_pipe_issue<D, (IDX + S - 1) % S>(lds, tb + t + S - 1, dma, rk, rv, w);
   __builtin_amdgcn_sched_barrier(0);
   if (t >= ntw) return;  // no key from tile t on is visible to any query of the wave
@@ -340,7 +353,7 @@ __device__ __forceinline__ void fwd_pipe_step(lds_char* lds, int t, int nt, int 
 
     const int j1 = (tb + t + 1) * BN;
     if ((j1 + BN > N) || (MASK && !win.all_visible(wq0, wq0 + 31, j1, j1 + BN - 1)))
-      fwd_mask<MASK>(s_nxt, j1, qrow, N, win, lane);
+      fwd_mask<MASK, NA>(s_nxt, j1, qrow, N, win, lane);
     __builtin_amdgcn_sched_barrier(0);
 
     // Run 2: O^T += V(t)^T P(t)^T, MFMA i = (j = i / NB, b = i % NB), and the
@@ -372,7 +385,7 @@ __device__ __forceinline__ void fwd_pipe_step(lds_char* lds, int t, int nt, int 
 }
 
 template <class T, int D, int MODE>
-__global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_pipe_kernel(const void* __restrict__ qp,
+__global__ __launch_bounds__(64 * FwdCfg<D>::kWaves, 2) void fwd_pipe_kernel(const void* __restrict__ qp,
                                                                      const void* __restrict__ kp,
                                                                      const void* __restrict__ vp,
                                                                      void* __restrict__ op, float* __restrict__ lsep,
@@ -381,7 +394,7 @@ __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_pipe_kernel(const void*
   // compile-time constant so that every window test folds; 2: any window.
   constexpr bool MASK = MODE != 0;
   const Win win = MODE == 1 ? Win{-1, 0} : win_in;
-  constexpr int NW = kFwdWaves, S = kPipeStages, BM = 32 * NW, BN = kFwdBN, NKK = D / 16, NB = D / 32;
+  constexpr int NW = FwdCfg<D>::kWaves, S = kPipeStages, BM = 32 * NW, BN = FwdCfg<D>::kBN, NKK = D / 16, NB = D / 32;
   constexpr int TILE = BN * D * 2, BUF = 2 * TILE;
   using Dma = DmaTile<BN, D, NW>;
   constexpr int PT = 2 * Dma::PER;
@@ -440,7 +453,7 @@ __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_pipe_kernel(const void*
   // Tile 0 landed (waited above); tiles 1 and 2 may be in flight.
   dma_wait_barrier<63>();
 
-  f32x16 acc[NB], sa[kFwdNA], sb[kFwdNA];
+  f32x16 acc[NB], sa[FwdCfg<D>::kNA], sb[FwdCfg<D>::kNA];
 #pragma unroll
   for (int b = 0; b < NB; ++b) acc[b] = (f32x16){};
   float mref = -INFINITY, l = 0.f;  // reference max (base 2) and this lane's part of the row sum
@@ -448,9 +461,9 @@ __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_pipe_kernel(const void*
   {
     const int j0 = tb * BN;
     if (j0 + BN > N || (MASK && !win.all_visible(wq0, wq0 + 31, j0, j0 + BN - 1)))
-      fwd_mask<MASK>(sa, j0, qrow, N, win, lane);
+      fwd_mask<MASK, FwdCfg<D>::kNA>(sa, j0, qrow, N, win, lane);
   }
-  fwd_rescale<NB>(fwd_rowmax(sa, c), acc, mref, l);
+  fwd_rescale<NB>(fwd_rowmax<FwdCfg<D>::kNA>(sa, c), acc, mref, l);
 
   for (int t = 0; t < nt; t += 4) {
     fwd_pipe_step<T, D, MASK, 0>(lds, t, nt, ntw, tb, dma, rk, rv, qf, koff, voff, acc, sa, sb, mref, l, wq0, qrow, N, win, c, w,
@@ -472,7 +485,7 @@ __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_pipe_kernel(const void*
 }
 
 template <class T, int D, int MODE>
-__global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_kernel(const void* __restrict__ qp,
+__global__ __launch_bounds__(64 * FwdCfg<D>::kWaves, 2) void fwd_kernel(const void* __restrict__ qp,
                                                                 const void* __restrict__ kp,
                                                                 const void* __restrict__ vp, void* __restrict__ op,
                                                                 float* __restrict__ lsep, Geom geo, int BH, int nqb,
@@ -481,7 +494,7 @@ __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_kernel(const void* __re
   // compile-time constant so that every window test folds; 2: any window.
   constexpr bool MASK = MODE != 0;
   const Win win = MODE == 1 ? Win{-1, 0} : win_in;
-  constexpr int NW = kFwdWaves, S = kFwdStages, BM = 32 * NW, BN = kFwdBN, NKK = D / 16, NB = D / 32;
+  constexpr int NW = FwdCfg<D>::kWaves, S = FwdCfg<D>::kStages, BM = 32 * NW, BN = FwdCfg<D>::kBN, NKK = D / 16, NB = D / 32;
   constexpr int TILE = BN * D * 2, BUF = 2 * TILE;
   using Dma = DmaTile<BN, D, NW>;
   __shared__ __attribute__((aligned(16))) char smem[S * BUF];
@@ -549,15 +562,15 @@ __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_kernel(const void* __re
 template <class T, int D, int MODE>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   const int BH = a.B * a.H;
-  const int BM = 32 * kFwdWaves;
+  const int BM = 32 * FwdCfg<D>::kWaves;
   const int nqb = (a.N + BM - 1) / BM;  // a.N: the longest sequence when packed
   const Win win{a.wl, a.wr};
   const Geom geo{a.N, a.H, a.H / a.Hkv, a.cu, a.T};
   if constexpr (kFwdPipelined<D>)
-    hipLaunchKernelGGL((fwd_pipe_kernel<T, D, MODE>), dim3(nqb * BH), dim3(64 * kFwdWaves), 0, st, a.q, a.k, a.v,
+    hipLaunchKernelGGL((fwd_pipe_kernel<T, D, MODE>), dim3(nqb * BH), dim3(64 * FwdCfg<D>::kWaves), 0, st, a.q, a.k, a.v,
                        a.o, a.lse, geo, BH, nqb, win, a.scale * kLog2e);
   else
-    hipLaunchKernelGGL((fwd_kernel<T, D, MODE>), dim3(nqb * BH), dim3(64 * kFwdWaves), 0, st, a.q, a.k, a.v, a.o,
+    hipLaunchKernelGGL((fwd_kernel<T, D, MODE>), dim3(nqb * BH), dim3(64 * FwdCfg<D>::kWaves), 0, st, a.q, a.k, a.v, a.o,
                        a.lse, geo, BH, nqb, win, a.scale * kLog2e);
   return hipGetLastError();
 }
