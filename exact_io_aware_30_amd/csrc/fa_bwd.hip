@@ -70,9 +70,11 @@ constexpr int kDqStages = kBwdStages;
 template <int D>
 struct DkdvCfg {
   static constexpr int kTile = D == 32 ? 64 : 32;
-  static constexpr int kOcc = D == 128 ? 2 : D == 64 ? 3 : 1;
+  // Minimum workgroups per CU for the register allocator (d = 128: 1 lets
+  // it schedule more freely; the kernel still fits two per CU).
+  static constexpr int kOcc = D == 128 ? 1 : D == 64 ? 3 : 1;
   static constexpr bool kVLds = D == 128;
-  static constexpr int kStages = 2, kPre1 = D == 64 ? 4 : 6, kPre2 = 3;
+  static constexpr int kStages = 2, kPre1 = D == 32 ? 6 : 4, kPre2 = 3;
 };
 #ifdef FA_DKDV_TILE
 #define FA_DKDV_CFG_TILE FA_DKDV_TILE

@@ -27,19 +27,16 @@
 #include "fa_launch.h"
 
 // Tile configuration (compile-time; defaults chosen by measurement).
-// FA_FWD_WAVES / FA_FWD_KEYBLOCKS, when defined, apply to every head
-// dimension.
-#ifndef FA_FWD_STAGES
-#define FA_FWD_STAGES 3
-#endif
+// FA_FWD_WAVES / FA_FWD_KEYBLOCKS / FA_FWD_STAGES, when defined, apply to
+// every head dimension.
 
 namespace fa {
 
 // Per head dimension: waves per workgroup (32 query rows each), key tile of
 // 32 * kNA rows, LDS ring depth of the plain kernel.  At d = 32 a workgroup
-// of 4 waves with 32-key tiles (two workgroups per CU) is 12% faster than 8
-// waves with 64-key tiles; at d = 64 and 128 it is 4-9% slower on the large
-// workloads.
+// of 4 waves with a 2-deep ring (many workgroups per CU) is 20% faster than
+// 8 waves with a 3-deep ring; at d = 64 and 128 the smaller workgroup is
+// 3-9% slower on the large workloads.
 template <int D>
 struct FwdCfg {
 #ifdef FA_FWD_WAVES
@@ -50,10 +47,14 @@ struct FwdCfg {
 #ifdef FA_FWD_KEYBLOCKS
   static constexpr int kNA = FA_FWD_KEYBLOCKS;
 #else
-  static constexpr int kNA = D == 32 ? 1 : 2;
+  static constexpr int kNA = 2;
 #endif
   static constexpr int kBN = 32 * kNA;
+#ifdef FA_FWD_STAGES
   static constexpr int kStages = FA_FWD_STAGES;
+#else
+  static constexpr int kStages = D == 32 ? 2 : 3;
+#endif
 };
 
 // Rescale threshold in base-2 units: the reference maximum used for the
