@@ -47,13 +47,21 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const void* __restrict_
 }
 
 constexpr int kBwdWaves = 4, kBwdStages = FA_BWD_STAGES;
+// dQ: MFMAs' worth of LDS operand reads kept in flight in the S/dP and dQ
+// runs of the tile without the interleave.
+#ifndef FA_DQ_PRE1
+#define FA_DQ_PRE1 6
+#endif
+#ifndef FA_DQ_PRE2
+#define FA_DQ_PRE2 3
+#endif
 // dQ key tile rows and ring depth.
 #ifdef FA_DQ_TILE
 template <int D>
 constexpr int kDqTile = FA_DQ_TILE;
 #else
 template <int D>
-constexpr int kDqTile = 64;
+constexpr int kDqTile = D == 128 ? 32 : 64;
 #endif
 #ifdef FA_DQ_STAGES
 template <int D>
@@ -444,7 +452,7 @@ __device__ __forceinline__ void dq_tile(const lds_char* kt, const lds_char* vt, 
       s[a] = Elem<T>::mma(lds_rows_operand<D>(kt, 32 * a, kk, lane), qf[kk], s[a]);
       dp[a] = Elem<T>::mma(lds_rows_operand<D>(vt, 32 * a, kk, lane), dof[kk], dp[a]);
     }
-  sched_mfma_lds<2 * NA * NKK, 1, 6>();
+  sched_mfma_lds<2 * NA * NKK, 1, (2 * NA * NKK < FA_DQ_PRE1 ? 2 * NA * NKK : FA_DQ_PRE1)>();
   prio_mfma_end();
   if (edge) {
     const int klo = MASK ? win.lo(qrow) : kUnbounded, khi = MASK ? win.hi(qrow, N) : N - 1;
@@ -471,7 +479,7 @@ __device__ __forceinline__ void dq_tile(const lds_char* kt, const lds_char* vt, 
   for (int j = 0; j < 2 * NA; ++j)
 #pragma unroll
     for (int b = 0; b < NB; ++b) dqa[b] = Elem<T>::mma(lds_cols_operand<D>(kt, j, 32 * b, lane), dsf[j], dqa[b]);
-  sched_mfma_lds<2 * NA * NB, 2, 3>();
+  sched_mfma_lds<2 * NA * NB, 2, (2 * NA * NB < FA_DQ_PRE2 ? 2 * NA * NB : FA_DQ_PRE2)>();
   prio_mfma_end();
 }
 
@@ -481,15 +489,16 @@ __device__ __forceinline__ void dq_tile(const lds_char* kt, const lds_char* vt, 
 // elements per MFMA; dQ^T with dS = P (dP - D) formed one packed operand
 // ahead of the MFMAs that take it.  The MFMA pipe then runs while the wave's
 // own softmax work issues.
-// Used at d = 32 and 64 (10% and 5% faster dQ on the ragged fp16 d = 32 and
-// bf16 d = 64 workloads); at d = 128 it needs every register and gains
-// nothing.  FA_DQ_PIPE=0/1 forces one form for every head dimension.
+// Used at every head dimension (10% and 5% faster dQ on the ragged fp16
+// d = 32 and bf16 d = 64 workloads; at d = 128 it fits the registers with
+// 32-key tiles and is 1.6% faster on the causal workload, even on the full
+// one).  FA_DQ_PIPE=0/1 forces one form for every head dimension.
 #ifdef FA_DQ_PIPE
 template <int D>
 constexpr bool kDqPipe = FA_DQ_PIPE != 0;
 #else
 template <int D>
-constexpr bool kDqPipe = D != 128;
+constexpr bool kDqPipe = true;
 #endif
 // LDS operand reads run this many MFMAs ahead in the score runs and the dQ run.
 #ifdef FA_DQ_PIPE_PRE1
@@ -502,6 +511,7 @@ constexpr int kDqPipePre1 = D == 64 ? 1 : 2;
 #ifndef FA_DQ_PIPE_PRE3
 #define FA_DQ_PIPE_PRE3 1
 #endif
+
 template <class T, int D, bool MASK, int NA>
 __device__ __forceinline__ void dq_tile_pipe(const lds_char* kt, const lds_char* vt, const u32x4* qf,
                                              const u32x4* dof, f32x16* dqa, float l2, float dd, bool edge, int j0,

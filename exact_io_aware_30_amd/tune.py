@@ -61,6 +61,7 @@ SPACES = {
         "pre1_6": ["-DFA_DKDV_PRE1=6"],
         "pre1_4_occ1": ["-DFA_DKDV_PRE1=4", "-DFA_DKDV_OCC=1"],
         "pre1_4_pre2_2": ["-DFA_DKDV_PRE1=4", "-DFA_DKDV_PRE2=2"],
+        "pre1_4_pre2_4": ["-DFA_DKDV_PRE1=4", "-DFA_DKDV_PRE2=4"],
         "pre2_2": ["-DFA_DKDV_PRE2=2"],
     },
     "dq": {
@@ -70,6 +71,11 @@ SPACES = {
         "pipe": ["-DFA_DQ_PIPE=1"],
         "nopipe": ["-DFA_DQ_PIPE=0"],
         "t32_pipe": ["-DFA_DQ_TILE=32", "-DFA_DQ_PIPE=1"],
+        "pre1_4": ["-DFA_DQ_PRE1=4"],
+        "pre1_8": ["-DFA_DQ_PRE1=8"],
+        "pre2_2": ["-DFA_DQ_PRE2=2"],
+        "pre2_4": ["-DFA_DQ_PRE2=4"],
+        "pre1_4_pre2_2": ["-DFA_DQ_PRE1=4", "-DFA_DQ_PRE2=2"],
     },
 }
 SOURCE = {"fwd": "fa_fwd.hip", "dkdv": "fa_bwd.hip", "dq": "fa_bwd.hip"}
