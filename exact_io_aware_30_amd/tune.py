@@ -63,6 +63,10 @@ SPACES = {
         "pre1_4_pre2_2": ["-DFA_DKDV_PRE1=4", "-DFA_DKDV_PRE2=2"],
         "pre1_4_pre2_4": ["-DFA_DKDV_PRE1=4", "-DFA_DKDV_PRE2=4"],
         "pre2_2": ["-DFA_DKDV_PRE2=2"],
+        "vlds": ["-DFA_DKDV_VLDS=1"],
+        "pre1_3_vlds": ["-DFA_DKDV_PRE1=3", "-DFA_DKDV_VLDS=1"],
+        "occ2_vlds": ["-DFA_DKDV_OCC=2", "-DFA_DKDV_VLDS=1"],
+        "pre2_4": ["-DFA_DKDV_PRE2=4"],
         "tile64": ["-DFA_DKDV_TILE=64"],
         "vregs": ["-DFA_DKDV_VLDS=0"],
         "stages3": ["-DFA_DKDV_STAGES=3"],
