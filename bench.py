@@ -30,6 +30,9 @@ both halved under the causal mask.
                                 (for hardware byte counters)
     --results PATH              also write every JSON record the run prints
                                 to PATH as one JSON list (a results file)
+    --graph                     also time the step captured once in a HIP
+                                graph and replayed (graph_ms_per_step,
+                                graph_tflops); `value` stays the eager rate
 
 Without a mode option it prints one JSON line.  Besides the contract fields it carries
   roofline      the dominant kernel (longest average launch, timed with HIP
@@ -500,6 +503,8 @@ def main():
     ap.add_argument("--compare", action="store_true")
     ap.add_argument("--oom", action="store_true")
     ap.add_argument("--compare-step", choices=("flash", "ordinary"), default=None)
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured in a HIP graph (replays; reported as graph_* fields)")
     ap.add_argument("--results", default=None, help="also write every JSON record printed to this file "
                                                     "(a JSON list)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -574,6 +579,19 @@ def run(args):
     wall = time.perf_counter() - t0
     per = {p: sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / args.steps for j, p in enumerate(phases)}
     assert torch.isfinite(o).all() and torch.isfinite(dq).all(), "non-finite output"
+    graph_ms = None
+    if args.graph:
+        # The same step captured once and replayed: no per-launch host cost.
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     if args.calib_copy_mib:
         calib_copy(args.calib_copy_mib)
 
@@ -624,6 +642,9 @@ def run(args):
         "cpu_baseline": None,
         "library_hash": library_hash(),
     }
+    if graph_ms is not None:
+        line["graph_ms_per_step"] = round(graph_ms, 4)
+        line["graph_tflops"] = round(fb / (graph_ms * 1e-3) / 1e12, 2)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     emit(line)
