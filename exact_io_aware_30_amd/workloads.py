@@ -99,16 +99,16 @@ def flops(w: Workload):
     return float(f), float(b), float(f + b)
 
 
-def kernel_flops(w: Workload):
+def kernel_flops(w: Workload, executed: bool = False):
     """Counted FLOPs attributed to each kernel (causal halved).
 
     The dK/dV kernel carries the QK^T recompute, dO V^T, P^T dO and dS^T Q
     (8 B H N^2 d); the dQ kernel carries dS K (2 B H N^2 d).  The dQ
     kernel's own recomputation of S and dP is work the deterministic layout
-    adds, not counted.
+    adds, not counted; with ``executed`` it is included (6 B H N^2 d).
     """
     base = w.B * w.H * w.N * w.N * w.d * (0.5 if w.causal else 1.0)
-    return {"fwd": 4 * base, "bwd_dkdv": 8 * base, "bwd_dq": 2 * base, "bwd_preprocess": 0.0}
+    return {"fwd": 4 * base, "bwd_dkdv": 8 * base, "bwd_dq": (6 if executed else 2) * base, "bwd_preprocess": 0.0}
 
 
 def algorithmic_bytes(w: Workload):
