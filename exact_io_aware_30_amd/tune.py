@@ -50,6 +50,9 @@ SPACES = {
         "w4_k1_s2": ["-DFA_FWD_WAVES=4", "-DFA_FWD_KEYBLOCKS=1", "-DFA_FWD_STAGES=2"],
         "w4_k1_s3": ["-DFA_FWD_WAVES=4", "-DFA_FWD_KEYBLOCKS=1", "-DFA_FWD_STAGES=3"],
         "w2_k2_s2": ["-DFA_FWD_WAVES=2", "-DFA_FWD_KEYBLOCKS=2", "-DFA_FWD_STAGES=2"],
+        "prio": ["-DFA_FWD_PRIO=1"],
+        "pipe_pre_2_2": ["-DFA_FWD_PIPE_PRE1=2", "-DFA_FWD_PIPE_PRE2=2"],
+        "pipe_pre_4_3": ["-DFA_FWD_PIPE_PRE1=4", "-DFA_FWD_PIPE_PRE2=3"],
     },
     "dkdv": {
         "default": [],
@@ -83,6 +86,12 @@ SPACES = {
         "pre2_2": ["-DFA_DQ_PRE2=2"],
         "pre2_4": ["-DFA_DQ_PRE2=4"],
         "pre1_4_pre2_2": ["-DFA_DQ_PRE1=4", "-DFA_DQ_PRE2=2"],
+        "stages3": ["-DFA_DQ_STAGES=3"],
+        "stages4": ["-DFA_DQ_STAGES=4"],
+        "pipe_pre1_3": ["-DFA_DQ_PIPE_PRE1=3"],
+        "pipe_pre1_4": ["-DFA_DQ_PIPE_PRE1=4"],
+        "pipe_pre3_2": ["-DFA_DQ_PIPE_PRE3=2"],
+        "pipe_pre1_3_pre3_2": ["-DFA_DQ_PIPE_PRE1=3", "-DFA_DQ_PIPE_PRE3=2"],
     },
 }
 SOURCE = {"fwd": "fa_fwd.hip", "dkdv": "fa_bwd.hip", "dq": "fa_bwd.hip"}
