@@ -25,6 +25,10 @@ both halved under the causal mask.
     python bench.py --oom       bf16 causal d=128, B=1, H=16, N = 4K .. 128K:
                                 peak memory and time of both versions until
                                 ordinary attention runs out of memory
+    python bench.py --variants  grouped-query heads, sliding windows, a packed
+                                variable-length batch and the autograd
+                                interface, forward+backward TFLOP/s over the
+                                exact visible query-key pairs
     python bench.py --compare-step flash|ordinary --workload W
                                 one forward+backward step of one version
                                 (for hardware byte counters)
@@ -471,6 +475,136 @@ def oom():
         torch.cuda.empty_cache()
 
 
+def variants():
+    """Throughput of the wider forms: grouped-query heads, sliding windows,
+    packed variable-length batches, and the autograd interface beside raw
+    ABI calls.  FLOPs: 4 d (forward) + 10 d (backward) per visible
+    query-key pair and query head, counted exactly (for the plain causal
+    mask this is N(N+1)/2 pairs, not the N^2/2 of the headline convention)."""
+    import torch
+
+    from exact_io_aware_30_amd import binding, interface, workloads
+
+    dev = torch.device("cuda:0")
+    B, H, N, d = 2, 16, 8192, 128
+    scale = d ** -0.5
+    rows = []
+
+    def put(kind, desc, ms, pairs_heads, extra=None):
+        fl = 14.0 * d * pairs_heads
+        r = {"form": kind, "case": desc, "fwd_bwd_ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+             "frac_mfma_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        r.update(extra or {})
+        rows.append(r)
+
+    def bufs(shape_q, shape_kv, seed):
+        q = workloads.make_tensor(shape_q, "bf16", seed, dev)
+        do = workloads.make_tensor(shape_q, "bf16", seed + 1, dev)
+        k = workloads.make_tensor(shape_kv, "bf16", seed + 2, dev)
+        v = workloads.make_tensor(shape_kv, "bf16", seed + 3, dev)
+        o, dq = torch.empty_like(q), torch.empty_like(q)
+        dk, dv = torch.empty_like(k), torch.empty_like(k)
+        return q, k, v, do, o, dq, dk, dv
+
+    # grouped-query heads: 16 query heads over 16, 4, 1 key/value heads
+    for hkv in (16, 4, 1):
+        q, k, v, do, o, dq, dk, dv = bufs((B, H, N, d), (B, hkv, N, d), 5000 + hkv)
+        lse = torch.empty(B, H, N, dtype=torch.float32, device=dev)
+        delta = torch.empty_like(lse)
+        nbytes = binding.fa_bwd_workspace_size(B, H, hkv, N, d)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
+
+        def step(ws=ws):
+            binding.fa_fwd_gqa(q, k, v, o, lse, scale, True)
+            binding.fa_bwd_preprocess(o, do, delta)
+            binding.fa_bwd_ex_ws(q, k, v, do, lse, delta, dq, dk, dv, scale, (-1, 0), ws)
+
+        extra = {"workspace_mib": round(nbytes / 2 ** 20, 1)}
+        if nbytes:  # the same step without the head split, for comparison
+            extra["unsplit_ms"] = round(_median_ms(lambda: step(None), warmup=3, reps=10)[0], 4)
+        put("gqa", f"bf16 [2,16,8192,128] causal, Hkv={hkv}", _median_ms(step, warmup=3, reps=10)[0],
+            B * H * workloads.visible_pairs(N, True), extra)
+        del q, k, v, do, o, dq, dk, dv, lse, delta, ws
+
+    # sliding windows on the headline shape
+    q, k, v, do, o, dq, dk, dv = bufs((B, H, N, d), (B, H, N, d), 5100)
+    lse = torch.empty(B, H, N, dtype=torch.float32, device=dev)
+    delta = torch.empty_like(lse)
+    for win in ((-1, 0), (1024, 0), (256, 0), (512, 512)):
+        def step(win=win):
+            binding.fa_fwd_ex(q, k, v, o, lse, scale, win)
+            binding.fa_bwd_preprocess(o, do, delta)
+            binding.fa_bwd_ex(q, k, v, do, lse, delta, dq, dk, dv, scale, win)
+
+        put("window", f"bf16 [2,16,8192,128] window (left, right) = {win}",
+            _median_ms(step, warmup=3, reps=10)[0], B * H * workloads.visible_pairs(N, False, win))
+
+    # autograd interface beside the raw calls (same inputs, causal)
+    def raw():
+        binding.fa_fwd(q, k, v, o, lse, scale, True)
+        binding.fa_bwd_preprocess(o, do, delta)
+        binding.fa_bwd(q, k, v, do, lse, delta, dq, dk, dv, scale, True)
+
+    qa, ka, va = (x.detach().clone().requires_grad_(True) for x in (q, k, v))
+
+    def auto():
+        qa.grad = ka.grad = va.grad = None
+        out = interface.flash_attn(qa, ka, va, causal=True, softmax_scale=scale)
+        out.backward(do)
+
+    t_raw, t_auto = _median_ms(raw, warmup=3, reps=10)[0], _median_ms(auto, warmup=3, reps=10)[0]
+    put("interface", "flash_attn + backward (autograd), bf16 [2,16,8192,128] causal", t_auto,
+        B * H * workloads.visible_pairs(N, True), {"raw_abi_ms": round(t_raw, 4), "overhead_ms": round(t_auto - t_raw, 4)})
+    del q, k, v, do, o, dq, dk, dv, lse, delta, qa, ka, va
+
+    # packed variable-length batch: 24 sequences of seeded lengths 256 .. 4096
+    g = torch.Generator().manual_seed(5200)
+    lens = torch.randint(256, 4097, (24,), generator=g).tolist()
+    T, mx = sum(lens), max(lens)
+    cu = torch.tensor([0] + torch.tensor(lens).cumsum(0).tolist(), dtype=torch.int32, device=dev)
+    q, k, v, do, o, dq, dk, dv = bufs((H, T, d), (H, T, d), 5300)
+    lse = torch.empty(H, T, dtype=torch.float32, device=dev)
+    delta = torch.empty_like(lse)
+
+    def step():
+        binding.fa_fwd_varlen(q, k, v, o, lse, cu, mx, scale, (-1, 0))
+        binding.fa_bwd_preprocess(o.view(1, H, T, d), do.view(1, H, T, d), delta.view(1, H, T))
+        binding.fa_bwd_varlen(q, k, v, do, lse, delta, dq, dk, dv, cu, mx, scale, (-1, 0))
+
+    put("varlen", f"bf16 H=16 d=128 causal, 24 packed sequences, T={T}, lengths {min(lens)}..{mx}",
+        _median_ms(step, warmup=3, reps=10)[0], H * sum(workloads.visible_pairs(n, True) for n in lens))
+    del q, k, v, do, o, dq, dk, dv, lse, delta
+
+    # the same packed batch with one key/value head (multi-query), head split on
+    q, k, v, do, o, dq, dk, dv = bufs((H, T, d), (1, T, d), 5400)
+    lse = torch.empty(H, T, dtype=torch.float32, device=dev)
+    delta = torch.empty_like(lse)
+    nbytes = binding.fa_bwd_varlen_workspace_size(len(lens), mx, T, H, 1, d)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
+
+    def step(ws=ws):
+        binding.fa_fwd_varlen(q, k, v, o, lse, cu, mx, scale, (-1, 0))
+        binding.fa_bwd_preprocess(o.view(1, H, T, d), do.view(1, H, T, d), delta.view(1, H, T))
+        binding.fa_bwd_varlen_ws(q, k, v, do, lse, delta, dq, dk, dv, cu, mx, scale, (-1, 0), ws)
+
+    extra = {"workspace_mib": round(nbytes / 2 ** 20, 1)}
+    if nbytes:
+        extra["unsplit_ms"] = round(_median_ms(lambda: step(None), warmup=3, reps=10)[0], 4)
+    put("varlen", f"bf16 H=16 Hkv=1 d=128 causal, the same 24 packed sequences", _median_ms(step, warmup=3, reps=10)[0],
+        H * sum(workloads.visible_pairs(n, True) for n in lens), extra)
+
+    print("| form | case | fwd+bwd ms | TFLOP/s (exact visible pairs) | % of 2.5 PF | notes |")
+    print("|---|---|---|---|---|---|")
+    for r in rows:
+        note = f"raw ABI {r['raw_abi_ms']} ms, overhead {r['overhead_ms']} ms" if "raw_abi_ms" in r else \
+            f"head split: {r['workspace_mib']} MiB workspace; unsplit {r['unsplit_ms']} ms" if "unsplit_ms" in r \
+            else ""
+        print(f"| {r['form']} | {r['case']} | {r['fwd_bwd_ms']} | {r['tflops']} | {100 * r['frac_mfma_peak']:.1f} "
+              f"| {note} |")
+    for r in rows:
+        emit(r)
+
+
 def compare_step(version, name):
     """One forward+backward step of one version on one workload, nothing else
     launched on the device (for hardware byte counters)."""
@@ -502,6 +636,7 @@ def main():
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--compare", action="store_true")
     ap.add_argument("--oom", action="store_true")
+    ap.add_argument("--variants", action="store_true")
     ap.add_argument("--compare-step", choices=("flash", "ordinary"), default=None)
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured in a HIP graph (replays; reported as graph_* fields)")
@@ -530,8 +665,9 @@ def run(args):
         if args.calib_copy_mib:
             calib_copy(args.calib_copy_mib)
         return
-    if args.report or args.sweep or args.compare or args.oom:
-        (report if args.report else sweep if args.sweep else compare if args.compare else oom)()
+    if args.report or args.sweep or args.compare or args.oom or args.variants:
+        (report if args.report else sweep if args.sweep else compare if args.compare else oom if args.oom
+         else variants)()
         if args.calib_copy_mib:
             calib_copy(args.calib_copy_mib)
         return

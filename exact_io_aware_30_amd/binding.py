@@ -47,13 +47,20 @@ _SIG = {
     "fa_bwd_dq_ex": [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _i, _i, _p],
     "fa_fwd_varlen": [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _i, _i, _p],
     "fa_bwd_varlen": [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _i, _i, _p],
+    "fa_bwd_ex_ws": [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _i, _i, _p, ctypes.c_size_t,
+                     _p],
+    "fa_bwd_varlen_ws": [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _i, _i, _p,
+                         ctypes.c_size_t, _p],
+    "fa_bwd_workspace_size": [_i, _i, _i, _i, _i],
+    "fa_bwd_varlen_workspace_size": [_i, _i, _i, _i, _i, _i],
     "fa_status_string": [_i],
     "fa_version": [],
 }
 for _name, _args in _SIG.items():
     _fn = getattr(_lib, _name)
     _fn.argtypes = _args
-    _fn.restype = ctypes.c_char_p if _name == "fa_status_string" else _i
+    _fn.restype = ctypes.c_char_p if _name == "fa_status_string" else \
+        ctypes.c_size_t if _name.endswith("_workspace_size") else _i
 
 EXPORTED = tuple(_SIG)
 
@@ -254,6 +261,37 @@ def fa_bwd_dq_ex(q, k, v, do, lse, delta, dq, scale: float, window) -> None:
                              _DT[q.dtype], _stream(q)), "fa_bwd_dq_ex")
 
 
+def fa_bwd_workspace_size(B: int, H: int, Hkv: int, N: int, d: int) -> int:
+    """Bytes of workspace with which fa_bwd_ex_ws splits the query heads of a
+    key/value head over several dK/dV workgroups (0: no split pays)."""
+    return int(_lib.fa_bwd_workspace_size(int(B), int(H), int(Hkv), int(N), int(d)))
+
+
+def fa_bwd_varlen_workspace_size(B: int, max_seqlen: int, T: int, H: int, Hkv: int, d: int) -> int:
+    return int(_lib.fa_bwd_varlen_workspace_size(int(B), int(max_seqlen), int(T), int(H), int(Hkv), int(d)))
+
+
+def _workspace(ws, device):
+    """(pointer, bytes) of an optional uint8 workspace tensor on `device`."""
+    if ws is None:
+        return None, 0
+    if ws.dtype != torch.uint8 or not ws.is_cuda or not ws.is_contiguous() or ws.device != device:
+        raise ValueError("workspace must be a contiguous uint8 GPU tensor on q's device")
+    return ws.data_ptr(), ws.numel()
+
+
+def fa_bwd_ex_ws(q, k, v, do, lse, delta, dq, dk, dv, scale: float, window, workspace) -> None:
+    B, H, N, d = _bhnd(q, "q")
+    Hkv = _kv(q, ((k, "k"), (v, "v"), (dk, "dk"), (dv, "dv")))
+    _same(q, (do, "do"), (dq, "dq"))
+    _rows(q, (lse, "lse"), (delta, "delta"))
+    wl, wr = window
+    wp, wb = _workspace(workspace, q.device)
+    _check(_lib.fa_bwd_ex_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                             delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, N, d,
+                             float(scale), int(wl), int(wr), _DT[q.dtype], wp, wb, _stream(q)), "fa_bwd_ex_ws")
+
+
 def attention_forward(q, k, v, scale: float, causal: bool, window=None):
     """(o, lse) with o like q and lse float32 [B, H, N]; k and v may have
     fewer heads than q (grouped-query attention); window = (left, right)
@@ -275,7 +313,13 @@ def attention_backward(q, k, v, o, do, lse, scale: float, causal: bool, window=N
     delta = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     fa_bwd_preprocess(o, do, delta)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    if window is not None:
+    B, H, N, d = q.shape
+    nbytes = fa_bwd_workspace_size(B, H, k.shape[1], N, d) if k.dim() == 4 else 0
+    if nbytes:
+        # few key/value heads: split their query heads over more workgroups
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+        fa_bwd_ex_ws(q, k, v, do, lse, delta, dq, dk, dv, scale, _window(window, causal), ws)
+    elif window is not None:
         fa_bwd_ex(q, k, v, do, lse, delta, dq, dk, dv, scale, _window(window, causal))
     elif k.dim() == 4 and k.shape[1] != q.shape[1]:
         fa_bwd_gqa(q, k, v, do, lse, delta, dq, dk, dv, scale, causal)
@@ -328,6 +372,18 @@ def fa_bwd_varlen(q, k, v, do, lse, delta, dq, dk, dv, cu_seqlens, max_seqlen: i
                               _stream(q)), "fa_bwd_varlen")
 
 
+def fa_bwd_varlen_ws(q, k, v, do, lse, delta, dq, dk, dv, cu_seqlens, max_seqlen: int, scale: float, window,
+                     workspace) -> None:
+    H, Hkv, T, d, B = _packed(q, ((k, "k"), (v, "v"), (dk, "dk"), (dv, "dv")), ((do, "do"), (dq, "dq")),
+                              ((lse, "lse"), (delta, "delta")), cu_seqlens)
+    wl, wr = window
+    wp, wb = _workspace(workspace, q.device)
+    _check(_lib.fa_bwd_varlen_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                                 delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), cu_seqlens.data_ptr(),
+                                 B, int(max_seqlen), T, H, Hkv, d, float(scale), int(wl), int(wr), _DT[q.dtype], wp,
+                                 wb, _stream(q)), "fa_bwd_varlen_ws")
+
+
 def attention_forward_varlen(q, k, v, cu_seqlens, max_seqlen: int, scale: float, causal: bool, window=None):
     """(o [H, T, d], lse [H, T]) for packed sequences."""
     o = torch.empty_like(q)
@@ -344,5 +400,8 @@ def attention_backward_varlen(q, k, v, o, do, lse, cu_seqlens, max_seqlen: int, 
     delta = torch.empty((H, T), dtype=torch.float32, device=q.device)
     fa_bwd_preprocess(o.view(1, H, T, d), do.view(1, H, T, d), delta.view(1, H, T))
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    fa_bwd_varlen(q, k, v, do, lse, delta, dq, dk, dv, cu_seqlens, max_seqlen, scale, _window(window, causal))
+    nbytes = fa_bwd_varlen_workspace_size(cu_seqlens.numel() - 1, max_seqlen, T, H, k.shape[0], d) \
+        if k.dim() == 3 else 0
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None
+    fa_bwd_varlen_ws(q, k, v, do, lse, delta, dq, dk, dv, cu_seqlens, max_seqlen, scale, _window(window, causal), ws)
     return dq, dk, dv, delta

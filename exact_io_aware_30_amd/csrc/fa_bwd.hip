@@ -12,6 +12,7 @@
 #include "fa_launch.h"
 
 #include <algorithm>
+#include <type_traits>
 
 // Tile configuration (compile-time; defaults chosen by measurement).
 #ifndef FA_BWD_STAGES
@@ -290,26 +291,28 @@ __device__ __forceinline__ void dkdv_step(lds_char* lds, int t, int nt, int i_st
 // queries that see some key of the block, and only tiles that cross an edge
 // of a key's window are masked.
 // ---------------------------------------------------------------------------
-// The ring loop over query tiles, once per query head of the key/value
-// head's group (G = 1 without grouping: the gradients of a shared K and V
-// are the sums over the heads that read them), and the final store of dK
-// and dV.  The first head's first tiles were issued by the caller.
-template <class T, int D, bool MASK, class VOp>
+// The ring loop over query tiles, once per query head g0 .. g0 + ng - 1 of
+// the key/value head's group (G = 1 without grouping: the gradients of a
+// shared K and V are the sums over the heads that read them), and the final
+// store of dK and dV, or of their float32 partial sums over those heads when
+// the group is split over several workgroups.  The first head's first tiles
+// were issued by the caller.
+template <class T, int D, bool MASK, bool SPLIT, class VOp, class Dst>
 __device__ __forceinline__ void dkdv_run(lds_char* lds, int nt, int i_start, const DmaTile<Dkdv<D>::kTile, D, kBwdWaves>& dma,
                                          const void* qp, const void* dop, const float* lsep, const float* deltap,
-                                         const Geom& geo, int b, int hk, int N, const u32x4* kf, const VOp& vop,
-                                         __amdgpu_buffer_rsrc_t rdk, __amdgpu_buffer_rsrc_t rdv, int wk0, int krow,
-                                         Win win, float c, float scale, int w, int lane) {
+                                         const Geom& geo, int b, int hk, int g0, int ng, int N, const u32x4* kf,
+                                         const VOp& vop, Dst rdk, Dst rdv,
+                                         int wk0, int krow, Win win, float c, float scale, int w, int lane) {
   constexpr int S = Dkdv<D>::kStages, NB = D / 32, BMQ = Dkdv<D>::kTile;
   constexpr int BUF = 2 * BMQ * D * 2 + 2 * kStatsRows * 4;
   const uint32_t bytes = (uint32_t)N * D * 2;
   f32x16 dka[NB], dva[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) dka[b] = dva[b] = (f32x16){};
-  for (int g = 0; g < geo.G; ++g) {
+  for (int g = 0; g < ng; ++g) {
     long qr0, kvr0;
     int len;
-    geo.slice(b, hk * geo.G + g, qr0, kvr0, len);
+    geo.slice(b, hk * geo.G + g0 + g, qr0, kvr0, len);
     const size_t head = (size_t)qr0 * D * 2;
     const Rsrc rq = make_rsrc_words((const char*)qp + head, bytes);
     const Rsrc rdo = make_rsrc_words((const char*)dop + head, bytes);
@@ -338,17 +341,30 @@ __device__ __forceinline__ void dkdv_run(lds_char* lds, int nt, int i_start, con
                                        win, c, w, lane);
     }
   }
-  store_rows<T, D>(rdk, krow, dka, scale, lane);
-  store_rows<T, D>(rdv, krow, dva, 1.0f, lane);
+  if constexpr (SPLIT) {
+    // float32 partial rows (built here, after the loop, to keep the
+    // descriptors out of the loop's registers)
+    store_rows_f32<D>(make_rsrc(rdk, (uint32_t)N * D * 4), krow, dka, lane);
+    store_rows_f32<D>(make_rsrc(rdv, (uint32_t)N * D * 4), krow, dva, lane);
+  } else {
+    store_rows<T, D>(rdk, krow, dka, scale, lane);
+    store_rows<T, D>(rdv, krow, dva, 1.0f, lane);
+  }
 }
 
-// Grid: key blocks x key/value heads (BHkv = B * H / G of them); the query
-// heads of key/value head hk are hk G .. hk G + G - 1 of the same batch.
-template <class T, int D, int MODE>
+// Grid: key blocks x head splits x key/value heads (BHkv = B * H / G of
+// them); the query heads of key/value head hk are hk G .. hk G + G - 1 of
+// the same batch.  With GS = 1 a workgroup takes the whole group and stores
+// dK and dV; with GS > 1 (GS divides G) split s takes heads s G/GS ..
+// (s + 1) G/GS - 1 and stores float32 sums (dK unscaled) into
+// part[s][row][D] (dK) and part[GS + s][row][D] (dV), rows numbered as in
+// the K tensor (R of them), for dkdv_reduce_kernel to add up.
+template <class T, int D, int MODE, bool SPLIT>
 __global__ __launch_bounds__(64 * kBwdWaves, Dkdv<D>::kOcc) void dkdv_kernel(
     const void* __restrict__ qp, const void* __restrict__ kp, const void* __restrict__ vp,
     const void* __restrict__ dop, const float* __restrict__ lsep, const float* __restrict__ deltap,
-    void* __restrict__ dkp, void* __restrict__ dvp, Geom geo, int BHkv, Win win_in, float c, float scale) {
+    void* __restrict__ dkp, void* __restrict__ dvp, float* __restrict__ part, int GS_in, Geom geo, int BHkv,
+    Win win_in, float c, float scale) {
   // MODE 0: no window (full mask); 1: the causal window (-1, 0), a
   // compile-time constant so that every window test folds; 2: any window.
   constexpr bool MASK = MODE != 0;
@@ -364,21 +380,35 @@ __global__ __launch_bounds__(64 * kBwdWaves, Dkdv<D>::kOcc) void dkdv_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, known uniform
+  const int GS = SPLIT ? GS_in : 1;
   const int x = blockIdx.x;
-  const int kb = x / BHkv, bhkv = x % BHkv;
-  const int Hkv = geo.H / geo.G;
+  const int kb = x / (BHkv * GS), rest = x - kb * (BHkv * GS);
+  // Uniform across the workgroup: kept in scalar registers.
+  const int split = SPLIT ? __builtin_amdgcn_readfirstlane(rest / BHkv) : 0, bhkv = rest - split * BHkv;
+  const int ng = SPLIT ? __builtin_amdgcn_readfirstlane(geo.G / GS) : geo.G;
+  const int Hkv = geo.H / geo.G, g0 = split * ng;
   const int b = bhkv / Hkv, hk = bhkv % Hkv;
   const int k0 = kb * BNK;
-  long qr0, kvr0;  // the group's first query head, and the key/value head
+  long qr0, kvr0;  // the split's first query head, and the key/value head
   int N;
-  geo.slice(b, hk * geo.G, qr0, kvr0, N);
+  geo.slice(b, hk * geo.G + g0, qr0, kvr0, N);
   if (k0 >= N) return;  // past the end of a shorter packed sequence (the whole workgroup)
   const size_t headkv = (size_t)kvr0 * D * 2;
   const size_t head0 = (size_t)qr0 * D * 2;
   const uint32_t bytes = (uint32_t)N * D * 2;
   const auto rk = make_rsrc((const char*)kp + headkv, bytes);
-  const auto rdk = make_rsrc((char*)dkp + headkv, bytes);
-  const auto rdv = make_rsrc((char*)dvp + headkv, bytes);
+  // dK and dV destinations: buffer descriptors of the output rows, or with
+  // SPLIT the float32 partial rows of this split.
+  using Dst = std::conditional_t<SPLIT, const float*, __amdgpu_buffer_rsrc_t>;
+  Dst rdk, rdv;
+  if constexpr (SPLIT) {
+    const long R = geo.cu ? (long)Hkv * geo.T : (long)BHkv * geo.N;
+    rdk = part + ((long)split * R + kvr0) * D;
+    rdv = rdk + (long)GS * R * D;
+  } else {
+    rdk = make_rsrc((char*)dkp + headkv, bytes);
+    rdv = make_rsrc((char*)dvp + headkv, bytes);
+  }
 
   // Query rows i_start .. i_end - 1 hold every query that sees a key of the block.
   const int i_start = MASK ? win.query_lo(k0) : 0, i_end = MASK ? win.query_hi(k0 + BNK - 1, N) : N;
@@ -424,11 +454,46 @@ __global__ __launch_bounds__(64 * kBwdWaves, Dkdv<D>::kOcc) void dkdv_kernel(
     if (S > 3 && nt > 2) dkdv_issue<D>(lds + (2 % S) * BUF, i_start + 2 * BMQ, dma, rq, rdo, rl, rd, w, lane);
   }
   if constexpr (VL)
-    dkdv_run<T, D, MASK>(lds, nt, i_start, dma, qp, dop, lsep, deltap, geo, b, hk, N, kf, VLds<D>{vt, 32 * w},
-                         rdk, rdv, wk0, krow, win, c, scale, w, lane);
+    dkdv_run<T, D, MASK, SPLIT>(lds, nt, i_start, dma, qp, dop, lsep, deltap, geo, b, hk, g0, ng, N, kf,
+                                VLds<D>{vt, 32 * w}, rdk, rdv, wk0, krow, win, c, scale, w, lane);
   else
-    dkdv_run<T, D, MASK>(lds, nt, i_start, dma, qp, dop, lsep, deltap, geo, b, hk, N, kf, VRegs{vf}, rdk, rdv,
-                         wk0, krow, win, c, scale, w, lane);
+    dkdv_run<T, D, MASK, SPLIT>(lds, nt, i_start, dma, qp, dop, lsep, deltap, geo, b, hk, g0, ng, N, kf, VRegs{vf},
+                                rdk, rdv, wk0, krow, win, c, scale, w, lane);
+}
+
+// Sum of the GS float32 partials of dK and dV (split 0 first, so the bits
+// depend only on GS), dK times the scale, rounded to the element type.  One
+// workgroup per dK/dV key block: rows k0 .. k0 + 127 of one key/value head,
+// D / 4 lanes per row, four columns per lane.
+template <class T, int D>
+__global__ __launch_bounds__(256) void dkdv_reduce_kernel(const float* __restrict__ part, void* __restrict__ dkp,
+                                                          void* __restrict__ dvp, int GS, Geom geo, int BHkv,
+                                                          float scale) {
+  constexpr int BNK = 32 * kBwdWaves, LPR = D / 4, RPI = 256 / LPR;
+  const int x = blockIdx.x, kb = x / BHkv, bhkv = x % BHkv;
+  const int Hkv = geo.H / geo.G, b = bhkv / Hkv, hk = bhkv % Hkv;
+  long qr0, kvr0;
+  int N;
+  geo.slice(b, hk * geo.G, qr0, kvr0, N);
+  const int k0 = kb * BNK;
+  if (k0 >= N) return;
+  const int rows = min(BNK, N - k0);
+  const long R = geo.cu ? (long)Hkv * geo.T : (long)BHkv * geo.N;
+  const long plane = R * D;
+  const int c4 = threadIdx.x % LPR;
+  for (int r = threadIdx.x / LPR; r < rows; r += RPI) {
+    const long e = (kvr0 + k0 + r) * D + 4 * c4;
+    float4 sk = *(const float4*)(part + e), sv = *(const float4*)(part + GS * plane + e);
+    for (int s = 1; s < GS; ++s) {
+      const float4 pk = *(const float4*)(part + s * plane + e), pv = *(const float4*)(part + (GS + s) * plane + e);
+      sk.x += pk.x; sk.y += pk.y; sk.z += pk.z; sk.w += pk.w;
+      sv.x += pv.x; sv.y += pv.y; sv.z += pv.z; sv.w += pv.w;
+    }
+    const u32x2 ok = {Elem<T>::pack2(sk.x * scale, sk.y * scale), Elem<T>::pack2(sk.z * scale, sk.w * scale)};
+    const u32x2 ov = {Elem<T>::pack2(sv.x, sv.y), Elem<T>::pack2(sv.z, sv.w)};
+    *(u32x2*)((char*)dkp + e * 2) = ok;
+    *(u32x2*)((char*)dvp + e * 2) = ov;
+  }
 }
 
 // One key tile of the dQ kernel for one wave (`edge`: the tile crosses an
@@ -750,8 +815,18 @@ static hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t st) {
   const int BHkv = a.B * a.Hkv;
   const int nkb = (a.N + 127) / 128;
   const Geom geo{a.N, a.H, a.H / a.Hkv, a.cu, a.T};
-  hipLaunchKernelGGL((dkdv_kernel<T, D, MODE>), dim3(nkb * BHkv), dim3(256), 0, st, a.q, a.k, a.v, a.dO, a.lse,
-                     a.delta, a.dk, a.dv, geo, BHkv, Win{a.wl, a.wr}, a.scale * kLog2e, a.scale);
+  if (!a.part) {
+    hipLaunchKernelGGL((dkdv_kernel<T, D, MODE, false>), dim3(nkb * BHkv), dim3(256), 0, st, a.q, a.k, a.v, a.dO,
+                       a.lse, a.delta, a.dk, a.dv, nullptr, 1, geo, BHkv, Win{a.wl, a.wr}, a.scale * kLog2e, a.scale);
+    return hipGetLastError();
+  }
+  const int GS = a.splits;
+  hipLaunchKernelGGL((dkdv_kernel<T, D, MODE, true>), dim3(nkb * BHkv * GS), dim3(256), 0, st, a.q, a.k, a.v, a.dO,
+                     a.lse, a.delta, a.dk, a.dv, a.part, GS, geo, BHkv, Win{a.wl, a.wr}, a.scale * kLog2e, a.scale);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((dkdv_reduce_kernel<T, D>), dim3(nkb * BHkv), dim3(256), 0, st, a.part, a.dk, a.dv, GS, geo,
+                     BHkv, a.scale);
   return hipGetLastError();
 }
 

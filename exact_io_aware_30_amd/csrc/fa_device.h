@@ -148,6 +148,9 @@ __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 __device__ __forceinline__ void bstore8(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 v) {
   __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
 }
+__device__ __forceinline__ void bstore16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
 
 // ---------------------------------------------------------------------------
 // Swizzled LDS tile of ROWS x D 16-bit elements.
@@ -457,6 +460,24 @@ __device__ __forceinline__ void store_rows(__amdgpu_buffer_rsrc_t dst, int row, 
       u32x2 v = {Elem<T>::pack2(acc[b][4 * g + 0] * mul, acc[b][4 * g + 1] * mul),
                  Elem<T>::pack2(acc[b][4 * g + 2] * mul, acc[b][4 * g + 3] * mul)};
       bstore8(dst, (uint32_t)((row * D + col) * 2), v);
+    }
+}
+
+// The same rows kept in float32 (partial sums that a later pass adds up).
+template <int D>
+__device__ __forceinline__ void store_rows_f32(__amdgpu_buffer_rsrc_t dst, int row, const f32x16* acc, int lane) {
+  const int h = lane >> 5;
+  // The element is taken by value first: a bit cast applied directly to a
+  // vector-element expression reads the vector's first element.
+  auto bits = [](float x) { return __builtin_bit_cast(uint32_t, x); };
+#pragma unroll
+  for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int col = 32 * b + 8 * g + 4 * h;
+      const u32x4 v = {bits(acc[b][4 * g + 0]), bits(acc[b][4 * g + 1]), bits(acc[b][4 * g + 2]),
+                       bits(acc[b][4 * g + 3])};
+      bstore16(dst, (uint32_t)((row * D + col) * 4), v);
     }
 }
 

@@ -37,6 +37,12 @@ struct BwdArgs {
   bool bf16;
   const int* cu = nullptr;  // packed variable-length, as in FwdArgs
   int T = 0;
+  // Query heads of a key/value head's group split over `splits` dK/dV
+  // workgroups (splits divides H / Hkv), their float32 partial sums in
+  // `part` (2 * splits * R * d floats, R = rows of the K tensor); null: no
+  // split.
+  float* part = nullptr;
+  int splits = 1;
 };
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st);

@@ -99,6 +99,21 @@ def flops(w: Workload):
     return float(f), float(b), float(f + b)
 
 
+def visible_pairs(n: int, causal: bool, window=None) -> int:
+    """Query-key pairs a length-n sequence attends: key j visible to query i
+    iff i - left <= j <= i + right (-1: no bound), right capped at 0 by the
+    causal flag."""
+    import numpy as np
+
+    left, right = (-1, -1) if window is None else (int(window[0]), int(window[1]))
+    if causal:
+        right = 0 if right < 0 else min(right, 0)
+    i = np.arange(n, dtype=np.int64)
+    lo = np.zeros(n, dtype=np.int64) if left < 0 else np.maximum(0, i - left)
+    hi = np.full(n, n - 1, dtype=np.int64) if right < 0 else np.minimum(n - 1, i + right)
+    return int(np.maximum(hi - lo + 1, 0).sum())
+
+
 def kernel_flops(w: Workload, executed: bool = False):
     """Counted FLOPs attributed to each kernel (causal halved).
 

@@ -23,9 +23,10 @@
  * Scale        scale > 0 and finite; the caller passes 1/sqrt(d) for the
  *              usual attention ("flash-attn-triton" docs, "The argument").
  * Alignment    every pointer 16-byte aligned.
- * Ownership    the caller allocates and owns every buffer.  The library
- *              allocates no device memory, keeps no mutable global state and
- *              may be called from several host threads.
+ * Ownership    the caller allocates and owns every buffer, workspaces
+ *              included.  The library allocates no device memory, keeps no
+ *              mutable global state and may be called from several host
+ *              threads.
  * Streams      `stream` is a hipStream_t (NULL = the default stream).  Every
  *              call only enqueues kernels on that stream and returns; nothing
  *              synchronises.  Outputs are valid once the stream reaches them.
@@ -35,10 +36,13 @@
  *              Faults during execution surface at the caller's next
  *              synchronisation as HIP errors.  Outputs must not overlap
  *              inputs or each other (FA_ERR_ALIAS).
- * Determinism  no atomics: repeated calls on the same inputs give the same bits.
+ * Determinism  no atomics: repeated calls on the same inputs give the same bits
+ *              (the workspace forms: with the same workspace size).
  */
 #ifndef FA_MI355X_H
 #define FA_MI355X_H
+
+#include <stddef.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -199,6 +203,53 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* dO,
                   void* dv, const int* cu_seqlens, int B, int max_seqlen,
                   int T, int H, int Hkv, int d, float scale, int window_left,
                   int window_right, fa_dtype dt, void* stream);
+
+/*
+ * Workspace forms of the backward, for few key/value heads (multi-query and
+ * grouped-query attention with small Hkv).  The dK/dV kernel runs one
+ * workgroup per block of 128 keys of each key/value head, which loops over
+ * the H / Hkv query heads that share it; with few key/value heads that grid
+ * leaves compute units idle.  With a workspace the query heads of a group
+ * are split over S workgroups (S divides H / Hkv), each of which writes
+ * float32 partial sums of dK and dV into the workspace; a second kernel adds
+ * the S partials in a fixed order (split 0 first) and rounds them to dt.
+ * The operation and every rule are those of fa_bwd_ex and fa_bwd_varlen
+ * (the head axis of the gradient sums is the grouped-query form's, "flash
+ * attention" note, "Versions and Evolution"), plus:
+ *   workspace        device pointer, 16-byte aligned when used, owned by the
+ *                    caller; nothing in it is read before this call writes
+ *                    it (no clearing needed); it must not overlap any
+ *                    argument (FA_ERR_ALIAS).  Calls that share a workspace
+ *                    must be ordered on one stream.
+ *   workspace_bytes  its size.  The library takes S from its own rule (the
+ *                    smallest divisor of H / Hkv that brings the dK/dV grid
+ *                    to 2048 workgroups), then lowers S to the largest
+ *                    divisor that fits 2 * S * R * d * 4 bytes, R being the
+ *                    rows of the K tensor (B * Hkv * N batched, Hkv * T
+ *                    packed); S = 1 uses no workspace and gives the bits of
+ *                    the form without it.  NULL with workspace_bytes > 0 is
+ *                    FA_ERR_INVALID_ARG.
+ * dQ does not depend on S; dK and dV are deterministic for a given S.
+ *
+ * fa_bwd_workspace_size / fa_bwd_varlen_workspace_size return the bytes the
+ * rule asks for (0 when no split applies, including H = Hkv, or when the
+ * sizes are invalid); they touch no device.
+ */
+int fa_bwd_ex_ws(const void* q, const void* k, const void* v, const void* dO,
+                 const float* lse, const float* delta, void* dq, void* dk,
+                 void* dv, int B, int H, int Hkv, int N, int d, float scale,
+                 int window_left, int window_right, fa_dtype dt,
+                 void* workspace, size_t workspace_bytes, void* stream);
+int fa_bwd_varlen_ws(const void* q, const void* k, const void* v,
+                     const void* dO, const float* lse, const float* delta,
+                     void* dq, void* dk, void* dv, const int* cu_seqlens,
+                     int B, int max_seqlen, int T, int H, int Hkv, int d,
+                     float scale, int window_left, int window_right,
+                     fa_dtype dt, void* workspace, size_t workspace_bytes,
+                     void* stream);
+size_t fa_bwd_workspace_size(int B, int H, int Hkv, int N, int d);
+size_t fa_bwd_varlen_workspace_size(int B, int max_seqlen, int T, int H,
+                                    int Hkv, int d);
 
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* fa_status_string(int status);

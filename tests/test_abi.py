@@ -35,6 +35,8 @@ def test_header_functions_are_exported():
                             "fa_fwd_gqa", "fa_bwd_gqa", "fa_bwd_dkdv_gqa", "fa_bwd_dq_gqa",
                             "fa_fwd_ex", "fa_bwd_ex", "fa_bwd_dkdv_ex", "fa_bwd_dq_ex",
                             "fa_fwd_varlen", "fa_bwd_varlen",
+                            "fa_bwd_ex_ws", "fa_bwd_varlen_ws", "fa_bwd_workspace_size",
+                            "fa_bwd_varlen_workspace_size",
                             "fa_status_string", "fa_version"])
     out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (fa_\w+)$", out, flags=re.M))
@@ -223,3 +225,42 @@ def test_every_kernel_launch_stub_is_defined():
     out = subprocess.run(["nm", "-D", binding.LIB_PATH], capture_output=True, text=True).stdout
     missing = [line for line in out.splitlines() if " U " in line and "device_stub" in line]
     assert not missing, missing[:3]
+
+
+def test_workspace_forms_reject(p):
+    # fa_bwd_ex_ws(q, k, v, dO, lse, delta, dq, dk, dv, B, H, Hkv, N, d, scale, wl, wr, dt, ws, ws_bytes, stream)
+    def f(ws, nbytes, B=1, H=8, Hkv=1, N=64, d=32):
+        return lib.fa_bwd_ex_ws(*p[:9], B, H, Hkv, N, d, 0.125, -1, 0, 1, ws, nbytes, None)
+
+    need = binding.fa_bwd_workspace_size(1, 8, 1, 64, 32)
+    assert need == 2 * 8 * 64 * 32 * 4  # one key block: all 8 heads split, dK and dV float32 partials
+    assert f(None, 16) == INVALID  # bytes without a pointer
+    assert f(p[9] + 8, need) == ALIGN  # a workspace the split would use must be 16-byte aligned
+    assert f(p[0], need) == ALIAS  # over q
+    assert f(p[9], need, Hkv=3) == INVALID  # 8 heads are not a multiple of 3
+    assert f(p[9], need, d=48) == UNSUPPORTED
+    # fa_bwd_varlen_ws(..., cu, B, max_seqlen, T, H, Hkv, d, scale, wl, wr, dt, ws, ws_bytes, stream)
+    vneed = binding.fa_bwd_varlen_workspace_size(2, 32, 64, 8, 1, 32)
+    assert vneed == 2 * 8 * 64 * 32 * 4
+    assert lib.fa_bwd_varlen_ws(*p[:9], p[10], 2, 32, 64, 8, 1, 32, 0.125, -1, 0, 1, None, 16, None) == INVALID
+    assert lib.fa_bwd_varlen_ws(*p[:9], p[10], 2, 32, 64, 8, 1, 32, 0.125, -1, 0, 1, p[3], vneed, None) == ALIAS
+
+
+def test_workspace_size_rule():
+    ws = binding.fa_bwd_workspace_size
+    assert ws(2, 16, 16, 8192, 128) == 0  # no grouping: nothing to split
+    assert ws(1, 4, 3, 64, 64) == 0 and ws(0, 4, 1, 64, 64) == 0 and ws(1, 4, 1, 64, 48) == 0  # invalid
+    # 64 key blocks x 2 batches x 4 kv heads = 512 workgroups: 4 splits reach 2048
+    assert ws(2, 16, 4, 8192, 128) == 2 * 4 * (2 * 4 * 8192) * 128 * 4
+    # 1024 workgroups: 2 splits
+    assert ws(2, 16, 8, 8192, 128) == 2 * 2 * (2 * 8 * 8192) * 128 * 4
+    # 128 workgroups: all 16 heads split, 2048
+    assert ws(2, 16, 1, 8192, 128) == 2 * 16 * (2 * 8192) * 128 * 4
+    # split counts are divisors of the group, at most the group: 12 heads, 100 workgroups -> 12
+    assert ws(1, 12, 1, 12800, 64) == 2 * 12 * 12800 * 64 * 4
+    # groups of 3 heads, 2 kv heads x 200 key blocks = 400 workgroups: at most 3 splits
+    assert ws(1, 6, 2, 25600, 32) == 2 * 3 * (2 * 25600) * 32 * 4
+    # enough workgroups already: no split
+    assert ws(8, 32, 8, 8192, 128) == 0
+    # 24 sequences x 32 key blocks of the longest = 768 workgroups: 4 splits
+    assert binding.fa_bwd_varlen_workspace_size(24, 4077, 55662, 16, 1, 128) == 2 * 4 * 55662 * 128 * 4

@@ -1,6 +1,7 @@
 """Host-side logic of bench.py, on the CPU: the multi-GPU refusal, the
 staleness rule for counter summaries, the summary parsers, the --results
-file, and the ordinary-attention footprint probe's size arithmetic."""
+file, the ordinary-attention footprint probe's size arithmetic, and the
+exact visible-pair count the wider forms are priced with."""
 
 import json
 import os
@@ -12,6 +13,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 import bench  # noqa: E402
+from exact_io_aware_30_amd import workloads  # noqa: E402
 
 
 def test_more_than_one_gpu_is_refused():
@@ -102,3 +104,33 @@ def test_ordinary_comparator_math_on_the_cpu(causal):
     ref = oracle.attention_backward(*(x.double().numpy() for x in (q, k, v, do)), 0.25, causal)
     for name, t in (("o", o), ("dq", dq), ("dk", dk), ("dv", dv)):
         np.testing.assert_allclose(t.double().numpy(), ref[name], rtol=1e-4, atol=1e-5, err_msg=name)
+
+
+def _pairs_brute(n, causal, window):
+    left, right = (-1, -1) if window is None else window
+    count = 0
+    for i in range(n):
+        for j in range(n):
+            if causal and j > i:
+                continue
+            if left >= 0 and j < i - left:
+                continue
+            if right >= 0 and j > i + right:
+                continue
+            count += 1
+    return count
+
+
+@pytest.mark.parametrize("n", [1, 2, 7, 64, 133])
+@pytest.mark.parametrize("causal,window", [(False, None), (True, None), (False, (3, 0)), (True, (5, 9)),
+                                           (False, (4, 4)), (False, (0, 0)), (True, (-1, 2)), (False, (200, -1))])
+def test_visible_pairs_matches_brute_force(n, causal, window):
+    assert workloads.visible_pairs(n, causal, window) == _pairs_brute(n, causal, window)
+
+
+def test_visible_pairs_closed_forms():
+    n = 8192
+    assert workloads.visible_pairs(n, True) == n * (n + 1) // 2
+    assert workloads.visible_pairs(n, False) == n * n
+    w = 1024  # left window w, causal: row i sees min(i, w) + 1 keys
+    assert workloads.visible_pairs(n, False, (w, 0)) == sum(min(i, w) + 1 for i in range(n))
