@@ -144,12 +144,25 @@ struct VLds {
 
 // The three phases of one query tile of the dK/dV kernels for one wave.
 // Phase 1 (MFMA): S^T and dP^T of the tile (lane = key, registers = query).
+// The V operand is negated (the workgroup's V rows are stored with their
+// signs flipped) and the dP^T accumulator starts from the tile's D values,
+// so the MFMAs leave D - dP, and dS = P (dP - D) is -(P (D - dP)): the sign
+// is carried into the final dK scale.  st + kStatsRows holds the tile's D.
 template <class T, int D, int NA, class VOp>
 __device__ __forceinline__ void dkdv_scores(const lds_char* qt, const lds_char* dot, const u32x4* kf, const VOp& vop,
-                                            f32x16* s, f32x16* dp, int lane) {
+                                            const float* st, f32x16* s, f32x16* dp, int lane) {
   constexpr int NKK = D / 16;
+  const int h = lane >> 5;
 #pragma unroll
-  for (int a = 0; a < NA; ++a) s[a] = dp[a] = (f32x16){};
+  for (int a = 0; a < NA; ++a) {
+    s[a] = (f32x16){};
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 dd = *(const f32x4*)(st + kStatsRows + 32 * a + 8 * g + 4 * h);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dp[a][4 * g + e] = dd[e];
+    }
+  }
   prio_mfma_begin();
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk)
@@ -167,8 +180,8 @@ __device__ __forceinline__ void dkdv_scores(const lds_char* qt, const lds_char* 
 
 // Phase 2 (VALU): mask (only when `edge`: the tile crosses an edge of the
 // window of some of the wave's keys), P = 2^(S c - L log2 e),
-// dS = P (dP - D), packed into MFMA operands.  st holds the tile's L
-// (st[0..63]) and D (st[64..127]).
+// -dS = P (D - dP) from the accumulator, packed into MFMA operands.  st holds
+// the tile's L (st[0..63]) and D (st[64..127]).
 template <class T, int NA>
 __device__ __forceinline__ void dkdv_probs(f32x16* s, f32x16* dp, const float* st, u32x4* pf, u32x4* dsf, bool edge,
                                            int i0, int krow, Win win, float c, int lane) {
@@ -192,13 +205,12 @@ __device__ __forceinline__ void dkdv_probs(f32x16* s, f32x16* dp, const float* s
     for (int g = 0; g < 4; ++g) {
       const int qi = 32 * a + 8 * g + 4 * h;
       const f32x4 l2 = *(const f32x4*)(st + qi) * kLog2e;
-      const f32x4 dd = *(const f32x4*)(st + kStatsRows + qi);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * g + e;
         const float p = exp2_fast(__builtin_fmaf(s[a][r], c, -l2[e]));
         s[a][r] = p;
-        dp[a][r] = p * (dp[a][r] - dd[e]);
+        dp[a][r] = p * dp[a][r];
       }
     }
 #pragma unroll
@@ -235,7 +247,7 @@ __device__ __forceinline__ void dkdv_tile(const lds_char* qt, const lds_char* do
                                           Win win, float c, int lane) {
   f32x16 s[NA], dp[NA];
   u32x4 pf[2 * NA], dsf[2 * NA];
-  dkdv_scores<T, D, NA>(qt, dot, kf, vop, s, dp, lane);
+  dkdv_scores<T, D, NA>(qt, dot, kf, vop, st, s, dp, lane);
   dkdv_probs<T, NA>(s, dp, st, pf, dsf, edge, i0, krow, win, c, lane);
   dkdv_accum<T, D, NA>(qt, dot, pf, dsf, dka, dva, lane);
 }
@@ -347,7 +359,7 @@ __device__ __forceinline__ void dkdv_run(lds_char* lds, int nt, int i_start, con
     store_rows_f32<D>(make_rsrc(rdk, (uint32_t)N * D * 4), krow, dka, lane);
     store_rows_f32<D>(make_rsrc(rdv, (uint32_t)N * D * 4), krow, dva, lane);
   } else {
-    store_rows<T, D>(rdk, krow, dka, scale, lane);
+    store_rows<T, D>(rdk, krow, dka, -scale, lane);  // dka holds -dK / scale
     store_rows<T, D>(rdv, krow, dva, 1.0f, lane);
   }
 }
@@ -444,6 +456,19 @@ __global__ __launch_bounds__(64 * kBwdWaves, Dkdv<D>::kOcc) void dkdv_kernel(
   for (int kk = 0; kk < NKK; ++kk) {
     land(kf[kk]);
     if constexpr (!VL) land(vf[kk]);
+  }
+  // The signs of the workgroup's V rows flipped once (exact), for the
+  // dP^T accumulation that starts from D (dkdv_scores).
+  if constexpr (VL) {
+    // Every wave's share of the V tile landed before its K loads; after the
+    // barrier each lane flips 16-byte chunks of the whole tile, and the
+    // ring's first barrier (after an lgkmcnt(0) wait) publishes them.
+    __builtin_amdgcn_s_barrier();
+    lds_u32x4* const v4 = (lds_u32x4*)vt;
+    for (int i = tid; i < VTILE / 16; i += 64 * NW) v4[i] ^= kSignBits16;
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) vf[kk] ^= kSignBits16;
   }
   {
     const Rsrc rq = make_rsrc_words((const char*)qp + head0, bytes);
@@ -825,8 +850,9 @@ static hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t st) {
                      a.lse, a.delta, a.dk, a.dv, a.part, GS, geo, BHkv, Win{a.wl, a.wr}, a.scale * kLog2e, a.scale);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  // The partials hold -dK / scale (the dK/dV kernel's sign convention).
   hipLaunchKernelGGL((dkdv_reduce_kernel<T, D>), dim3(nkb * BHkv), dim3(256), 0, st, a.part, a.dk, a.dv, GS, geo,
-                     BHkv, a.scale);
+                     BHkv, -a.scale);
   return hipGetLastError();
 }
 

@@ -145,6 +145,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
+// Sign bits of the two 16-bit elements in each dword (fp16 and bf16 alike):
+// XOR negates every element exactly.
+constexpr u32x4 kSignBits16 = {0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
 __device__ __forceinline__ void bstore8(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 v) {
   __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
 }
