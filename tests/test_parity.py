@@ -198,6 +198,39 @@ def test_deterministic_and_split_calls_match():
     assert torch.equal(dk, dk2) and torch.equal(dv, dv2) and torch.equal(dq, dq2)
 
 
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_inputs_are_read_only(d):
+    """No entry point writes to its inputs: the dK/dV kernel works on a copy
+    of V with its signs flipped in LDS (or in registers), never on V itself;
+    the grouped-query split path and the packed form included."""
+    w = wl.Workload("readonly", "bf16", 2, 4, 333, d, True, 1.0, 4100 + d)
+    say(f"[parity] {w.describe()}: inputs unchanged")
+    b = _binding()
+    q, k, v, do = (x.cuda() for x in wl.make_inputs(w))
+    kg, vg = k[:, :1].contiguous(), v[:, :1].contiguous()  # one key/value head: the head split
+    snap = [x.clone() for x in (q, k, v, do, kg, vg)]
+    o, lse = b.attention_forward(q, k, v, w.scale, True)
+    lse_s, o_s = lse.clone(), o.clone()
+    dq, dk, dv, delta = b.attention_backward(q, k, v, o, do, lse, w.scale, True)
+    delta_s = delta.clone()
+    b.fa_bwd(q, k, v, do, lse, delta, dq, dk, dv, w.scale, True)
+    og, lg = b.attention_forward(q, kg, vg, w.scale, True)
+    assert b.fa_bwd_workspace_size(2, 4, 1, 333, d) > 0
+    b.attention_backward(q, kg, vg, og, do, lg, w.scale, True)
+    T = 2 * 333
+    cu = torch.tensor([0, 333, T], dtype=torch.int32, device="cuda")
+    qp, kp, vp, dop = (x.transpose(0, 1).reshape(4, T, d).contiguous() for x in (q, k, v, do))
+    snap_p = [x.clone() for x in (qp, kp, vp, dop, cu)]
+    op, lp = b.attention_forward_varlen(qp, kp, vp, cu, 333, w.scale, True)
+    b.attention_backward_varlen(qp, kp, vp, op, dop, lp, cu, 333, w.scale, True)
+    torch.cuda.synchronize()
+    for before, after in zip(snap, (q, k, v, do, kg, vg)):
+        assert torch.equal(before, after), "an input was modified"
+    for before, after in zip(snap_p, (qp, kp, vp, dop, cu)):
+        assert torch.equal(before, after), "a packed input was modified"
+    assert torch.equal(lse, lse_s) and torch.equal(o, o_s) and torch.equal(delta, delta_s)
+
+
 def test_side_stream():
     w = wl.Workload("stream", "fp16", 1, 4, 640, 64, False, 1.0, 4242)
     say(f"[parity] {w.describe()} on a side stream")
