@@ -12,7 +12,9 @@ both halved under the causal mask.
                                 calls after 10 warm-up calls, min and max),
                                 device-memory growth, and the oracle on one
                                 head of each (a markdown table, then one JSON
-                                line per workload)
+                                line per workload), then the forward's MFMA
+                                and vector-ALU ceilings per head dimension
+                                from rates measured by libfa_probe.so
     python bench.py --sweep     bf16 causal d=128, B=1, H=16, N = 1K .. 64K:
                                 one pass of each kernel per N (for hardware
                                 counters) and its time
@@ -222,6 +224,61 @@ def report():
               f"| {r['device_memory_growth_bytes']} B | {r['oracle_one_head_s']} s ({r['oracle_tflops']} TF/s) |")
     for r in rows:
         emit(r)
+    ceilings(rows)
+
+
+PROBE_LIBRARY = os.path.join(ROOT, "exact_io_aware_30_amd", "libfa_probe.so")
+
+
+def probe_rates():
+    """Instruction rates measured on the GPU by libfa_probe.so: dense bf16
+    MFMA TFLOP/s, v_exp_f32 and v_fma_f32 lane-results per second, and the
+    forward's per-score vector sequence in scores per second (1e12 units)."""
+    import ctypes
+
+    import torch
+
+    lib = ctypes.CDLL(PROBE_LIBRARY)
+    lib.fa_probe_rates.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.c_int, ctypes.c_void_p]
+    lib.fa_probe_rates.restype = ctypes.c_int
+    out = (ctypes.c_double * 5)()
+    rc = lib.fa_probe_rates(out, 5, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    if rc != 0:
+        raise RuntimeError(f"fa_probe_rates failed (status {rc})")
+    return {"mfma_bf16_tflops": out[0], "exp_tlanes_per_s": out[1], "fma_tlanes_per_s": out[2],
+            "softmax_tscores_per_s": out[3], "compute_units": int(out[4])}
+
+
+def forward_ceilings(rates, d: int):
+    """Forward TFLOP/s ceilings at head dimension d from measured rates: the
+    matrix core alone; the vector ALU alone (each score carries 4 d counted
+    FLOPs and needs the per-score sequence: scale-and-subtract, exponential,
+    row-sum add, half a max3, half a pack; the kernel adds address and mask
+    work, so this bound is optimistic); and both executed one after the
+    other, which is how the kernels' counters show them running."""
+    mfma = float(rates["mfma_bf16_tflops"])
+    valu = 4.0 * d * float(rates["softmax_tscores_per_s"])
+    return {"d": d, "mfma_tflops": mfma, "valu_tflops": valu, "serial_tflops": 1.0 / (1.0 / mfma + 1.0 / valu)}
+
+
+def ceilings(rows=()):
+    """Measured ceilings beside the measured forward of each workload."""
+    rates = probe_rates()
+    print(f"\nceilings (measured on this GPU, {rates['compute_units']} CUs): dense bf16 MFMA "
+          f"{rates['mfma_bf16_tflops']:.0f} TFLOP/s; v_exp_f32 {rates['exp_tlanes_per_s']:.1f}e12/s; "
+          f"v_fma_f32 {rates['fma_tlanes_per_s']:.1f}e12/s; forward per-score sequence "
+          f"{rates['softmax_tscores_per_s']:.2f}e12 scores/s")
+    print("| d | MFMA ceiling TF/s | VALU ceiling TF/s | both in series TF/s | measured forward TF/s |")
+    print("|---|---|---|---|---|")
+    out = []
+    for d in (32, 64, 128):
+        c = forward_ceilings(rates, d)
+        meas = ", ".join(f"{r['fwd_tflops']} ({r['workload'].split(':')[0]})" for r in rows
+                         if f",d={d}]" in r["workload"])
+        print(f"| {d} | {c['mfma_tflops']:.0f} | {c['valu_tflops']:.0f} | {c['serial_tflops']:.0f} | {meas or '-'} |")
+        out.append({k: (round(v, 1) if isinstance(v, float) else v) for k, v in c.items()})
+    emit({"probe_rates": {k: (round(v, 3) if isinstance(v, float) else v) for k, v in rates.items()},
+          "forward_ceilings": out})
 
 
 SWEEP_N = (1024, 2048, 4096, 8192, 16384, 32768, 65536)

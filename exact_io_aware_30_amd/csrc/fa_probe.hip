@@ -1,0 +1,129 @@
+// Instruction-rate microbenchmarks (see include/fa_probe.h).  Four loops,
+// one workgroup of 512 lanes per compute unit, each writing one float per
+// lane so that nothing is optimised away.
+#include "../../include/fa_probe.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 512;  // 8 waves: 2 per SIMD
+constexpr int kRegs = 16;      // independent chains per lane in the VALU loops
+
+enum Kind { kMfma = 0, kExp = 1, kFma = 2, kSoftmax = 3 };
+
+template <int KIND>
+__global__ __launch_bounds__(kThreads) void probe_kernel(float* out, int iters, float c) {
+  const int tid = threadIdx.x;
+  float r = 0.f;
+  if constexpr (KIND == kMfma) {
+    bf16x8 a, b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      a[i] = (__bf16)(1e-3f * (tid + i));
+      b[i] = (__bf16)(1e-3f * (tid - i));
+    }
+    f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    for (int it = 0; it < iters; ++it) {
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) r += c0[i] + c1[i] + c2[i] + c3[i];
+  } else {
+    float x[kRegs];
+#pragma unroll
+    for (int j = 0; j < kRegs; ++j) x[j] = -1e-3f * (tid + j);
+    float sum = 0.f, mx = -1e30f;
+    unsigned pk = 0;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int j = 0; j < kRegs; ++j) {
+        if constexpr (KIND == kExp) {
+          x[j] = __builtin_amdgcn_exp2f(-__builtin_fabsf(x[j]));  // stays in (0, 1]
+        } else if constexpr (KIND == kFma) {
+          x[j] = __builtin_fmaf(x[j], c, -c);
+        } else {
+          // one score: scale and subtract the reference, exponential, row sum;
+          // every second score: a max3 of the pair and a bf16 pack of the pair
+          x[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[j], c, -c));
+          sum += x[j];
+          if (j & 1) {
+            mx = fmaxf(mx, fmaxf(x[j - 1], x[j]));
+            pk ^= __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){x[j - 1], x[j]}, bf16x2));
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kRegs; ++j) r += x[j];
+    r += sum + mx + (float)(pk & 0xff);
+  }
+  out[blockIdx.x * kThreads + tid] = r;
+}
+
+template <int KIND>
+hipError_t time_kernel(float* out, int grid, int iters, hipStream_t st, float* best_ms) {
+  hipEvent_t e0, e1;
+  hipError_t err = hipEventCreate(&e0);
+  if (err != hipSuccess) return err;
+  if ((err = hipEventCreate(&e1)) != hipSuccess) {
+    (void)hipEventDestroy(e0);
+    return err;
+  }
+  hipLaunchKernelGGL((probe_kernel<KIND>), dim3(grid), dim3(kThreads), 0, st, out, iters, 0.5f);  // warm-up
+  float best = 1e30f;
+  for (int rep = 0; rep < 3 && err == hipSuccess; ++rep) {
+    err = hipEventRecord(e0, st);
+    if (err == hipSuccess) {
+      hipLaunchKernelGGL((probe_kernel<KIND>), dim3(grid), dim3(kThreads), 0, st, out, iters, 0.5f);
+      err = hipGetLastError();
+    }
+    if (err == hipSuccess) err = hipEventRecord(e1, st);
+    if (err == hipSuccess) err = hipEventSynchronize(e1);
+    float ms = 0.f;
+    if (err == hipSuccess) err = hipEventElapsedTime(&ms, e0, e1);
+    if (err == hipSuccess) best = std::min(best, ms);
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  *best_ms = best;
+  return err;
+}
+
+}  // namespace
+
+extern "C" int fa_probe_rates(double* out, int n, void* stream) {
+  if (!out || n < 5) return -1;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -4;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) return -4;
+  float* buf = nullptr;
+  if (hipMalloc(&buf, (size_t)cus * kThreads * sizeof(float)) != hipSuccess) return -4;
+  // Iteration counts give each loop a few milliseconds.
+  const int it_mfma = 20000, it_valu = 4000;
+  float ms[4] = {0, 0, 0, 0};
+  hipError_t err = time_kernel<kMfma>(buf, cus, it_mfma, st, &ms[0]);
+  if (err == hipSuccess) err = time_kernel<kExp>(buf, cus, it_valu, st, &ms[1]);
+  if (err == hipSuccess) err = time_kernel<kFma>(buf, cus, it_valu, st, &ms[2]);
+  if (err == hipSuccess) err = time_kernel<kSoftmax>(buf, cus, it_valu, st, &ms[3]);
+  (void)hipFree(buf);
+  if (err != hipSuccess) return -4;
+  const double waves = (double)cus * (kThreads / 64), lanes = (double)cus * kThreads;
+  out[0] = waves * it_mfma * 4 * 32768.0 / (ms[0] * 1e-3) / 1e12;
+  out[1] = lanes * it_valu * kRegs / (ms[1] * 1e-3) / 1e12;
+  out[2] = lanes * it_valu * kRegs / (ms[2] * 1e-3) / 1e12;
+  out[3] = lanes * it_valu * kRegs / (ms[3] * 1e-3) / 1e12;
+  out[4] = cus;
+  return 0;
+}

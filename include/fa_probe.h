@@ -1,0 +1,41 @@
+/*
+ * fa_probe.h -- instruction-rate microbenchmarks of the MI355X (gfx950) the
+ * attention kernels run on.  Measurement support, not part of the attention
+ * path: libfa_probe.so is built beside libfa_mi355x.so and only the
+ * benchmark calls it.
+ *
+ * The forward spends, per score element, one FMA (scale and subtract the
+ * running maximum), one exponential, one add (row sum), half a max3 (row
+ * maximum) and half a bf16 pack on the vector ALU, beside 4 d FLOPs of MFMA
+ * work ("flash-attn-triton" docs, Fig. 3: the per-tile update).  At small d
+ * that vector work, not the matrix core, bounds the kernel; these loops
+ * measure both rates on the box instead of assuming them.
+ */
+#ifndef FA_PROBE_H
+#define FA_PROBE_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * fa_probe_rates -- runs four loops on every compute unit (one workgroup of
+ * 8 waves per CU, 2 waves per SIMD), each timed with HIP events on `stream`
+ * (NULL = the default stream; the call synchronises with it), best of three:
+ *   out[0]  dense bf16 MFMA rate, TFLOP/s (v_mfma_f32_32x32x16_bf16, four
+ *           independent accumulators per wave)
+ *   out[1]  v_exp_f32 rate, 1e12 lane-results per second
+ *   out[2]  v_fma_f32 rate, 1e12 lane-results per second
+ *   out[3]  the forward's per-score vector sequence above, 1e12 scores/s
+ *   out[4]  compute units used
+ * n is the number of doubles out can hold (at least 5).  The probe kernels
+ * touch no memory but one float per lane written to a buffer the call
+ * allocates and frees.  Returns 0, -1 for a bad argument, -4 for a HIP error.
+ */
+int fa_probe_rates(double* out, int n, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_PROBE_H */

@@ -264,3 +264,23 @@ def test_workspace_size_rule():
     assert ws(8, 32, 8, 8192, 128) == 0
     # 24 sequences x 32 key blocks of the longest = 768 workgroups: 4 splits
     assert binding.fa_bwd_varlen_workspace_size(24, 4077, 55662, 16, 1, 128) == 2 * 4 * 55662 * 128 * 4
+
+
+def test_probe_library_exports_and_rejects():
+    """libfa_probe.so (measurement support) exports what include/fa_probe.h
+    declares, and rejects bad arguments before touching the GPU."""
+    import ctypes
+
+    from exact_io_aware_30_amd.build import PROBE_LIB_PATH
+
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(os.path.dirname(HEADER), "fa_probe.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
+    assert names == ["fa_probe_rates"]
+    out = subprocess.run(["nm", "-D", "--defined-only", PROBE_LIB_PATH], capture_output=True, text=True).stdout
+    assert set(names) <= set(re.findall(r"\bT (fa_\w+)$", out, flags=re.M))
+    lib = ctypes.CDLL(PROBE_LIB_PATH)
+    lib.fa_probe_rates.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.c_int, ctypes.c_void_p]
+    lib.fa_probe_rates.restype = ctypes.c_int
+    buf = (ctypes.c_double * 5)()
+    assert lib.fa_probe_rates(None, 5, None) == -1
+    assert lib.fa_probe_rates(buf, 4, None) == -1

@@ -134,3 +134,13 @@ def test_visible_pairs_closed_forms():
     assert workloads.visible_pairs(n, False) == n * n
     w = 1024  # left window w, causal: row i sees min(i, w) + 1 keys
     assert workloads.visible_pairs(n, False, (w, 0)) == sum(min(i, w) + 1 for i in range(n))
+
+
+def test_forward_ceilings_arithmetic():
+    rates = {"mfma_bf16_tflops": 2000.0, "softmax_tscores_per_s": 4.0}
+    c = bench.forward_ceilings(rates, 128)
+    assert c["valu_tflops"] == pytest.approx(4 * 128 * 4.0)  # 4 d FLOPs per score
+    assert c["serial_tflops"] == pytest.approx(1 / (1 / 2000.0 + 1 / 2048.0))
+    assert bench.forward_ceilings(rates, 32)["valu_tflops"] == pytest.approx(c["valu_tflops"] / 4)
+    # in series the pair is slower than either alone
+    assert c["serial_tflops"] < min(c["mfma_tflops"], c["valu_tflops"])

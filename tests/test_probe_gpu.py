@@ -1,0 +1,25 @@
+"""The instruction-rate probes behind the benchmark's ceilings, on the GPU:
+every rate positive and in a range the MI355X can reach (dense bf16 MFMA
+under the published 2.5 PFLOP/s; an exponential no faster than an FMA; the
+per-score sequence, which holds an exponential and several other vector
+instructions, slower than either)."""
+
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def test_probe_rates_are_plausible():
+    r = bench.probe_rates()
+    print(r, flush=True)
+    assert r["compute_units"] >= 1
+    assert 200.0 < r["mfma_bf16_tflops"] < 2600.0
+    assert 0 < r["exp_tlanes_per_s"] <= r["fma_tlanes_per_s"] * 1.05
+    assert 0 < r["softmax_tscores_per_s"] < r["exp_tlanes_per_s"]
