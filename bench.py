@@ -241,12 +241,20 @@ def probe_rates():
     lib = ctypes.CDLL(PROBE_LIBRARY)
     lib.fa_probe_rates.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.c_int, ctypes.c_void_p]
     lib.fa_probe_rates.restype = ctypes.c_int
-    out = (ctypes.c_double * 5)()
-    rc = lib.fa_probe_rates(out, 5, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    out = (ctypes.c_double * 8)()
+    rc = lib.fa_probe_rates(out, 8, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
     if rc != 0:
         raise RuntimeError(f"fa_probe_rates failed (status {rc})")
     return {"mfma_bf16_tflops": out[0], "exp_tlanes_per_s": out[1], "fma_tlanes_per_s": out[2],
-            "softmax_tscores_per_s": out[3], "compute_units": int(out[4])}
+            "softmax_tscores_per_s": out[3], "compute_units": int(out[4]),
+            "pair_mfma_ms": out[5], "pair_valu_ms": out[6], "pair_both_ms": out[7],
+            "pair_overlap": overlap_fraction(out[5], out[6], out[7])}
+
+
+def overlap_fraction(t_mfma: float, t_valu: float, t_both: float) -> float:
+    """Share of the shorter half's time hidden under the longer one when both
+    run interleaved: 0 = executed one after the other, 1 = fully hidden."""
+    return (t_mfma + t_valu - t_both) / min(t_mfma, t_valu)
 
 
 def forward_ceilings(rates, d: int):
@@ -267,7 +275,10 @@ def ceilings(rows=()):
     print(f"\nceilings (measured on this GPU, {rates['compute_units']} CUs): dense bf16 MFMA "
           f"{rates['mfma_bf16_tflops']:.0f} TFLOP/s; v_exp_f32 {rates['exp_tlanes_per_s']:.1f}e12/s; "
           f"v_fma_f32 {rates['fma_tlanes_per_s']:.1f}e12/s; forward per-score sequence "
-          f"{rates['softmax_tscores_per_s']:.2f}e12 scores/s")
+          f"{rates['softmax_tscores_per_s']:.2f}e12 scores/s; an interleaved loop of one MFMA per two scores' "
+          f"vector work runs in {rates['pair_both_ms']:.3f} ms against {rates['pair_mfma_ms']:.3f} (MFMAs alone) and "
+          f"{rates['pair_valu_ms']:.3f} (vector work alone): {100 * rates['pair_overlap']:.0f}% of the shorter half "
+          f"hidden")
     print("| d | MFMA ceiling TF/s | VALU ceiling TF/s | both in series TF/s | measured forward TF/s |")
     print("|---|---|---|---|---|")
     out = []

@@ -17,13 +17,56 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 constexpr int kThreads = 512;  // 8 waves: 2 per SIMD
 constexpr int kRegs = 16;      // independent chains per lane in the VALU loops
 
-enum Kind { kMfma = 0, kExp = 1, kFma = 2, kSoftmax = 3 };
+enum Kind { kMfma = 0, kExp = 1, kFma = 2, kSoftmax = 3, kPairMfma = 4, kPairValu = 5, kPair = 6 };
+
+// One score of the forward's per-score vector sequence on chain x; every
+// second score also a max3 and a bf16 pack of the pair.
+__device__ __forceinline__ void score_step(float* x, int j, float c, float& sum, float& mx, unsigned& pk) {
+  x[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[j], c, -c));
+  sum += x[j];
+  if (j & 1) {
+    mx = fmaxf(mx, fmaxf(x[j - 1], x[j]));
+    pk ^= __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){x[j - 1], x[j]}, bf16x2));
+  }
+}
 
 template <int KIND>
 __global__ __launch_bounds__(kThreads) void probe_kernel(float* out, int iters, float c) {
   const int tid = threadIdx.x;
   float r = 0.f;
-  if constexpr (KIND == kMfma) {
+  if constexpr (KIND >= kPairMfma) {
+    // The interleaved pair: per step one MFMA (on one of four accumulators)
+    // and the per-score sequence of two scores, in issue order; kPairMfma
+    // and kPairValu run one half of it alone.
+    bf16x8 a, b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      a[i] = (__bf16)(1e-3f * (tid + i));
+      b[i] = (__bf16)(1e-3f * (tid - i));
+    }
+    f32x16 acc[4] = {};
+    float x[kRegs];
+#pragma unroll
+    for (int j = 0; j < kRegs; ++j) x[j] = -1e-3f * (tid + j);
+    float sum = 0.f, mx = -1e30f;
+    unsigned pk = 0;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int k = 0; k < kRegs / 2; ++k) {
+        if constexpr (KIND != kPairValu) acc[k & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[k & 3], 0, 0, 0);
+        if constexpr (KIND != kPairMfma) {
+          score_step(x, 2 * k, c, sum, mx, pk);
+          score_step(x, 2 * k + 1, c, sum, mx, pk);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kRegs; ++j) r += x[j];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) r += acc[0][i] + acc[1][i] + acc[2][i] + acc[3][i];
+    r += sum + mx + (float)(pk & 0xff);
+  } else if constexpr (KIND == kMfma) {
     bf16x8 a, b;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -53,14 +96,7 @@ __global__ __launch_bounds__(kThreads) void probe_kernel(float* out, int iters, 
         } else if constexpr (KIND == kFma) {
           x[j] = __builtin_fmaf(x[j], c, -c);
         } else {
-          // one score: scale and subtract the reference, exponential, row sum;
-          // every second score: a max3 of the pair and a bf16 pack of the pair
-          x[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[j], c, -c));
-          sum += x[j];
-          if (j & 1) {
-            mx = fmaxf(mx, fmaxf(x[j - 1], x[j]));
-            pk ^= __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){x[j - 1], x[j]}, bf16x2));
-          }
+          score_step(x, j, c, sum, mx, pk);
         }
       }
     }
@@ -103,7 +139,7 @@ hipError_t time_kernel(float* out, int grid, int iters, hipStream_t st, float* b
 }  // namespace
 
 extern "C" int fa_probe_rates(double* out, int n, void* stream) {
-  if (!out || n < 5) return -1;
+  if (!out || n < 8) return -1;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -4;
@@ -112,11 +148,14 @@ extern "C" int fa_probe_rates(double* out, int n, void* stream) {
   if (hipMalloc(&buf, (size_t)cus * kThreads * sizeof(float)) != hipSuccess) return -4;
   // Iteration counts give each loop a few milliseconds.
   const int it_mfma = 20000, it_valu = 4000;
-  float ms[4] = {0, 0, 0, 0};
+  float ms[7] = {0, 0, 0, 0, 0, 0, 0};
   hipError_t err = time_kernel<kMfma>(buf, cus, it_mfma, st, &ms[0]);
   if (err == hipSuccess) err = time_kernel<kExp>(buf, cus, it_valu, st, &ms[1]);
   if (err == hipSuccess) err = time_kernel<kFma>(buf, cus, it_valu, st, &ms[2]);
   if (err == hipSuccess) err = time_kernel<kSoftmax>(buf, cus, it_valu, st, &ms[3]);
+  if (err == hipSuccess) err = time_kernel<kPairMfma>(buf, cus, it_valu, st, &ms[4]);
+  if (err == hipSuccess) err = time_kernel<kPairValu>(buf, cus, it_valu, st, &ms[5]);
+  if (err == hipSuccess) err = time_kernel<kPair>(buf, cus, it_valu, st, &ms[6]);
   (void)hipFree(buf);
   if (err != hipSuccess) return -4;
   const double waves = (double)cus * (kThreads / 64), lanes = (double)cus * kThreads;
@@ -125,5 +164,8 @@ extern "C" int fa_probe_rates(double* out, int n, void* stream) {
   out[2] = lanes * it_valu * kRegs / (ms[2] * 1e-3) / 1e12;
   out[3] = lanes * it_valu * kRegs / (ms[3] * 1e-3) / 1e12;
   out[4] = cus;
+  out[5] = ms[4];  // the interleaved pair: MFMA half alone, ms
+  out[6] = ms[5];  //                       vector half alone, ms
+  out[7] = ms[6];  //                       both, ms
   return 0;
 }

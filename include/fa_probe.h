@@ -19,7 +19,7 @@ extern "C" {
 #endif
 
 /*
- * fa_probe_rates -- runs four loops on every compute unit (one workgroup of
+ * fa_probe_rates -- runs seven loops on every compute unit (one workgroup of
  * 8 waves per CU, 2 waves per SIMD), each timed with HIP events on `stream`
  * (NULL = the default stream; the call synchronises with it), best of three:
  *   out[0]  dense bf16 MFMA rate, TFLOP/s (v_mfma_f32_32x32x16_bf16, four
@@ -28,7 +28,11 @@ extern "C" {
  *   out[2]  v_fma_f32 rate, 1e12 lane-results per second
  *   out[3]  the forward's per-score vector sequence above, 1e12 scores/s
  *   out[4]  compute units used
- * n is the number of doubles out can hold (at least 5).  The probe kernels
+ *   out[5..7]  milliseconds of an interleaved loop -- per step one MFMA and
+ *           the per-score sequence of two scores -- with only its MFMAs,
+ *           only its vector work, and both: how much of the smaller half
+ *           hides under the larger one when the two are independent
+ * n is the number of doubles out can hold (at least 8).  The probe kernels
  * touch no memory but one float per lane written to a buffer the call
  * allocates and frees.  Returns 0, -1 for a bad argument, -4 for a HIP error.
  */

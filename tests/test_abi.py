@@ -281,6 +281,6 @@ def test_probe_library_exports_and_rejects():
     lib = ctypes.CDLL(PROBE_LIB_PATH)
     lib.fa_probe_rates.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.c_int, ctypes.c_void_p]
     lib.fa_probe_rates.restype = ctypes.c_int
-    buf = (ctypes.c_double * 5)()
-    assert lib.fa_probe_rates(None, 5, None) == -1
-    assert lib.fa_probe_rates(buf, 4, None) == -1
+    buf = (ctypes.c_double * 8)()
+    assert lib.fa_probe_rates(None, 8, None) == -1
+    assert lib.fa_probe_rates(buf, 7, None) == -1

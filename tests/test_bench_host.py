@@ -144,3 +144,9 @@ def test_forward_ceilings_arithmetic():
     assert bench.forward_ceilings(rates, 32)["valu_tflops"] == pytest.approx(c["valu_tflops"] / 4)
     # in series the pair is slower than either alone
     assert c["serial_tflops"] < min(c["mfma_tflops"], c["valu_tflops"])
+
+
+def test_overlap_fraction():
+    assert bench.overlap_fraction(1.0, 0.5, 1.5) == pytest.approx(0.0)  # one after the other
+    assert bench.overlap_fraction(1.0, 0.5, 1.0) == pytest.approx(1.0)  # the shorter fully hidden
+    assert bench.overlap_fraction(1.0, 0.8, 1.4) == pytest.approx(0.5)

@@ -2,7 +2,8 @@
 every rate positive and in a range the MI355X can reach (dense bf16 MFMA
 under the published 2.5 PFLOP/s; an exponential no faster than an FMA; the
 per-score sequence, which holds an exponential and several other vector
-instructions, slower than either)."""
+instructions, slower than either; the interleaved MFMA + vector loop no
+faster than its longer half and no slower than both halves)."""
 
 import os
 import sys
@@ -23,3 +24,6 @@ def test_probe_rates_are_plausible():
     assert 200.0 < r["mfma_bf16_tflops"] < 2600.0
     assert 0 < r["exp_tlanes_per_s"] <= r["fma_tlanes_per_s"] * 1.05
     assert 0 < r["softmax_tscores_per_s"] < r["exp_tlanes_per_s"]
+    # the interleaved pair takes at least as long as its longer half, at most both halves (5% timing slack)
+    longer = max(r["pair_mfma_ms"], r["pair_valu_ms"])
+    assert 0.95 * longer <= r["pair_both_ms"] <= 1.05 * (r["pair_mfma_ms"] + r["pair_valu_ms"])
