@@ -368,9 +368,10 @@ __device__ __forceinline__ void dkdv_run(lds_char* lds, int nt, int i_start, con
 // them); the query heads of key/value head hk are hk G .. hk G + G - 1 of
 // the same batch.  With GS = 1 a workgroup takes the whole group and stores
 // dK and dV; with GS > 1 (GS divides G) split s takes heads s G/GS ..
-// (s + 1) G/GS - 1 and stores float32 sums (dK unscaled) into
-// part[s][row][D] (dK) and part[GS + s][row][D] (dV), rows numbered as in
-// the K tensor (R of them), for dkdv_reduce_kernel to add up.
+// (s + 1) G/GS - 1 and stores float32 sums (dK as -dK / scale, the sign
+// convention of dkdv_scores) into part[s][row][D] (dK) and
+// part[GS + s][row][D] (dV), rows numbered as in the K tensor (R of them),
+// for dkdv_reduce_kernel to add up.
 template <class T, int D, int MODE, bool SPLIT>
 __global__ __launch_bounds__(64 * kBwdWaves, Dkdv<D>::kOcc) void dkdv_kernel(
     const void* __restrict__ qp, const void* __restrict__ kp, const void* __restrict__ vp,
@@ -487,7 +488,8 @@ __global__ __launch_bounds__(64 * kBwdWaves, Dkdv<D>::kOcc) void dkdv_kernel(
 }
 
 // Sum of the GS float32 partials of dK and dV (split 0 first, so the bits
-// depend only on GS), dK times the scale, rounded to the element type.  One
+// depend only on GS), dK times `scale` (the launcher passes -scale, undoing
+// the partials' sign), rounded to the element type.  One
 // workgroup per dK/dV key block: rows k0 .. k0 + 127 of one key/value head,
 // D / 4 lanes per row, four columns per lane.
 template <class T, int D>
