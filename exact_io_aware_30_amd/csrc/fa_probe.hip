@@ -17,7 +17,8 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 constexpr int kThreads = 512;  // 8 waves: 2 per SIMD
 constexpr int kRegs = 16;      // independent chains per lane in the VALU loops
 
-enum Kind { kMfma = 0, kExp = 1, kFma = 2, kSoftmax = 3, kPairMfma = 4, kPairValu = 5, kPair = 6 };
+enum Kind { kMfma = 0, kExp = 1, kFma = 2, kSoftmax = 3, kPairMfma = 4, kPairValu = 5, kPair = 6, kPairAgprMfma = 7,
+            kPairAgpr = 8 };
 
 // One score of the forward's per-score vector sequence on chain x; every
 // second score also a max3 and a bf16 pack of the pair.
@@ -53,13 +54,23 @@ __global__ __launch_bounds__(kThreads) void probe_kernel(float* out, int iters, 
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
       for (int k = 0; k < kRegs / 2; ++k) {
-        if constexpr (KIND != kPairValu) acc[k & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[k & 3], 0, 0, 0);
-        if constexpr (KIND != kPairMfma) {
+        if constexpr (KIND == kPairAgprMfma || KIND == kPairAgpr)
+          // The accumulator in AGPRs (the MFMA-only register file).
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc[k & 3]) : "v"(a), "v"(b));
+        else if constexpr (KIND != kPairValu)
+          acc[k & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[k & 3], 0, 0, 0);
+        if constexpr (KIND != kPairMfma && KIND != kPairAgprMfma) {
           score_step(x, 2 * k, c, sum, mx, pk);
           score_step(x, 2 * k + 1, c, sum, mx, pk);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+    }
+    if constexpr (KIND == kPairAgprMfma || KIND == kPairAgpr) {
+      // The compiler does not see the assembly MFMAs: wait states between
+      // their last result and the reads below, with every accumulator tied
+      // to the statement.
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]));
     }
 #pragma unroll
     for (int j = 0; j < kRegs; ++j) r += x[j];
@@ -136,7 +147,158 @@ hipError_t time_kernel(float* out, int grid, int iters, hipStream_t st, float* b
   return err;
 }
 
+// ---------------------------------------------------------------------------
+// LDS probes.  Every kernel of the library feeds each 32x32x16 MFMA one
+// 1 KiB operand from LDS (a K, V, Q or dO tile read by the 64 lanes of a
+// wave); these loops measure how fast LDS delivers such reads, alone and as
+// MFMA operands, with the same 8 waves per CU.
+constexpr int kLdsBytes = 32768;  // one 32 KiB buffer; lanes read 16-byte chunks, consecutive lanes adjacent
+constexpr int kLdsSteps = 8;      // reads (and MFMAs) per loop iteration
+
+enum LdsKind { kLdsRead = 0, kLdsMfma1 = 1, kLdsMfma2 = 2 };
+
+typedef unsigned u32x4p __attribute__((ext_vector_type(4)));
+
+template <int KIND>
+__global__ __launch_bounds__(kThreads) void lds_probe_kernel(float* out, int iters) {
+  __shared__ __attribute__((aligned(16))) unsigned char buf[kLdsBytes];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int i = tid; i < kLdsBytes / 4; i += kThreads)
+    reinterpret_cast<unsigned*>(buf)[i] = 0x3c003c00u ^ (unsigned)(i * 2654435761u >> 20);
+  __syncthreads();
+  // Step k of wave w reads 1 KiB block (w + k) mod 32: 64 lanes x 16 bytes,
+  // contiguous, so every read is free of bank conflicts.
+  const unsigned base = (unsigned)(lane * 16);
+  float r = 0.f;
+  f32x16 acc[4] = {};
+  bf16x8 b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) b[i] = (__bf16)(1e-3f * (tid - i));
+  // The same 8 blocks every iteration (LDS has no cache, so repeated reads
+  // cost the same), which keeps address arithmetic out of the loop.
+  auto addr = [&](int, int k) { return base + (unsigned)(((w + k) & 31) * 1024); };
+  if constexpr (KIND == kLdsRead) {
+    for (int it = 0; it < iters; ++it) {
+      u32x4p x[kLdsSteps];
+#pragma unroll
+      for (int k = 0; k < kLdsSteps; ++k) x[k] = *reinterpret_cast<const u32x4p*>(buf + addr(it, k));
+      // All 8 reads in flight, then one wait: keeps every byte of each read.
+      asm volatile("" ::"v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]), "v"(x[7]));
+    }
+  } else {
+    // Per iteration the 8 operand reads are issued kPre MFMAs ahead of
+    // their use (scheduling groups: kPre reads, then MFMA and read pairs,
+    // then the last MFMAs), the pattern of the attention kernels' MFMA runs.
+    constexpr int kPre = 4;
+    for (int it = 0; it < iters; ++it) {
+      u32x4p x[kLdsSteps], y[kLdsSteps];
+#pragma unroll
+      for (int k = 0; k < kLdsSteps; ++k) {
+        x[k] = *reinterpret_cast<const u32x4p*>(buf + addr(it, k));
+        // kLdsMfma2: the B operand from LDS too (a second 1 KiB per MFMA).
+        if constexpr (KIND == kLdsMfma2) y[k] = *reinterpret_cast<const u32x4p*>(buf + (addr(it, k) ^ 16384u));
+      }
+#pragma unroll
+      for (int k = 0; k < kLdsSteps; ++k) {
+        const bf16x8 bk = KIND == kLdsMfma2 ? __builtin_bit_cast(bf16x8, y[k]) : b;
+        acc[k & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x[k]), bk, acc[k & 3], 0, 0, 0);
+      }
+      constexpr int R = KIND == kLdsMfma2 ? 2 : 1;  // reads per MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, kPre * R, 0);
+#pragma unroll
+      for (int k = 0; k < kLdsSteps - kPre; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kPre, 0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) r += acc[0][i] + acc[1][i] + acc[2][i] + acc[3][i];
+  out[blockIdx.x * kThreads + tid] = r;
+}
+
+template <int KIND>
+hipError_t time_lds(float* out, int grid, int iters, hipStream_t st, float* best_ms) {
+  hipEvent_t e0, e1;
+  hipError_t err = hipEventCreate(&e0);
+  if (err != hipSuccess) return err;
+  if ((err = hipEventCreate(&e1)) != hipSuccess) {
+    (void)hipEventDestroy(e0);
+    return err;
+  }
+  hipLaunchKernelGGL((lds_probe_kernel<KIND>), dim3(grid), dim3(kThreads), 0, st, out, iters);  // warm-up
+  float best = 1e30f;
+  for (int rep = 0; rep < 3 && err == hipSuccess; ++rep) {
+    err = hipEventRecord(e0, st);
+    if (err == hipSuccess) {
+      hipLaunchKernelGGL((lds_probe_kernel<KIND>), dim3(grid), dim3(kThreads), 0, st, out, iters);
+      err = hipGetLastError();
+    }
+    if (err == hipSuccess) err = hipEventRecord(e1, st);
+    if (err == hipSuccess) err = hipEventSynchronize(e1);
+    float ms = 0.f;
+    if (err == hipSuccess) err = hipEventElapsedTime(&ms, e0, e1);
+    if (err == hipSuccess) best = std::min(best, ms);
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  *best_ms = best;
+  return err;
+}
+
+// Which SIMD each wave of a 512-lane workgroup runs on: the SIMD_ID field
+// (bits 5:4) of the HW_ID hardware register, and the CU_ID field (11:8).
+__global__ __launch_bounds__(kThreads) void wave_simd_kernel(int* out) {
+  const unsigned hw = __builtin_amdgcn_s_getreg((31 << 11) | (0 << 6) | 4);  // HW_ID, all 32 bits
+  const int tid = threadIdx.x;
+  if ((tid & 63) == 0) out[blockIdx.x * (kThreads / 64) + (tid >> 6)] = (int)(((hw >> 8) & 15u) << 4 | ((hw >> 4) & 3u));
+}
+
 }  // namespace
+
+extern "C" int fa_probe_lds(double* out, int n, void* stream) {
+  if (!out || n < 6) return -1;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -4;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) return -4;
+  float* buf = nullptr;
+  if (hipMalloc(&buf, (size_t)cus * kThreads * sizeof(float)) != hipSuccess) return -4;
+  const int iters = 4000;
+  float ms[4] = {0, 0, 0, 0};
+  hipError_t err = time_lds<kLdsRead>(buf, cus, iters, st, &ms[0]);
+  if (err == hipSuccess) err = time_lds<kLdsMfma1>(buf, cus, iters, st, &ms[1]);
+  if (err == hipSuccess) err = time_lds<kLdsMfma2>(buf, cus, iters, st, &ms[2]);
+  if (err == hipSuccess) err = time_kernel<kMfma>(buf, cus, iters * kLdsSteps / 4, st, &ms[3]);
+  (void)hipFree(buf);
+  if (err != hipSuccess) return -4;
+  const double waves = (double)cus * (kThreads / 64), steps = waves * iters * kLdsSteps;
+  out[0] = steps * 1024.0 / (ms[0] * 1e-3) / 1e12;            // LDS reads alone, TB/s (whole chip)
+  out[1] = steps * 32768.0 / (ms[1] * 1e-3) / 1e12;           // MFMA with one 1 KiB LDS operand each, TFLOP/s
+  out[2] = steps * 32768.0 / (ms[2] * 1e-3) / 1e12;           // the same with a second 1 KiB read per MFMA
+  out[3] = steps * 32768.0 / (ms[3] * 1e-3) / 1e12;           // the same number of MFMAs from registers, TFLOP/s
+  out[4] = cus;
+  out[5] = ms[0];
+  return 0;
+}
+
+extern "C" int fa_probe_wave_simd(int* out, int n, void* stream) {
+  if (!out || n < 1) return -1;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -4;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) return -4;
+  const int total = cus * (kThreads / 64);
+  int* buf = nullptr;
+  if (hipMalloc(&buf, (size_t)total * sizeof(int)) != hipSuccess) return -4;
+  hipLaunchKernelGGL(wave_simd_kernel, dim3(cus), dim3(kThreads), 0, st, buf);
+  hipError_t err = hipGetLastError();
+  if (err == hipSuccess) err = hipMemcpyAsync(out, buf, (size_t)std::min(n, total) * sizeof(int), hipMemcpyDeviceToHost, st);
+  if (err == hipSuccess) err = hipStreamSynchronize(st);
+  (void)hipFree(buf);
+  return err == hipSuccess ? std::min(n, total) : -4;
+}
 
 extern "C" int fa_probe_rates(double* out, int n, void* stream) {
   if (!out || n < 8) return -1;
@@ -148,7 +310,7 @@ extern "C" int fa_probe_rates(double* out, int n, void* stream) {
   if (hipMalloc(&buf, (size_t)cus * kThreads * sizeof(float)) != hipSuccess) return -4;
   // Iteration counts give each loop a few milliseconds.
   const int it_mfma = 20000, it_valu = 4000;
-  float ms[7] = {0, 0, 0, 0, 0, 0, 0};
+  float ms[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
   hipError_t err = time_kernel<kMfma>(buf, cus, it_mfma, st, &ms[0]);
   if (err == hipSuccess) err = time_kernel<kExp>(buf, cus, it_valu, st, &ms[1]);
   if (err == hipSuccess) err = time_kernel<kFma>(buf, cus, it_valu, st, &ms[2]);
@@ -156,6 +318,8 @@ extern "C" int fa_probe_rates(double* out, int n, void* stream) {
   if (err == hipSuccess) err = time_kernel<kPairMfma>(buf, cus, it_valu, st, &ms[4]);
   if (err == hipSuccess) err = time_kernel<kPairValu>(buf, cus, it_valu, st, &ms[5]);
   if (err == hipSuccess) err = time_kernel<kPair>(buf, cus, it_valu, st, &ms[6]);
+  if (n >= 10 && err == hipSuccess) err = time_kernel<kPairAgprMfma>(buf, cus, it_valu, st, &ms[7]);
+  if (n >= 10 && err == hipSuccess) err = time_kernel<kPairAgpr>(buf, cus, it_valu, st, &ms[8]);
   (void)hipFree(buf);
   if (err != hipSuccess) return -4;
   const double waves = (double)cus * (kThreads / 64), lanes = (double)cus * kThreads;
@@ -167,5 +331,9 @@ extern "C" int fa_probe_rates(double* out, int n, void* stream) {
   out[5] = ms[4];  // the interleaved pair: MFMA half alone, ms
   out[6] = ms[5];  //                       vector half alone, ms
   out[7] = ms[6];  //                       both, ms
+  if (n >= 10) {
+    out[8] = ms[7];  // the pair with AGPR accumulators: MFMA half alone, ms
+    out[9] = ms[8];  //                                  both, ms
+  }
   return 0;
 }

@@ -32,11 +32,45 @@ extern "C" {
  *           the per-score sequence of two scores -- with only its MFMAs,
  *           only its vector work, and both: how much of the smaller half
  *           hides under the larger one when the two are independent
+ *   out[8..9]  (when n >= 10) the same loop with the MFMA accumulators in
+ *           AGPRs, the register file only MFMAs address, through assembly
+ *           MFMAs: its MFMAs alone, and both halves, ms
  * n is the number of doubles out can hold (at least 8).  The probe kernels
  * touch no memory but one float per lane written to a buffer the call
  * allocates and frees.  Returns 0, -1 for a bad argument, -4 for a HIP error.
  */
 int fa_probe_rates(double* out, int n, void* stream);
+
+/*
+ * fa_probe_lds -- LDS delivery rate, alone and as MFMA operands.  Each
+ * attention kernel feeds every 32x32x16 MFMA one 1 KiB operand read from
+ * LDS by its wave; these loops run that pattern on every compute unit (one
+ * workgroup of 8 waves per CU, 2 waves per SIMD, a 32 KiB LDS buffer, reads
+ * of 16 contiguous bytes per lane, free of bank conflicts), timed like
+ * fa_probe_rates:
+ *   out[0]  ds_read_b128 alone, TB/s over the whole chip (8 reads in
+ *           flight per wave)
+ *   out[1]  MFMAs whose A operand is such a read, issued 4 MFMAs ahead,
+ *           TFLOP/s
+ *   out[2]  the same with the B operand read from LDS too (2 KiB per MFMA)
+ *   out[3]  the same number of MFMAs with both operands in registers
+ *   out[4]  compute units used
+ *   out[5]  milliseconds of the read-only loop
+ * n is the number of doubles out can hold (at least 6).  Returns 0, -1 for
+ * a bad argument, -4 for a HIP error.
+ */
+int fa_probe_lds(double* out, int n, void* stream);
+
+/*
+ * fa_probe_wave_simd -- where the hardware places the waves of a workgroup
+ * of 8 waves (512 lanes), the shape of the forward kernel's workgroups: one
+ * such workgroup per compute unit, each wave reading its HW_ID hardware
+ * register.  out[8 g + w] receives (CU_ID << 4) | SIMD_ID of wave w of
+ * workgroup g, for as many entries as n allows (8 per compute unit at
+ * most).  Returns the number of entries written, -1 for a bad argument, -4
+ * for a HIP error; the call synchronises with `stream`.
+ */
+int fa_probe_wave_simd(int* out, int n, void* stream);
 
 #ifdef __cplusplus
 }

@@ -275,7 +275,7 @@ def test_probe_library_exports_and_rejects():
 
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(os.path.dirname(HEADER), "fa_probe.h")).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
-    assert names == ["fa_probe_rates"]
+    assert names == ["fa_probe_lds", "fa_probe_rates", "fa_probe_wave_simd"]
     out = subprocess.run(["nm", "-D", "--defined-only", PROBE_LIB_PATH], capture_output=True, text=True).stdout
     assert set(names) <= set(re.findall(r"\bT (fa_\w+)$", out, flags=re.M))
     lib = ctypes.CDLL(PROBE_LIB_PATH)
@@ -284,3 +284,12 @@ def test_probe_library_exports_and_rejects():
     buf = (ctypes.c_double * 8)()
     assert lib.fa_probe_rates(None, 8, None) == -1
     assert lib.fa_probe_rates(buf, 7, None) == -1
+    lib.fa_probe_lds.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.c_int, ctypes.c_void_p]
+    lib.fa_probe_lds.restype = ctypes.c_int
+    assert lib.fa_probe_lds(None, 6, None) == -1
+    assert lib.fa_probe_lds(buf, 5, None) == -1
+    lib.fa_probe_wave_simd.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.c_int, ctypes.c_void_p]
+    lib.fa_probe_wave_simd.restype = ctypes.c_int
+    ibuf = (ctypes.c_int * 8)()
+    assert lib.fa_probe_wave_simd(None, 8, None) == -1
+    assert lib.fa_probe_wave_simd(ibuf, 0, None) == -1

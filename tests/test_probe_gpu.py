@@ -3,7 +3,9 @@ every rate positive and in a range the MI355X can reach (dense bf16 MFMA
 under the published 2.5 PFLOP/s; an exponential no faster than an FMA; the
 per-score sequence, which holds an exponential and several other vector
 instructions, slower than either; the interleaved MFMA + vector loop no
-faster than its longer half and no slower than both halves)."""
+faster than its longer half and no slower than both halves; LDS-fed MFMA
+loops no faster than the register-fed one; every wave of a 512-lane
+workgroup on one compute unit, two per SIMD)."""
 
 import os
 import sys
@@ -27,3 +29,21 @@ def test_probe_rates_are_plausible():
     # the interleaved pair takes at least as long as its longer half, at most both halves (5% timing slack)
     longer = max(r["pair_mfma_ms"], r["pair_valu_ms"])
     assert 0.95 * longer <= r["pair_both_ms"] <= 1.05 * (r["pair_mfma_ms"] + r["pair_valu_ms"])
+
+
+def test_probe_lds_is_plausible():
+    r = bench.probe_lds()
+    print(r, flush=True)
+    assert r["compute_units"] >= 1
+    assert r["lds_read_tbs"] > 0
+    assert 200.0 < r["mfma_regs_tflops"] < 2600.0
+    # an operand read from LDS cannot make the matrix core faster (5% timing slack)
+    assert 0 < r["mfma_lds2_tflops"] <= 1.05 * r["mfma_lds1_tflops"] <= 1.05 * 1.05 * r["mfma_regs_tflops"]
+
+
+def test_wave_placement():
+    r = bench.probe_wave_simd()
+    print(r, flush=True)
+    assert r["one_cu_per_group"]
+    assert sorted(r["simd_of_wave"]) == [0, 0, 1, 1, 2, 2, 3, 3]
+    assert r["pairs_same_in_all"]
