@@ -193,6 +193,16 @@ constexpr int kPipeStages = 4;
 #define FA_FWD_PIPE_PRE2 2
 #endif
 constexpr int kPipePre1 = FA_FWD_PIPE_PRE1, kPipePre2 = FA_FWD_PIPE_PRE2;
+// Where the row sums of tile t are added: under the QK^T MFMAs of tile t+1
+// beside the exponentials (0), or under the PV MFMAs of tile t beside the
+// row maximum (1).  With 1 the QK^T run's vector work per MFMA (two
+// exponentials, two FMAs, half a pack) fits in the MFMA's 32 cycles and the
+// PV run, which had little besides the maximum, takes the adds: 2-3%
+// faster at d = 128, bit-identical (the adds run in the same order).
+#ifndef FA_FWD_SUM_IN_PV
+#define FA_FWD_SUM_IN_PV 1
+#endif
+constexpr bool kSumInPv = FA_FWD_SUM_IN_PV != 0;
 // Used at d = 128, where a tile's VALU work fits under its MFMAs; at d = 64
 // and 32 (half and a quarter of the MFMAs per score) the plain kernel is
 // faster.  FA_FWD_PIPE=0/1 forces one form for every head dimension.
@@ -339,18 +349,20 @@ __device__ __forceinline__ void fwd_pipe_step(lds_char* lds, int t, int nt, int 
       for (int e = 0; e < E; ++e) {
         const int x = i * E + e, a = x / 16, r = x % 16;
         s_cur[a][r] = exp2_fast(__builtin_fmaf(s_cur[a][r], c, -mr));  // P in place
-        rs += s_cur[a][r];
+        if constexpr (!kSumInPv) rs += s_cur[a][r];
         if (r % 8 == 7) pf[x / 8] = pack8<T>(s_cur[a], (r / 8));
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     fwd_prio_end();
-    l += rs;
-    // Pin P and l here, or the compiler sinks their VALU work past the
+    // Pin P (and l) here, or the compiler sinks their VALU work past the
     // branch below, away from the MFMAs it is meant to run under.
 #pragma unroll
     for (int j = 0; j < 2 * NA; ++j) land(pf[j]);
-    land(l);
+    if constexpr (!kSumInPv) {
+      l += rs;
+      land(l);
+    }
 
     const int j1 = (tb + t + 1) * BN;
     if ((j1 + BN > N) || (MASK && !win.all_visible(wq0, wq0 + 31, j1, j1 + BN - 1)))
@@ -377,10 +389,12 @@ __device__ __forceinline__ void fwd_pipe_step(lds_char* lds, int t, int nt, int 
       for (int e = 0; e < F; ++e) {
         const int x = i * F + e;
         mx = fmaxf(mx, s_nxt[x / 16][x % 16]);
+        if constexpr (kSumInPv) rs += s_cur[x / 16][x % 16];
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     fwd_prio_end();
+    if constexpr (kSumInPv) l += rs;
     fwd_rescale<NB>(max_with_partner(mx) * c, acc, mref, l);
   }
 }

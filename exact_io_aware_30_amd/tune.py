@@ -53,6 +53,7 @@ SPACES = {
         "prio": ["-DFA_FWD_PRIO=1"],
         "pipe_pre_2_2": ["-DFA_FWD_PIPE_PRE1=2", "-DFA_FWD_PIPE_PRE2=2"],
         "pipe_pre_4_3": ["-DFA_FWD_PIPE_PRE1=4", "-DFA_FWD_PIPE_PRE2=3"],
+        "sum_in_qk": ["-DFA_FWD_SUM_IN_PV=0"],
     },
     "dkdv": {
         "default": [],
