@@ -264,12 +264,13 @@ def probe_lds():
     lib = ctypes.CDLL(PROBE_LIBRARY)
     lib.fa_probe_lds.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.c_int, ctypes.c_void_p]
     lib.fa_probe_lds.restype = ctypes.c_int
-    out = (ctypes.c_double * 6)()
-    rc = lib.fa_probe_lds(out, 6, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    out = (ctypes.c_double * 8)()
+    rc = lib.fa_probe_lds(out, 8, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
     if rc != 0:
         raise RuntimeError(f"fa_probe_lds failed (status {rc})")
     return {"lds_read_tbs": out[0], "mfma_lds1_tflops": out[1], "mfma_lds2_tflops": out[2],
-            "mfma_regs_tflops": out[3], "compute_units": int(out[4]), "lds_read_ms": out[5]}
+            "mfma_regs_tflops": out[3], "compute_units": int(out[4]), "lds_read_ms": out[5],
+            "mfma_chain1_tflops": out[6], "mfma_chain2_tflops": out[7]}
 
 
 def probe_wave_simd():

@@ -157,6 +157,59 @@ constexpr int kLdsSteps = 8;      // reads (and MFMAs) per loop iteration
 
 enum LdsKind { kLdsRead = 0, kLdsMfma1 = 1, kLdsMfma2 = 2 };
 
+// MFMAs from registers on CHAINS accumulators in rotation: with one, each
+// MFMA takes the previous one's result as its accumulator input.
+template <int CHAINS>
+__global__ __launch_bounds__(kThreads) void chain_kernel(float* out, int iters) {
+  const int tid = threadIdx.x;
+  bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(1e-3f * (tid + i));
+    b[i] = (__bf16)(1e-3f * (tid - i));
+  }
+  f32x16 acc[CHAINS] = {};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k % CHAINS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[k % CHAINS], 0, 0, 0);
+  }
+  float r = 0.f;
+#pragma unroll
+  for (int c = 0; c < CHAINS; ++c)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) r += acc[c][i];
+  out[blockIdx.x * kThreads + tid] = r;
+}
+
+template <int CHAINS>
+hipError_t time_chain(float* out, int grid, int iters, hipStream_t st, float* best_ms) {
+  hipEvent_t e0, e1;
+  hipError_t err = hipEventCreate(&e0);
+  if (err != hipSuccess) return err;
+  if ((err = hipEventCreate(&e1)) != hipSuccess) {
+    (void)hipEventDestroy(e0);
+    return err;
+  }
+  hipLaunchKernelGGL((chain_kernel<CHAINS>), dim3(grid), dim3(kThreads), 0, st, out, iters);  // warm-up
+  float best = 1e30f;
+  for (int rep = 0; rep < 3 && err == hipSuccess; ++rep) {
+    err = hipEventRecord(e0, st);
+    if (err == hipSuccess) {
+      hipLaunchKernelGGL((chain_kernel<CHAINS>), dim3(grid), dim3(kThreads), 0, st, out, iters);
+      err = hipGetLastError();
+    }
+    if (err == hipSuccess) err = hipEventRecord(e1, st);
+    if (err == hipSuccess) err = hipEventSynchronize(e1);
+    float ms = 0.f;
+    if (err == hipSuccess) err = hipEventElapsedTime(&ms, e0, e1);
+    if (err == hipSuccess) best = std::min(best, ms);
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  *best_ms = best;
+  return err;
+}
+
 typedef unsigned u32x4p __attribute__((ext_vector_type(4)));
 
 template <int KIND>
@@ -271,6 +324,9 @@ extern "C" int fa_probe_lds(double* out, int n, void* stream) {
   if (err == hipSuccess) err = time_lds<kLdsMfma1>(buf, cus, iters, st, &ms[1]);
   if (err == hipSuccess) err = time_lds<kLdsMfma2>(buf, cus, iters, st, &ms[2]);
   if (err == hipSuccess) err = time_kernel<kMfma>(buf, cus, iters * kLdsSteps / 4, st, &ms[3]);
+  float chain_ms[2] = {0, 0};
+  if (n >= 8 && err == hipSuccess) err = time_chain<1>(buf, cus, iters, st, &chain_ms[0]);
+  if (n >= 8 && err == hipSuccess) err = time_chain<2>(buf, cus, iters, st, &chain_ms[1]);
   (void)hipFree(buf);
   if (err != hipSuccess) return -4;
   const double waves = (double)cus * (kThreads / 64), steps = waves * iters * kLdsSteps;
@@ -280,6 +336,10 @@ extern "C" int fa_probe_lds(double* out, int n, void* stream) {
   out[3] = steps * 32768.0 / (ms[3] * 1e-3) / 1e12;           // the same number of MFMAs from registers, TFLOP/s
   out[4] = cus;
   out[5] = ms[0];
+  if (n >= 8) {
+    out[6] = steps * 32768.0 / (chain_ms[0] * 1e-3) / 1e12;  // one dependent accumulator chain, TFLOP/s
+    out[7] = steps * 32768.0 / (chain_ms[1] * 1e-3) / 1e12;  // two chains
+  }
   return 0;
 }
 

@@ -56,6 +56,9 @@ int fa_probe_rates(double* out, int n, void* stream);
  *   out[3]  the same number of MFMAs with both operands in registers
  *   out[4]  compute units used
  *   out[5]  milliseconds of the read-only loop
+ *   out[6..7]  (when n >= 8) MFMAs from registers on one accumulator (each
+ *           takes the previous one's result as its accumulator input) and
+ *           on two in rotation, TFLOP/s
  * n is the number of doubles out can hold (at least 6).  Returns 0, -1 for
  * a bad argument, -4 for a HIP error.
  */

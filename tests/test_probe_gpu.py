@@ -4,7 +4,8 @@ under the published 2.5 PFLOP/s; an exponential no faster than an FMA; the
 per-score sequence, which holds an exponential and several other vector
 instructions, slower than either; the interleaved MFMA + vector loop no
 faster than its longer half and no slower than both halves; LDS-fed MFMA
-loops no faster than the register-fed one; every wave of a 512-lane
+loops no faster than the register-fed one; MFMAs on one or two dependent
+accumulator chains under the peak; every wave of a 512-lane
 workgroup on one compute unit, two per SIMD)."""
 
 import os
@@ -39,6 +40,10 @@ def test_probe_lds_is_plausible():
     assert 200.0 < r["mfma_regs_tflops"] < 2600.0
     # an operand read from LDS cannot make the matrix core faster (5% timing slack)
     assert 0 < r["mfma_lds2_tflops"] <= 1.05 * r["mfma_lds1_tflops"] <= 1.05 * 1.05 * r["mfma_regs_tflops"]
+    # dependent accumulator chains: a positive rate under the published peak
+    # (measured at the full MFMA rate: a chained MFMA does not wait for the
+    # previous one's result)
+    assert 0 < r["mfma_chain1_tflops"] < 2600.0 and 0 < r["mfma_chain2_tflops"] < 2600.0
 
 
 def test_wave_placement():
