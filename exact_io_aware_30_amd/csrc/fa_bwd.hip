@@ -122,6 +122,19 @@ struct Dkdv {
   static constexpr bool kVLds = FA_DKDV_CFG_VLDS;
   static_assert(kTile == 32 || kTile == 64, "dK/dV query tile");
 };
+// A tile's dV MFMAs issued before its dK MFMAs with dS formed between them
+// (1), or dS formed in the vector phase and the two kinds alternating (0).
+// Bit-identical either way; 1 is 3% faster at d = 32 (fp16 [3,12,2000,32]
+// full), and at d = 128 causal 5% slower, so it is the default at d = 32
+// only.  Not used for general windows, whose mask tests leave no registers
+// for it.  FA_DKDV_DV_FIRST=0/1 forces one form for every head dimension.
+#ifdef FA_DKDV_DV_FIRST
+template <int D>
+constexpr bool kDvFirst = FA_DKDV_DV_FIRST != 0;
+#else
+template <int D>
+constexpr bool kDvFirst = D == 32;
+#endif
 // L and D of a query tile: one dword per lane of a wave, so 64 rows of each
 // are copied (rows past the tile are not read).
 constexpr int kStatsRows = 64;
@@ -220,6 +233,63 @@ __device__ __forceinline__ void dkdv_probs(f32x16* s, f32x16* dp, const float* s
   }
 }
 
+// Phase 2 when dS is formed in phase 3 (kDvFirst): the mask,
+// P = 2^(S c - L log2 e) and its packing; dp keeps D - dP.
+template <class T, int NA>
+__device__ __forceinline__ void dkdv_probs_p(f32x16* s, const float* st, u32x4* pf, bool edge, int i0, int krow,
+                                             Win win, float c, int lane) {
+  const int h = lane >> 5;
+  if (edge) {
+    const int rlo = (win.right < 0 ? kUnbounded : krow - win.right) - i0 - 4 * h;
+    const int rhi = (win.left < 0 ? (1 << 30) : krow + win.left) - i0 - 4 * h;
+#pragma unroll
+    for (int a = 0; a < NA; ++a)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int off = 32 * a + 8 * (r >> 2) + (r & 3);
+        if ((win.right >= 0 && off < rlo) || (win.left >= 0 && off > rhi)) s[a][r] = -INFINITY;
+      }
+  }
+#pragma unroll
+  for (int a = 0; a < NA; ++a)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 l2 = *(const f32x4*)(st + 32 * a + 8 * g + 4 * h) * kLog2e;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[a][4 * g + e] = exp2_fast(__builtin_fmaf(s[a][4 * g + e], c, -l2[e]));
+    }
+#pragma unroll
+  for (int j = 0; j < 2 * NA; ++j) pf[j] = pack8<T>(s[j >> 1], j & 1);
+}
+
+// Phase 3 with the dV MFMAs first: dV^T += dO^T P, then -dS = P (D - dP)
+// and its packing written after them (so that they can issue while those
+// MFMAs run), then dK^T += Q^T dS.  Each accumulator sums its products in
+// the same order as dkdv_accum: bit-identical results.
+template <class T, int D, int NA>
+__device__ __forceinline__ void dkdv_accum_dv_first(const lds_char* qt, const lds_char* dot, const u32x4* pf,
+                                                    const f32x16* s, f32x16* dp, f32x16* dka, f32x16* dva, int lane) {
+  constexpr int NB = D / 32;
+  u32x4 dsf[2 * NA];
+  prio_mfma_begin();
+#pragma unroll
+  for (int j = 0; j < 2 * NA; ++j)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) dva[b] = Elem<T>::mma(lds_cols_operand<D>(dot, j, 32 * b, lane), pf[j], dva[b]);
+#pragma unroll
+  for (int a = 0; a < NA; ++a)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dp[a][r] = s[a][r] * dp[a][r];
+#pragma unroll
+  for (int j = 0; j < 2 * NA; ++j) dsf[j] = pack8<T>(dp[j >> 1], j & 1);
+#pragma unroll
+  for (int j = 0; j < 2 * NA; ++j)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) dka[b] = Elem<T>::mma(lds_cols_operand<D>(qt, j, 32 * b, lane), dsf[j], dka[b]);
+  sched_mfma_lds<4 * NA * NB, 2, (4 * NA * NB < Dkdv<D>::kPre2 ? 4 * NA * NB : Dkdv<D>::kPre2)>();
+  prio_mfma_end();
+}
+
 // Phase 3 (MFMA): dV^T += dO^T P and dK^T += Q^T dS, A operands by
 // transposed LDS reads.
 template <class T, int D, int NA>
@@ -241,15 +311,20 @@ __device__ __forceinline__ void dkdv_accum(const lds_char* qt, const lds_char* d
 // One query tile of the dK/dV kernel for one wave, the three phases in a
 // row.  One code path for every tile, so the accumulator registers need no
 // copies at merges.
-template <class T, int D, int NA, class VOp>
+template <class T, int D, int NA, bool DVF, class VOp>
 __device__ __forceinline__ void dkdv_tile(const lds_char* qt, const lds_char* dot, const float* st, const u32x4* kf,
                                           const VOp& vop, f32x16* dka, f32x16* dva, bool edge, int i0, int krow,
                                           Win win, float c, int lane) {
   f32x16 s[NA], dp[NA];
   u32x4 pf[2 * NA], dsf[2 * NA];
   dkdv_scores<T, D, NA>(qt, dot, kf, vop, st, s, dp, lane);
-  dkdv_probs<T, NA>(s, dp, st, pf, dsf, edge, i0, krow, win, c, lane);
-  dkdv_accum<T, D, NA>(qt, dot, pf, dsf, dka, dva, lane);
+  if constexpr (DVF) {
+    dkdv_probs_p<T, NA>(s, st, pf, edge, i0, krow, win, c, lane);
+    dkdv_accum_dv_first<T, D, NA>(qt, dot, pf, s, dp, dka, dva, lane);
+  } else {
+    dkdv_probs<T, NA>(s, dp, st, pf, dsf, edge, i0, krow, win, c, lane);
+    dkdv_accum<T, D, NA>(qt, dot, pf, dsf, dka, dva, lane);
+  }
 }
 
 // Enqueue the DMA of query tile i0: Q rows, dO rows, then L and D (one
@@ -268,7 +343,7 @@ __device__ __forceinline__ void dkdv_issue(lds_char* b, int i0, const DmaTile<Dk
 // One ring step on query tile t, held in ring buffer IDX = t % S (a
 // compile-time index, so LDS operand addresses are register + immediate):
 // wait and barrier, DMA of tile t + S - 1, then the math.
-template <class T, int D, bool MASK, int IDX, class VOp>
+template <class T, int D, bool MASK, bool DVF, int IDX, class VOp>
 __device__ __forceinline__ void dkdv_step(lds_char* lds, int t, int nt, int i_start,
                                           const DmaTile<Dkdv<D>::kTile, D, kBwdWaves>& dma, Rsrc rq, Rsrc rdo, Rsrc rl,
                                           Rsrc rd, const u32x4* kf, const VOp& vop, f32x16* dka, f32x16* dva,
@@ -287,7 +362,7 @@ __device__ __forceinline__ void dkdv_step(lds_char* lds, int t, int nt, int i_st
   const lds_char* cur = lds + IDX * BUF;
   const float* st = (const float*)(cur + 2 * TILE);
   const bool edge = MASK && !win.all_visible(i0, i0 + BMQ - 1, wk0, wk0 + 31);
-  dkdv_tile<T, D, BMQ / 32>(cur, cur + TILE, st, kf, vop, dka, dva, edge, i0, krow, win, c, lane);
+  dkdv_tile<T, D, BMQ / 32, DVF>(cur, cur + TILE, st, kf, vop, dka, dva, edge, i0, krow, win, c, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -309,7 +384,7 @@ __device__ __forceinline__ void dkdv_step(lds_char* lds, int t, int nt, int i_st
 // store of dK and dV, or of their float32 partial sums over those heads when
 // the group is split over several workgroups.  The first head's first tiles
 // were issued by the caller.
-template <class T, int D, bool MASK, bool SPLIT, class VOp, class Dst>
+template <class T, int D, bool MASK, bool SPLIT, bool DVF, class VOp, class Dst>
 __device__ __forceinline__ void dkdv_run(lds_char* lds, int nt, int i_start, const DmaTile<Dkdv<D>::kTile, D, kBwdWaves>& dma,
                                          const void* qp, const void* dop, const float* lsep, const float* deltap,
                                          const Geom& geo, int b, int hk, int g0, int ng, int N, const u32x4* kf,
@@ -338,18 +413,18 @@ __device__ __forceinline__ void dkdv_run(lds_char* lds, int nt, int i_start, con
       if (S > 3 && nt > 2) dkdv_issue<D>(lds + (2 % S) * BUF, i_start + 2 * BMQ, dma, rq, rdo, rl, rd, w, lane);
     }
     for (int t = 0; t < nt; t += S) {
-      dkdv_step<T, D, MASK, 0>(lds, t, nt, i_start, dma, rq, rdo, rl, rd, kf, vop, dka, dva, wk0, krow, win, c, w,
+      dkdv_step<T, D, MASK, DVF, 0>(lds, t, nt, i_start, dma, rq, rdo, rl, rd, kf, vop, dka, dva, wk0, krow, win, c, w,
                                lane);
       if (t + 1 < nt)
-        dkdv_step<T, D, MASK, 1>(lds, t + 1, nt, i_start, dma, rq, rdo, rl, rd, kf, vop, dka, dva, wk0, krow, win, c,
+        dkdv_step<T, D, MASK, DVF, 1>(lds, t + 1, nt, i_start, dma, rq, rdo, rl, rd, kf, vop, dka, dva, wk0, krow, win, c,
                                  w, lane);
       if constexpr (S > 2)
         if (t + 2 < nt)
-          dkdv_step<T, D, MASK, 2 % S>(lds, t + 2, nt, i_start, dma, rq, rdo, rl, rd, kf, vop, dka, dva, wk0, krow,
+          dkdv_step<T, D, MASK, DVF, 2 % S>(lds, t + 2, nt, i_start, dma, rq, rdo, rl, rd, kf, vop, dka, dva, wk0, krow,
                                        win, c, w, lane);
       if constexpr (S > 3)
         if (t + 3 < nt)
-          dkdv_step<T, D, MASK, 3 % S>(lds, t + 3, nt, i_start, dma, rq, rdo, rl, rd, kf, vop, dka, dva, wk0, krow,
+          dkdv_step<T, D, MASK, DVF, 3 % S>(lds, t + 3, nt, i_start, dma, rq, rdo, rl, rd, kf, vop, dka, dva, wk0, krow,
                                        win, c, w, lane);
     }
   }
@@ -480,10 +555,10 @@ __global__ __launch_bounds__(64 * kBwdWaves, Dkdv<D>::kOcc) void dkdv_kernel(
     if (S > 3 && nt > 2) dkdv_issue<D>(lds + (2 % S) * BUF, i_start + 2 * BMQ, dma, rq, rdo, rl, rd, w, lane);
   }
   if constexpr (VL)
-    dkdv_run<T, D, MASK, SPLIT>(lds, nt, i_start, dma, qp, dop, lsep, deltap, geo, b, hk, g0, ng, N, kf,
+    dkdv_run<T, D, MASK, SPLIT, kDvFirst<D> && MODE != 2>(lds, nt, i_start, dma, qp, dop, lsep, deltap, geo, b, hk, g0, ng, N, kf,
                                 VLds<D>{vt, 32 * w}, rdk, rdv, wk0, krow, win, c, scale, w, lane);
   else
-    dkdv_run<T, D, MASK, SPLIT>(lds, nt, i_start, dma, qp, dop, lsep, deltap, geo, b, hk, g0, ng, N, kf, VRegs{vf},
+    dkdv_run<T, D, MASK, SPLIT, kDvFirst<D> && MODE != 2>(lds, nt, i_start, dma, qp, dop, lsep, deltap, geo, b, hk, g0, ng, N, kf, VRegs{vf},
                                 rdk, rdv, wk0, krow, win, c, scale, w, lane);
 }
 

@@ -54,6 +54,7 @@ SPACES = {
         "pipe_pre_2_2": ["-DFA_FWD_PIPE_PRE1=2", "-DFA_FWD_PIPE_PRE2=2"],
         "pipe_pre_4_3": ["-DFA_FWD_PIPE_PRE1=4", "-DFA_FWD_PIPE_PRE2=3"],
         "sum_in_qk": ["-DFA_FWD_SUM_IN_PV=0"],
+        "plain_sum_before_pv": ["-DFA_FWD_PLAIN_SUM_AFTER_PV=0"],
     },
     "dkdv": {
         "default": [],
@@ -74,6 +75,8 @@ SPACES = {
         "tile64": ["-DFA_DKDV_TILE=64"],
         "vregs": ["-DFA_DKDV_VLDS=0"],
         "stages3": ["-DFA_DKDV_STAGES=3"],
+        "dv_first": ["-DFA_DKDV_DV_FIRST=1"],
+        "dv_first_off": ["-DFA_DKDV_DV_FIRST=0"],
     },
     "dq": {
         "default": [],
