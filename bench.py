@@ -295,16 +295,20 @@ def probe_wave_simd():
 
 
 def wave_simd_summary(ids):
-    """Summarise (CU_ID << 4 | SIMD_ID) per wave, 8 waves per workgroup."""
+    """Summarise (XCC_ID << 8 | CU_ID << 4 | SIMD_ID) per wave, 8 waves per
+    workgroup; "xcd_round_robin" is the share of workgroups g placed on XCD
+    (g + x0) mod 8, x0 being workgroup 0's XCD."""
     groups = [ids[i:i + 8] for i in range(0, len(ids) - len(ids) % 8, 8)]
     simd = [[x & 3 for x in g] for g in groups]
     same_cu = all(len({x >> 4 for x in g}) == 1 for g in groups)
+    xcd = [g[0] >> 8 for g in groups]
+    rr = sum(1 for i, x in enumerate(xcd) if x == (xcd[0] + i) % 8) / max(1, len(xcd))
     def pairs(s):
         return sorted((a, b) for a in range(8) for b in range(a + 1, 8) if s[a] == s[b])
 
     return {"simd_of_wave": simd[0], "same_in_all": all(s == simd[0] for s in simd), "one_cu_per_group": same_cu,
             "shared_pairs": pairs(simd[0]), "pairs_same_in_all": all(pairs(s) == pairs(simd[0]) for s in simd),
-            "groups": len(groups)}
+            "groups": len(groups), "xcd_first_16": xcd[:16], "xcd_round_robin": rr}
 
 
 def overlap_fraction(t_mfma: float, t_valu: float, t_both: float) -> float:
@@ -351,7 +355,8 @@ def ceilings(rows=()):
           f"1 KiB LDS operand per MFMA, {lds['mfma_lds2_tflops']:.0f} with two")
     print(f"wave placement in a 512-lane workgroup: SIMD of waves 0..7 = {ws['simd_of_wave']} "
           f"(pairs sharing a SIMD: {ws['shared_pairs']}, the same pairs in all {ws['groups']} workgroups: "
-          f"{ws['pairs_same_in_all']})")
+          f"{ws['pairs_same_in_all']}); XCD of workgroups 0..15 = {ws['xcd_first_16']}, share placed round-robin "
+          f"over the 8 XCDs: {ws['xcd_round_robin']:.3f}")
     emit({"probe_rates": {k: (round(v, 3) if isinstance(v, float) else v) for k, v in rates.items()},
           "probe_lds": {k: (round(v, 3) if isinstance(v, float) else v) for k, v in lds.items()},
           "wave_placement": ws, "forward_ceilings": out})

@@ -301,11 +301,16 @@ hipError_t time_lds(float* out, int grid, int iters, hipStream_t st, float* best
 }
 
 // Which SIMD each wave of a 512-lane workgroup runs on: the SIMD_ID field
-// (bits 5:4) of the HW_ID hardware register, and the CU_ID field (11:8).
+// (bits 5:4) of the HW_ID hardware register, the CU_ID field (11:8), and the
+// XCD (accelerator complex die) from the XCC_ID register (bits 3:0).
 __global__ __launch_bounds__(kThreads) void wave_simd_kernel(int* out) {
   const unsigned hw = __builtin_amdgcn_s_getreg((31 << 11) | (0 << 6) | 4);  // HW_ID, all 32 bits
+  unsigned xcc;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
   const int tid = threadIdx.x;
-  if ((tid & 63) == 0) out[blockIdx.x * (kThreads / 64) + (tid >> 6)] = (int)(((hw >> 8) & 15u) << 4 | ((hw >> 4) & 3u));
+  if ((tid & 63) == 0)
+    out[blockIdx.x * (kThreads / 64) + (tid >> 6)] =
+        (int)((xcc & 15u) << 8 | ((hw >> 8) & 15u) << 4 | ((hw >> 4) & 3u));
 }
 
 }  // namespace

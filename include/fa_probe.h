@@ -68,8 +68,9 @@ int fa_probe_lds(double* out, int n, void* stream);
  * fa_probe_wave_simd -- where the hardware places the waves of a workgroup
  * of 8 waves (512 lanes), the shape of the forward kernel's workgroups: one
  * such workgroup per compute unit, each wave reading its HW_ID hardware
- * register.  out[8 g + w] receives (CU_ID << 4) | SIMD_ID of wave w of
- * workgroup g, for as many entries as n allows (8 per compute unit at
+ * register and the XCC_ID register (its XCD, one of the eight dies).
+ * out[8 g + w] receives (XCC_ID << 8) | (CU_ID << 4) | SIMD_ID of wave w
+ * of workgroup g, for as many entries as n allows (8 per compute unit at
  * most).  Returns the number of entries written, -1 for a bad argument, -4
  * for a HIP error; the call synchronises with `stream`.
  */

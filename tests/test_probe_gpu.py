@@ -52,3 +52,4 @@ def test_wave_placement():
     assert r["one_cu_per_group"]
     assert sorted(r["simd_of_wave"]) == [0, 0, 1, 1, 2, 2, 3, 3]
     assert r["pairs_same_in_all"]
+    assert all(0 <= x < 8 for x in r["xcd_first_16"])
