@@ -191,6 +191,22 @@ __device__ __forceinline__ void dkdv_scores(const lds_char* qt, const lds_char* 
   prio_mfma_end();
 }
 
+// Scores of queries outside the lane's key window to -inf: query i sees key
+// krow iff krow - right <= i <= krow + left, compared as offsets
+// 32a + 8(r/4) + r%4 from i0 + 4h.
+template <int NA>
+__device__ __forceinline__ void dkdv_mask(f32x16* s, int i0, int krow, Win win, int h) {
+  const int rlo = (win.right < 0 ? kUnbounded : krow - win.right) - i0 - 4 * h;
+  const int rhi = (win.left < 0 ? (1 << 30) : krow + win.left) - i0 - 4 * h;
+#pragma unroll
+  for (int a = 0; a < NA; ++a)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int off = 32 * a + 8 * (r >> 2) + (r & 3);
+      if ((win.right >= 0 && off < rlo) || (win.left >= 0 && off > rhi)) s[a][r] = -INFINITY;
+    }
+}
+
 // Phase 2 (VALU): mask (only when `edge`: the tile crosses an edge of the
 // window of some of the wave's keys), P = 2^(S c - L log2 e),
 // -dS = P (D - dP) from the accumulator, packed into MFMA operands.  st holds
@@ -199,19 +215,7 @@ template <class T, int NA>
 __device__ __forceinline__ void dkdv_probs(f32x16* s, f32x16* dp, const float* st, u32x4* pf, u32x4* dsf, bool edge,
                                            int i0, int krow, Win win, float c, int lane) {
   const int h = lane >> 5;
-  if (edge) {
-    // Query i sees the lane's key iff krow - right <= i <= krow + left;
-    // compared as offsets 32a + 8(r/4) + r%4 from i0 + 4h.
-    const int rlo = (win.right < 0 ? kUnbounded : krow - win.right) - i0 - 4 * h;
-    const int rhi = (win.left < 0 ? (1 << 30) : krow + win.left) - i0 - 4 * h;
-#pragma unroll
-    for (int a = 0; a < NA; ++a)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int off = 32 * a + 8 * (r >> 2) + (r & 3);
-        if ((win.right >= 0 && off < rlo) || (win.left >= 0 && off > rhi)) s[a][r] = -INFINITY;
-      }
-  }
+  if (edge) dkdv_mask<NA>(s, i0, krow, win, h);
 #pragma unroll
   for (int a = 0; a < NA; ++a)
 #pragma unroll
@@ -239,17 +243,7 @@ template <class T, int NA>
 __device__ __forceinline__ void dkdv_probs_p(f32x16* s, const float* st, u32x4* pf, bool edge, int i0, int krow,
                                              Win win, float c, int lane) {
   const int h = lane >> 5;
-  if (edge) {
-    const int rlo = (win.right < 0 ? kUnbounded : krow - win.right) - i0 - 4 * h;
-    const int rhi = (win.left < 0 ? (1 << 30) : krow + win.left) - i0 - 4 * h;
-#pragma unroll
-    for (int a = 0; a < NA; ++a)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int off = 32 * a + 8 * (r >> 2) + (r & 3);
-        if ((win.right >= 0 && off < rlo) || (win.left >= 0 && off > rhi)) s[a][r] = -INFINITY;
-      }
-  }
+  if (edge) dkdv_mask<NA>(s, i0, krow, win, h);
 #pragma unroll
   for (int a = 0; a < NA; ++a)
 #pragma unroll
