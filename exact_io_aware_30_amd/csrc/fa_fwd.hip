@@ -194,9 +194,9 @@ __device__ __forceinline__ void fwd_step(lds_char* lds, int t, int nt, int tb, c
 
 // ---------------------------------------------------------------------------
 // Software-pipelined form: per wave, the QK^T MFMAs of tile t+1 are issued
-// interleaved with the exponentials, row sums and bf16/fp16 packing of tile
-// t, and the PV MFMAs of tile t interleaved with the row maximum of tile
-// t+1, so one wave's VALU work runs under its own MFMAs.  Every tile needs K
+// interleaved with the exponentials and bf16/fp16 packing of tile t, and the
+// PV MFMAs of tile t interleaved with the row sums of tile t and the row
+// maximum of tile t+1, so one wave's VALU work runs under its own MFMAs.  Every tile needs K
 // of t+1 and V of t in LDS, so the ring is four tiles deep: tiles t, t+1 are
 // read while t+2 lands and t+3 is being issued into the buffer of t-1.
 // ---------------------------------------------------------------------------
@@ -344,8 +344,8 @@ __device__ __forceinline__ void fwd_pipe_step(lds_char* lds, int t, int nt, int 
     for (int x = 0; x < 2; ++x) vp[b][x] = (const lds_char*)(uintptr_t)(vb + voff[2 * b + x]);
 
   // Run 1: S^T(t+1) = K(t+1) Q^T, MFMA i = (kk = i / NA, a = i % NA), and
-  // p = 2^(S(t) c - mref), row sums and packing of tile t, E elements per
-  // MFMA.  K of tile t+1 is read even past the wave's (or the sequence's)
+  // p = 2^(S(t) c - mref) and packing of tile t (with kSumInPv off, also its
+  // row sums), E elements per MFMA.  K of tile t+1 is read even past the wave's (or the sequence's)
   // last tile: the buffer is in bounds and such scores are masked below.
   {
     constexpr int NM = NA * NKK, E = 16 * NA / NM, PRE = NM < kPipePre1 ? NM : kPipePre1;
@@ -387,7 +387,7 @@ __device__ __forceinline__ void fwd_pipe_step(lds_char* lds, int t, int nt, int 
     __builtin_amdgcn_sched_barrier(0);
 
     // Run 2: O^T += V(t)^T P(t)^T, MFMA i = (j = i / NB, b = i % NB), and the
-    // row maximum of S(t+1), F elements per MFMA.
+    // row maximum of S(t+1) and the row sums of P(t), F elements per MFMA.
     constexpr int NM2 = 2 * NA * NB, F = 16 * NA / NM2, PRE2 = NM2 < kPipePre2 ? NM2 : kPipePre2;
     u32x4 vop[NM2];
 #pragma unroll
