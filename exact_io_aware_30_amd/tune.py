@@ -54,6 +54,7 @@ SPACES = {
         "pipe_pre_2_2": ["-DFA_FWD_PIPE_PRE1=2", "-DFA_FWD_PIPE_PRE2=2"],
         "pipe_pre_4_3": ["-DFA_FWD_PIPE_PRE1=4", "-DFA_FWD_PIPE_PRE2=3"],
         "sum_in_qk": ["-DFA_FWD_SUM_IN_PV=0"],
+        "pipe_all": ["-DFA_FWD_PIPE=1"],
         "plain_sum_before_pv": ["-DFA_FWD_PLAIN_SUM_AFTER_PV=0"],
     },
     "dkdv": {
