@@ -14,7 +14,7 @@ both halved under the causal mask.
                                 head of each (a markdown table, then one JSON
                                 line per workload), then the forward's MFMA
                                 and vector-ALU ceilings per head dimension
-                                from rates measured by libfa_probe.so
+                                from rates measured by libfa_rates.so
     python bench.py --sweep     bf16 causal d=128, B=1, H=16, N = 1K .. 64K:
                                 one pass of each kernel per N (for hardware
                                 counters) and its time
@@ -227,88 +227,48 @@ def report():
     ceilings(rows)
 
 
-PROBE_LIBRARY = os.path.join(ROOT, "exact_io_aware_30_amd", "libfa_probe.so")
+RATES_LIBRARY = os.path.join(ROOT, "exact_io_aware_30_amd", "libfa_rates.so")
 
 
 def probe_rates():
-    """Instruction rates measured on the GPU by libfa_probe.so: dense bf16
-    MFMA TFLOP/s, v_exp_f32 and v_fma_f32 lane-results per second, and the
-    forward's per-score vector sequence in scores per second (1e12 units)."""
+    """Instruction rates measured on the GPU by libfa_rates.so: dense bf16
+    MFMA TFLOP/s, v_exp_f32 and v_fma_f32 lane-results per second, the
+    forward's per-score vector sequence in scores per second (1e12 units),
+    and the interleaved MFMA + vector loop's three timings."""
     import ctypes
 
     import torch
 
-    lib = ctypes.CDLL(PROBE_LIBRARY)
-    lib.fa_probe_rates.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.c_int, ctypes.c_void_p]
-    lib.fa_probe_rates.restype = ctypes.c_int
-    out = (ctypes.c_double * 10)()
-    rc = lib.fa_probe_rates(out, 10, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    lib = ctypes.CDLL(RATES_LIBRARY)
+    lib.fa_rates_valu.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.c_int, ctypes.c_void_p]
+    lib.fa_rates_valu.restype = ctypes.c_int
+    out = (ctypes.c_double * 8)()
+    rc = lib.fa_rates_valu(out, 8, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
     if rc != 0:
-        raise RuntimeError(f"fa_probe_rates failed (status {rc})")
+        raise RuntimeError(f"fa_rates_valu failed (status {rc})")
     return {"mfma_bf16_tflops": out[0], "exp_tlanes_per_s": out[1], "fma_tlanes_per_s": out[2],
             "softmax_tscores_per_s": out[3], "compute_units": int(out[4]),
             "pair_mfma_ms": out[5], "pair_valu_ms": out[6], "pair_both_ms": out[7],
-            "pair_overlap": overlap_fraction(out[5], out[6], out[7]),
-            "pair_agpr_mfma_ms": out[8], "pair_agpr_both_ms": out[9],
-            "pair_agpr_overlap": overlap_fraction(out[8], out[6], out[9])}
+            "pair_overlap": overlap_fraction(out[5], out[6], out[7])}
 
 
 def probe_lds():
-    """LDS rates measured by libfa_probe.so: ds_read_b128 alone (TB/s over
+    """LDS rates measured by libfa_rates.so: ds_read_b128 alone (TB/s over
     the chip), and dense bf16 MFMA TFLOP/s with one, two or no 1 KiB operands
     read from LDS per MFMA."""
     import ctypes
 
     import torch
 
-    lib = ctypes.CDLL(PROBE_LIBRARY)
-    lib.fa_probe_lds.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.c_int, ctypes.c_void_p]
-    lib.fa_probe_lds.restype = ctypes.c_int
-    out = (ctypes.c_double * 8)()
-    rc = lib.fa_probe_lds(out, 8, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    lib = ctypes.CDLL(RATES_LIBRARY)
+    lib.fa_rates_lds.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.c_int, ctypes.c_void_p]
+    lib.fa_rates_lds.restype = ctypes.c_int
+    out = (ctypes.c_double * 6)()
+    rc = lib.fa_rates_lds(out, 6, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
     if rc != 0:
-        raise RuntimeError(f"fa_probe_lds failed (status {rc})")
+        raise RuntimeError(f"fa_rates_lds failed (status {rc})")
     return {"lds_read_tbs": out[0], "mfma_lds1_tflops": out[1], "mfma_lds2_tflops": out[2],
-            "mfma_regs_tflops": out[3], "compute_units": int(out[4]), "lds_read_ms": out[5],
-            "mfma_chain1_tflops": out[6], "mfma_chain2_tflops": out[7]}
-
-
-def probe_wave_simd():
-    """SIMD of each wave of a 512-lane workgroup, read from the hardware by
-    libfa_probe.so: {"simd_of_wave": [8 ids of workgroup 0], "same_in_all":
-    whether every workgroup maps wave w to the same SIMD number,
-    "shared_pairs": the wave pairs of workgroup 0 that share a SIMD,
-    "pairs_same_in_all": whether every workgroup pairs its waves that way}."""
-    import ctypes
-
-    import torch
-
-    lib = ctypes.CDLL(PROBE_LIBRARY)
-    lib.fa_probe_wave_simd.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.c_int, ctypes.c_void_p]
-    lib.fa_probe_wave_simd.restype = ctypes.c_int
-    n = 8 * 1024
-    out = (ctypes.c_int * n)()
-    got = lib.fa_probe_wave_simd(out, n, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
-    if got < 8:
-        raise RuntimeError(f"fa_probe_wave_simd failed (status {got})")
-    return wave_simd_summary(list(out[:got]))
-
-
-def wave_simd_summary(ids):
-    """Summarise (XCC_ID << 8 | CU_ID << 4 | SIMD_ID) per wave, 8 waves per
-    workgroup; "xcd_round_robin" is the share of workgroups g placed on XCD
-    (g + x0) mod 8, x0 being workgroup 0's XCD."""
-    groups = [ids[i:i + 8] for i in range(0, len(ids) - len(ids) % 8, 8)]
-    simd = [[x & 3 for x in g] for g in groups]
-    same_cu = all(len({x >> 4 for x in g}) == 1 for g in groups)
-    xcd = [g[0] >> 8 for g in groups]
-    rr = sum(1 for i, x in enumerate(xcd) if x == (xcd[0] + i) % 8) / max(1, len(xcd))
-    def pairs(s):
-        return sorted((a, b) for a in range(8) for b in range(a + 1, 8) if s[a] == s[b])
-
-    return {"simd_of_wave": simd[0], "same_in_all": all(s == simd[0] for s in simd), "one_cu_per_group": same_cu,
-            "shared_pairs": pairs(simd[0]), "pairs_same_in_all": all(pairs(s) == pairs(simd[0]) for s in simd),
-            "groups": len(groups), "xcd_first_16": xcd[:16], "xcd_round_robin": rr}
+            "mfma_regs_tflops": out[3], "compute_units": int(out[4]), "lds_read_ms": out[5]}
 
 
 def overlap_fraction(t_mfma: float, t_valu: float, t_both: float) -> float:
@@ -349,17 +309,12 @@ def ceilings(rows=()):
         print(f"| {d} | {c['mfma_tflops']:.0f} | {c['valu_tflops']:.0f} | {c['serial_tflops']:.0f} | {meas or '-'} |")
         out.append({k: (round(v, 1) if isinstance(v, float) else v) for k, v in c.items()})
     lds = probe_lds()
-    ws = probe_wave_simd()
     print(f"LDS: ds_read_b128 alone {lds['lds_read_tbs']:.1f} TB/s over {lds['compute_units']} CUs; dense bf16 MFMA "
           f"{lds['mfma_regs_tflops']:.0f} TFLOP/s with operands in registers, {lds['mfma_lds1_tflops']:.0f} with one "
           f"1 KiB LDS operand per MFMA, {lds['mfma_lds2_tflops']:.0f} with two")
-    print(f"wave placement in a 512-lane workgroup: SIMD of waves 0..7 = {ws['simd_of_wave']} "
-          f"(pairs sharing a SIMD: {ws['shared_pairs']}, the same pairs in all {ws['groups']} workgroups: "
-          f"{ws['pairs_same_in_all']}); XCD of workgroups 0..15 = {ws['xcd_first_16']}, share placed round-robin "
-          f"over the 8 XCDs: {ws['xcd_round_robin']:.3f}")
     emit({"probe_rates": {k: (round(v, 3) if isinstance(v, float) else v) for k, v in rates.items()},
           "probe_lds": {k: (round(v, 3) if isinstance(v, float) else v) for k, v in lds.items()},
-          "wave_placement": ws, "forward_ceilings": out})
+          "forward_ceilings": out})
 
 
 SWEEP_N = (1024, 2048, 4096, 8192, 16384, 32768, 65536)

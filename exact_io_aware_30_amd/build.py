@@ -23,10 +23,10 @@ LIB_NAME = "libfa_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
 SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_api.cpp"]
-# Instruction-rate microbenchmarks for the benchmark's ceilings: a library of
+# Instruction-rate loops for the benchmark's measured ceilings: a library of
 # their own, so that the attention library holds only the attention path.
-PROBE_SOURCES = ["fa_probe.hip"]
-PROBE_LIB_PATH = os.path.join(HERE, "libfa_probe.so")
+RATES_SOURCES = ["fa_rates.hip"]
+RATES_LIB_PATH = os.path.join(HERE, "libfa_rates.so")
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950",
@@ -58,14 +58,14 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     objs = {}
     cmds = []
-    for src in SOURCES + PROBE_SOURCES:
+    for src in SOURCES + RATES_SOURCES:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
         objs[src] = obj
         cmds.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
     with concurrent.futures.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         for f in [ex.submit(_run, c, verbose) for c in cmds]:
             f.result()
-    for srcs, path in ((SOURCES, LIB_PATH), (PROBE_SOURCES, PROBE_LIB_PATH)):
+    for srcs, path in ((SOURCES, LIB_PATH), (RATES_SOURCES, RATES_LIB_PATH)):
         tmp = path + ".tmp"
         _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *(objs[s] for s in srcs), "-o", tmp], verbose)
         os.replace(tmp, path)

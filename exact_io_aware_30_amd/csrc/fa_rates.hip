@@ -1,7 +1,7 @@
-// Instruction-rate microbenchmarks (see include/fa_probe.h).  Four loops,
-// one workgroup of 512 lanes per compute unit, each writing one float per
-// lane so that nothing is optimised away.
-#include "../../include/fa_probe.h"
+// Instruction-rate loops behind the benchmark's measured ceilings (see
+// fa_rates.h).  One workgroup of 512 lanes per compute unit, each loop
+// writing one float per lane so that nothing is optimised away.
+#include "fa_rates.h"
 
 #include <hip/hip_runtime.h>
 
@@ -17,8 +17,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 constexpr int kThreads = 512;  // 8 waves: 2 per SIMD
 constexpr int kRegs = 16;      // independent chains per lane in the VALU loops
 
-enum Kind { kMfma = 0, kExp = 1, kFma = 2, kSoftmax = 3, kPairMfma = 4, kPairValu = 5, kPair = 6, kPairAgprMfma = 7,
-            kPairAgpr = 8 };
+enum Kind { kMfma = 0, kExp = 1, kFma = 2, kSoftmax = 3, kPairMfma = 4, kPairValu = 5, kPair = 6 };
 
 // One score of the forward's per-score vector sequence on chain x; every
 // second score also a max3 and a bf16 pack of the pair.
@@ -54,23 +53,14 @@ __global__ __launch_bounds__(kThreads) void probe_kernel(float* out, int iters, 
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
       for (int k = 0; k < kRegs / 2; ++k) {
-        if constexpr (KIND == kPairAgprMfma || KIND == kPairAgpr)
-          // The accumulator in AGPRs (the MFMA-only register file).
-          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc[k & 3]) : "v"(a), "v"(b));
-        else if constexpr (KIND != kPairValu)
+        if constexpr (KIND != kPairValu)
           acc[k & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[k & 3], 0, 0, 0);
-        if constexpr (KIND != kPairMfma && KIND != kPairAgprMfma) {
+        if constexpr (KIND != kPairMfma) {
           score_step(x, 2 * k, c, sum, mx, pk);
           score_step(x, 2 * k + 1, c, sum, mx, pk);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-    }
-    if constexpr (KIND == kPairAgprMfma || KIND == kPairAgpr) {
-      // The compiler does not see the assembly MFMAs: wait states between
-      // their last result and the reads below, with every accumulator tied
-      // to the statement.
-      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]));
     }
 #pragma unroll
     for (int j = 0; j < kRegs; ++j) r += x[j];
@@ -148,7 +138,7 @@ hipError_t time_kernel(float* out, int grid, int iters, hipStream_t st, float* b
 }
 
 // ---------------------------------------------------------------------------
-// LDS probes.  Every kernel of the library feeds each 32x32x16 MFMA one
+// LDS loops.  Every kernel of the library feeds each 32x32x16 MFMA one
 // 1 KiB operand from LDS (a K, V, Q or dO tile read by the 64 lanes of a
 // wave); these loops measure how fast LDS delivers such reads, alone and as
 // MFMA operands, with the same 8 waves per CU.
@@ -156,59 +146,6 @@ constexpr int kLdsBytes = 32768;  // one 32 KiB buffer; lanes read 16-byte chunk
 constexpr int kLdsSteps = 8;      // reads (and MFMAs) per loop iteration
 
 enum LdsKind { kLdsRead = 0, kLdsMfma1 = 1, kLdsMfma2 = 2 };
-
-// MFMAs from registers on CHAINS accumulators in rotation: with one, each
-// MFMA takes the previous one's result as its accumulator input.
-template <int CHAINS>
-__global__ __launch_bounds__(kThreads) void chain_kernel(float* out, int iters) {
-  const int tid = threadIdx.x;
-  bf16x8 a, b;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    a[i] = (__bf16)(1e-3f * (tid + i));
-    b[i] = (__bf16)(1e-3f * (tid - i));
-  }
-  f32x16 acc[CHAINS] = {};
-  for (int it = 0; it < iters; ++it) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) acc[k % CHAINS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[k % CHAINS], 0, 0, 0);
-  }
-  float r = 0.f;
-#pragma unroll
-  for (int c = 0; c < CHAINS; ++c)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) r += acc[c][i];
-  out[blockIdx.x * kThreads + tid] = r;
-}
-
-template <int CHAINS>
-hipError_t time_chain(float* out, int grid, int iters, hipStream_t st, float* best_ms) {
-  hipEvent_t e0, e1;
-  hipError_t err = hipEventCreate(&e0);
-  if (err != hipSuccess) return err;
-  if ((err = hipEventCreate(&e1)) != hipSuccess) {
-    (void)hipEventDestroy(e0);
-    return err;
-  }
-  hipLaunchKernelGGL((chain_kernel<CHAINS>), dim3(grid), dim3(kThreads), 0, st, out, iters);  // warm-up
-  float best = 1e30f;
-  for (int rep = 0; rep < 3 && err == hipSuccess; ++rep) {
-    err = hipEventRecord(e0, st);
-    if (err == hipSuccess) {
-      hipLaunchKernelGGL((chain_kernel<CHAINS>), dim3(grid), dim3(kThreads), 0, st, out, iters);
-      err = hipGetLastError();
-    }
-    if (err == hipSuccess) err = hipEventRecord(e1, st);
-    if (err == hipSuccess) err = hipEventSynchronize(e1);
-    float ms = 0.f;
-    if (err == hipSuccess) err = hipEventElapsedTime(&ms, e0, e1);
-    if (err == hipSuccess) best = std::min(best, ms);
-  }
-  (void)hipEventDestroy(e0);
-  (void)hipEventDestroy(e1);
-  *best_ms = best;
-  return err;
-}
 
 typedef unsigned u32x4p __attribute__((ext_vector_type(4)));
 
@@ -300,22 +237,9 @@ hipError_t time_lds(float* out, int grid, int iters, hipStream_t st, float* best
   return err;
 }
 
-// Which SIMD each wave of a 512-lane workgroup runs on: the SIMD_ID field
-// (bits 5:4) of the HW_ID hardware register, the CU_ID field (11:8), and the
-// XCD (accelerator complex die) from the XCC_ID register (bits 3:0).
-__global__ __launch_bounds__(kThreads) void wave_simd_kernel(int* out) {
-  const unsigned hw = __builtin_amdgcn_s_getreg((31 << 11) | (0 << 6) | 4);  // HW_ID, all 32 bits
-  unsigned xcc;
-  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
-  const int tid = threadIdx.x;
-  if ((tid & 63) == 0)
-    out[blockIdx.x * (kThreads / 64) + (tid >> 6)] =
-        (int)((xcc & 15u) << 8 | ((hw >> 8) & 15u) << 4 | ((hw >> 4) & 3u));
-}
-
 }  // namespace
 
-extern "C" int fa_probe_lds(double* out, int n, void* stream) {
+extern "C" int fa_rates_lds(double* out, int n, void* stream) {
   if (!out || n < 6) return -1;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   int dev = 0, cus = 0;
@@ -329,9 +253,6 @@ extern "C" int fa_probe_lds(double* out, int n, void* stream) {
   if (err == hipSuccess) err = time_lds<kLdsMfma1>(buf, cus, iters, st, &ms[1]);
   if (err == hipSuccess) err = time_lds<kLdsMfma2>(buf, cus, iters, st, &ms[2]);
   if (err == hipSuccess) err = time_kernel<kMfma>(buf, cus, iters * kLdsSteps / 4, st, &ms[3]);
-  float chain_ms[2] = {0, 0};
-  if (n >= 8 && err == hipSuccess) err = time_chain<1>(buf, cus, iters, st, &chain_ms[0]);
-  if (n >= 8 && err == hipSuccess) err = time_chain<2>(buf, cus, iters, st, &chain_ms[1]);
   (void)hipFree(buf);
   if (err != hipSuccess) return -4;
   const double waves = (double)cus * (kThreads / 64), steps = waves * iters * kLdsSteps;
@@ -341,31 +262,10 @@ extern "C" int fa_probe_lds(double* out, int n, void* stream) {
   out[3] = steps * 32768.0 / (ms[3] * 1e-3) / 1e12;           // the same number of MFMAs from registers, TFLOP/s
   out[4] = cus;
   out[5] = ms[0];
-  if (n >= 8) {
-    out[6] = steps * 32768.0 / (chain_ms[0] * 1e-3) / 1e12;  // one dependent accumulator chain, TFLOP/s
-    out[7] = steps * 32768.0 / (chain_ms[1] * 1e-3) / 1e12;  // two chains
-  }
   return 0;
 }
 
-extern "C" int fa_probe_wave_simd(int* out, int n, void* stream) {
-  if (!out || n < 1) return -1;
-  const hipStream_t st = static_cast<hipStream_t>(stream);
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return -4;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) return -4;
-  const int total = cus * (kThreads / 64);
-  int* buf = nullptr;
-  if (hipMalloc(&buf, (size_t)total * sizeof(int)) != hipSuccess) return -4;
-  hipLaunchKernelGGL(wave_simd_kernel, dim3(cus), dim3(kThreads), 0, st, buf);
-  hipError_t err = hipGetLastError();
-  if (err == hipSuccess) err = hipMemcpyAsync(out, buf, (size_t)std::min(n, total) * sizeof(int), hipMemcpyDeviceToHost, st);
-  if (err == hipSuccess) err = hipStreamSynchronize(st);
-  (void)hipFree(buf);
-  return err == hipSuccess ? std::min(n, total) : -4;
-}
-
-extern "C" int fa_probe_rates(double* out, int n, void* stream) {
+extern "C" int fa_rates_valu(double* out, int n, void* stream) {
   if (!out || n < 8) return -1;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   int dev = 0, cus = 0;
@@ -375,7 +275,7 @@ extern "C" int fa_probe_rates(double* out, int n, void* stream) {
   if (hipMalloc(&buf, (size_t)cus * kThreads * sizeof(float)) != hipSuccess) return -4;
   // Iteration counts give each loop a few milliseconds.
   const int it_mfma = 20000, it_valu = 4000;
-  float ms[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
+  float ms[7] = {0, 0, 0, 0, 0, 0, 0};
   hipError_t err = time_kernel<kMfma>(buf, cus, it_mfma, st, &ms[0]);
   if (err == hipSuccess) err = time_kernel<kExp>(buf, cus, it_valu, st, &ms[1]);
   if (err == hipSuccess) err = time_kernel<kFma>(buf, cus, it_valu, st, &ms[2]);
@@ -383,8 +283,6 @@ extern "C" int fa_probe_rates(double* out, int n, void* stream) {
   if (err == hipSuccess) err = time_kernel<kPairMfma>(buf, cus, it_valu, st, &ms[4]);
   if (err == hipSuccess) err = time_kernel<kPairValu>(buf, cus, it_valu, st, &ms[5]);
   if (err == hipSuccess) err = time_kernel<kPair>(buf, cus, it_valu, st, &ms[6]);
-  if (n >= 10 && err == hipSuccess) err = time_kernel<kPairAgprMfma>(buf, cus, it_valu, st, &ms[7]);
-  if (n >= 10 && err == hipSuccess) err = time_kernel<kPairAgpr>(buf, cus, it_valu, st, &ms[8]);
   (void)hipFree(buf);
   if (err != hipSuccess) return -4;
   const double waves = (double)cus * (kThreads / 64), lanes = (double)cus * kThreads;
@@ -396,9 +294,5 @@ extern "C" int fa_probe_rates(double* out, int n, void* stream) {
   out[5] = ms[4];  // the interleaved pair: MFMA half alone, ms
   out[6] = ms[5];  //                       vector half alone, ms
   out[7] = ms[6];  //                       both, ms
-  if (n >= 10) {
-    out[8] = ms[7];  // the pair with AGPR accumulators: MFMA half alone, ms
-    out[9] = ms[8];  //                                  both, ms
-  }
   return 0;
 }

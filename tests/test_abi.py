@@ -266,30 +266,25 @@ def test_workspace_size_rule():
     assert binding.fa_bwd_varlen_workspace_size(24, 4077, 55662, 16, 1, 128) == 2 * 4 * 55662 * 128 * 4
 
 
-def test_probe_library_exports_and_rejects():
-    """libfa_probe.so (measurement support) exports what include/fa_probe.h
+def test_rates_library_exports_and_rejects():
+    """libfa_rates.so (measurement support) exports what csrc/fa_rates.h
     declares, and rejects bad arguments before touching the GPU."""
     import ctypes
 
-    from exact_io_aware_30_amd.build import PROBE_LIB_PATH
+    from exact_io_aware_30_amd.build import CSRC, RATES_LIB_PATH
 
-    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(os.path.dirname(HEADER), "fa_probe.h")).read(), flags=re.S)
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(CSRC, "fa_rates.h")).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
-    assert names == ["fa_probe_lds", "fa_probe_rates", "fa_probe_wave_simd"]
-    out = subprocess.run(["nm", "-D", "--defined-only", PROBE_LIB_PATH], capture_output=True, text=True).stdout
+    assert names == ["fa_rates_lds", "fa_rates_valu"]
+    out = subprocess.run(["nm", "-D", "--defined-only", RATES_LIB_PATH], capture_output=True, text=True).stdout
     assert set(names) <= set(re.findall(r"\bT (fa_\w+)$", out, flags=re.M))
-    lib = ctypes.CDLL(PROBE_LIB_PATH)
-    lib.fa_probe_rates.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.c_int, ctypes.c_void_p]
-    lib.fa_probe_rates.restype = ctypes.c_int
+    lib = ctypes.CDLL(RATES_LIB_PATH)
+    lib.fa_rates_valu.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.c_int, ctypes.c_void_p]
+    lib.fa_rates_valu.restype = ctypes.c_int
     buf = (ctypes.c_double * 8)()
-    assert lib.fa_probe_rates(None, 8, None) == -1
-    assert lib.fa_probe_rates(buf, 7, None) == -1
-    lib.fa_probe_lds.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.c_int, ctypes.c_void_p]
-    lib.fa_probe_lds.restype = ctypes.c_int
-    assert lib.fa_probe_lds(None, 6, None) == -1
-    assert lib.fa_probe_lds(buf, 5, None) == -1
-    lib.fa_probe_wave_simd.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.c_int, ctypes.c_void_p]
-    lib.fa_probe_wave_simd.restype = ctypes.c_int
-    ibuf = (ctypes.c_int * 8)()
-    assert lib.fa_probe_wave_simd(None, 8, None) == -1
-    assert lib.fa_probe_wave_simd(ibuf, 0, None) == -1
+    assert lib.fa_rates_valu(None, 8, None) == -1
+    assert lib.fa_rates_valu(buf, 7, None) == -1
+    lib.fa_rates_lds.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.c_int, ctypes.c_void_p]
+    lib.fa_rates_lds.restype = ctypes.c_int
+    assert lib.fa_rates_lds(None, 6, None) == -1
+    assert lib.fa_rates_lds(buf, 5, None) == -1

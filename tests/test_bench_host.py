@@ -150,22 +150,3 @@ def test_overlap_fraction():
     assert bench.overlap_fraction(1.0, 0.5, 1.5) == pytest.approx(0.0)  # one after the other
     assert bench.overlap_fraction(1.0, 0.5, 1.0) == pytest.approx(1.0)  # the shorter fully hidden
     assert bench.overlap_fraction(1.0, 0.8, 1.4) == pytest.approx(0.5)
-
-
-def test_wave_simd_summary():
-    """The placement summary reads SIMD_ID from the low two bits and CU_ID
-    from the bits above, per workgroup of 8 waves."""
-    rr = [(3 << 8) | (5 << 4) | (w % 4) for w in range(8)] + [(4 << 8) | (9 << 4) | (w % 4) for w in range(8)]
-    s = bench.wave_simd_summary(rr)
-    assert s["xcd_first_16"] == [3, 4] and s["xcd_round_robin"] == 1.0
-    assert s["simd_of_wave"] == [0, 1, 2, 3, 0, 1, 2, 3]
-    assert s["same_in_all"] and s["one_cu_per_group"] and s["groups"] == 2
-    assert s["shared_pairs"] == [(0, 4), (1, 5), (2, 6), (3, 7)] and s["pairs_same_in_all"]
-    # second workgroup numbers its SIMDs differently but pairs the same waves
-    rr[8:16] = [(3 << 8) | (9 << 4) | ((w + 1) % 4) for w in range(8)]
-    s = bench.wave_simd_summary(rr)
-    assert not s["same_in_all"] and s["pairs_same_in_all"] and s["xcd_round_robin"] == 0.5
-    rr[8 + 1] = (3 << 8) | (9 << 4) | 1  # second workgroup: waves 0 and 1 on one SIMD
-    rr[3] = (6 << 4) | 3      # first workgroup split over two CUs
-    s = bench.wave_simd_summary(rr)
-    assert not s["pairs_same_in_all"] and not s["one_cu_per_group"]

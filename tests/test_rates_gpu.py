@@ -1,12 +1,10 @@
-"""The instruction-rate probes behind the benchmark's ceilings, on the GPU:
+"""The instruction-rate loops behind the benchmark's ceilings, on the GPU:
 every rate positive and in a range the MI355X can reach (dense bf16 MFMA
 under the published 2.5 PFLOP/s; an exponential no faster than an FMA; the
 per-score sequence, which holds an exponential and several other vector
 instructions, slower than either; the interleaved MFMA + vector loop no
 faster than its longer half and no slower than both halves; LDS-fed MFMA
-loops no faster than the register-fed one; MFMAs on one or two dependent
-accumulator chains under the peak; every wave of a 512-lane
-workgroup on one compute unit, two per SIMD)."""
+loops no faster than the register-fed one)."""
 
 import os
 import sys
@@ -20,7 +18,7 @@ import bench  # noqa: E402
 pytestmark = pytest.mark.gpu
 
 
-def test_probe_rates_are_plausible():
+def test_rates_are_plausible():
     r = bench.probe_rates()
     print(r, flush=True)
     assert r["compute_units"] >= 1
@@ -32,7 +30,7 @@ def test_probe_rates_are_plausible():
     assert 0.95 * longer <= r["pair_both_ms"] <= 1.05 * (r["pair_mfma_ms"] + r["pair_valu_ms"])
 
 
-def test_probe_lds_is_plausible():
+def test_lds_rates_are_plausible():
     r = bench.probe_lds()
     print(r, flush=True)
     assert r["compute_units"] >= 1
@@ -40,16 +38,3 @@ def test_probe_lds_is_plausible():
     assert 200.0 < r["mfma_regs_tflops"] < 2600.0
     # an operand read from LDS cannot make the matrix core faster (5% timing slack)
     assert 0 < r["mfma_lds2_tflops"] <= 1.05 * r["mfma_lds1_tflops"] <= 1.05 * 1.05 * r["mfma_regs_tflops"]
-    # dependent accumulator chains: a positive rate under the published peak
-    # (measured at the full MFMA rate: a chained MFMA does not wait for the
-    # previous one's result)
-    assert 0 < r["mfma_chain1_tflops"] < 2600.0 and 0 < r["mfma_chain2_tflops"] < 2600.0
-
-
-def test_wave_placement():
-    r = bench.probe_wave_simd()
-    print(r, flush=True)
-    assert r["one_cu_per_group"]
-    assert sorted(r["simd_of_wave"]) == [0, 0, 1, 1, 2, 2, 3, 3]
-    assert r["pairs_same_in_all"]
-    assert all(0 <= x < 8 for x in r["xcd_first_16"])
