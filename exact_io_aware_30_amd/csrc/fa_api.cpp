@@ -178,9 +178,12 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGNMENT;
   const long long tb = static_cast<long long>(H) * T * d * 2, rb = static_cast<long long>(H) * T * 4;
   const long long kvb = static_cast<long long>(Hkv) * T * d * 2;
-  const Range ins[3] = {range_of(q, tb), range_of(k, kvb), range_of(v, kvb)};
+  // The offsets are an input too: an output over them would be read by some
+  // workgroups while others write it.
+  const Range ins[4] = {range_of(q, tb), range_of(k, kvb), range_of(v, kvb),
+                        range_of(cu_seqlens, (static_cast<long long>(B) + 1) * 4)};
   const Range outs[2] = {range_of(o, tb), range_of(lse, rb)};
-  if ((rc = check_alias(outs, 2, ins, 3))) return rc;
+  if ((rc = check_alias(outs, 2, ins, 4))) return rc;
   fa::FwdArgs a{q, k, v, o, lse, B, H, max_seqlen, d, Hkv, scale, window_left, window_right, dt == FA_BF16};
   a.cu = cu_seqlens;
   a.T = T;
@@ -203,10 +206,10 @@ int fa_bwd_varlen_ws(const void* q, const void* k, const void* v, const void* dO
   const int gs = fitted_splits(B, Hkv, H / Hkv, max_seqlen, static_cast<long long>(Hkv) * T, d, workspace_bytes);
   const long long used = split_bytes(gs, static_cast<long long>(Hkv) * T, d);
   if (used > 0 && !aligned16(workspace)) return FA_ERR_ALIGNMENT;
-  const Range ins[6] = {range_of(q, tb), range_of(k, kvb), range_of(v, kvb), range_of(dO, tb), range_of(lse, rb),
-                        range_of(delta, rb)};
+  const Range ins[7] = {range_of(q, tb), range_of(k, kvb), range_of(v, kvb), range_of(dO, tb), range_of(lse, rb),
+                        range_of(delta, rb), range_of(cu_seqlens, (static_cast<long long>(B) + 1) * 4)};
   const Range outs[4] = {range_of(dq, tb), range_of(dk, kvb), range_of(dv, kvb), range_of(workspace, used)};
-  if ((rc = check_alias(outs, used > 0 ? 4 : 3, ins, 6))) return rc;
+  if ((rc = check_alias(outs, used > 0 ? 4 : 3, ins, 7))) return rc;
   fa::BwdArgs a = bwd_args(q, k, v, dO, lse, delta, dq, dk, dv, B, H, Hkv, max_seqlen, d, scale, window_left,
                            window_right, dt);
   a.cu = cu_seqlens;

@@ -193,6 +193,8 @@ int fa_bwd_dq_ex(const void* q, const void* k, const void* v, const void* dO,
  * those of a batch of max_seqlen rows.  The pre-pass is fa_bwd_preprocess
  * with B = 1, H, N = T.  Null cu_seqlens, B, max_seqlen or T below 1 return
  * FA_ERR_INVALID_ARG; a cu_seqlens not 4-byte aligned FA_ERR_ALIGNMENT.
+ * cu_seqlens is an input: an output or workspace that overlaps its B + 1
+ * offsets returns FA_ERR_ALIAS.
  */
 int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o,
                   float* lse, const int* cu_seqlens, int B, int max_seqlen,

@@ -208,6 +208,16 @@ def test_varlen_rejects(p):
     assert f(wl=-7) == INVALID
     assert f(cu=p[5] + 2) == ALIGN
     assert lib.fa_bwd_varlen(*p[:9], 0, 2, 32, 64, 1, 1, 64, 0.125, -1, 0, 1, None) == INVALID
+    # The offsets are an input: no output (nor the workspace) may cover them.
+    assert f(cu=p[3]) == ALIAS                     # o over the offsets
+    assert f(cu=p[4] + 64) == ALIAS                # lse over the offsets
+    cu = p[10]
+    assert lib.fa_bwd_varlen(*p[:6], cu, p[7], p[8], cu, 2, 32, 64, 1, 1, 64, 0.125, -1, 0, 1, None) == ALIAS  # dq
+    assert lib.fa_bwd_varlen(*p[:7], cu - 16, p[8], cu, 2, 32, 64, 1, 1, 64, 0.125, -1, 0, 1, None) == ALIAS  # dk
+    vneed = binding.fa_bwd_varlen_workspace_size(2, 32, 64, 8, 1, 32)
+    assert vneed > 0
+    assert lib.fa_bwd_varlen_ws(*p[:9], cu, 2, 32, 64, 8, 1, 32, 0.125, -1, 0, 1, cu - 4096, vneed,
+                                None) == ALIAS  # workspace
 
 
 def test_binding_rejects_host_tensors():
