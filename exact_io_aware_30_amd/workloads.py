@@ -82,6 +82,42 @@ def make_inputs(w: Workload, device="cpu"):
     return tuple(out)
 
 
+RISE_TILE = 64      # keys per block of the staircase below
+RISE_STEP = 12.0    # base-2 units the scores rise at each step block
+RISE_QCOORD = 8.0   # value of every query's last coordinate
+
+
+def rise_steps(n: int):
+    """Key blocks (of RISE_TILE keys) at which the staircase of
+    make_rising_inputs steps up: 1, 2, the middle one and the last one."""
+    nt = (n + RISE_TILE - 1) // RISE_TILE
+    return sorted({t for t in (1, 2, nt // 2, nt - 1) if 1 <= t <= nt - 1})
+
+
+def make_rising_inputs(w: Workload, device="cpu"):
+    """Inputs whose scores climb in steps along the key axis, so that every
+    query row's running maximum moves several times after its first key
+    block.  Start from make_inputs(w); set every query's last coordinate to
+    RISE_QCOORD and the last coordinate of key j to RISE_STEP * s(j) /
+    (RISE_QCOORD * scale * log2 e), s(j) the number of steps at or before
+    key block j // RISE_TILE; round to the dtype.  The last coordinate then
+    adds about RISE_STEP * s(j) base-2 units to every score of key j, on top
+    of the N(0, 1) part of the other d - 1 coordinates (keys of block 0 add
+    nothing)."""
+    q, k, v, do = make_inputs(w)
+    q, k = q.float(), k.float()
+    c = w.scale * math.log2(math.e)
+    steps = rise_steps(w.N)
+    blk = torch.arange(w.N) // RISE_TILE
+    s = torch.zeros(w.N)
+    for t in steps:
+        s += (blk >= t).float()
+    q[..., -1] = RISE_QCOORD
+    k[..., -1] = (RISE_STEP * s / (RISE_QCOORD * c)).view(1, 1, w.N)
+    dt = w.torch_dtype
+    return q.to(dt).to(device), k.to(dt).to(device), v.to(device), do.to(device)
+
+
 def make_tensor(shape, dtype: str, seed: int, device="cpu", scale: float = 1.0):
     """One seeded N(0,1)*scale fp32 draw rounded to ``dtype``."""
     g = torch.Generator(device="cpu")

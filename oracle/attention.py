@@ -256,12 +256,17 @@ def dq_rows(qh, kh, vh, doh, scale, causal, rows):
     return dq
 
 
-def dkdv_cols(qh, kh, vh, doh, scale, causal, cols, row_block=2048):
+def dkdv_cols(qh, kh, vh, doh, scale, causal, cols, row_block=2048, rows=None):
     """dK and dV of the given key rows (columns of P) of one head.
 
     Column j of P involves every query row i that sees key j (i >= j under
     the causal mask), and each such row needs its own full softmax, so this
     walks those rows in blocks of ``row_block`` with their full key range.
+
+    ``rows`` = (r_lo, r_hi) restricts the walk to query rows [r_lo, r_hi):
+    the result is then those rows' share of the sums dV_j = sum_i P_ij dO_i
+    and dK_j = scale sum_i dS_ij Q_i, so the shares of disjoint ranges that
+    cover [0, N) add up to the whole gradient.
     """
     qh, kh, vh, doh = _as64(qh), _as64(kh), _as64(vh), _as64(doh)
     N, d = qh.shape
@@ -270,9 +275,10 @@ def dkdv_cols(qh, kh, vh, doh, scale, causal, cols, row_block=2048):
     dv = np.zeros((cols.size, d))
     if cols.size == 0:
         return dk, dv
-    first = int(cols.min()) if causal else 0
-    for r0 in range(first, N, row_block):
-        r1 = min(N, r0 + row_block)
+    lo, hi = (0, N) if rows is None else (max(0, int(rows[0])), min(N, int(rows[1])))
+    first = max(lo, int(cols.min())) if causal else lo
+    for r0 in range(first, hi, row_block):
+        r1 = min(hi, r0 + row_block)
         nk = _key_extent(causal, r1, N)
         p, _ = _probs(_scores(qh, kh, scale, causal, r0, r1, nk))
         dob = doh[r0:r1]

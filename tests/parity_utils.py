@@ -69,3 +69,43 @@ def assert_grad(dtype, name, g, g_ref, what=""):
     e = err_rel(g, g_ref)
     say(f"  {what} {name} max-abs/max-ref {e:.3e} (tol {TOL_G[dtype]:g})")
     assert e <= TOL_G[dtype], f"{name} error {e}"
+
+
+def host_threads() -> int:
+    """Host threads for oracle work: the CPUs this process may use, at most 16."""
+    import os
+
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def dkdv_cols_split(qh, kh, vh, doh, scale, causal, cols, row_block=512, workers=None):
+    """oracle.dkdv_cols over [0, N), the query rows split into contiguous
+    ranges evaluated on host threads and their shares added in range order
+    (the sampler's ``rows`` option; NumPy releases the GIL in its kernels)."""
+    import concurrent.futures
+
+    import oracle
+
+    N = qh.shape[0]
+    n = workers or host_threads()
+    lo = int(np.min(cols)) if causal else 0
+    # causal: rows i carry about i - lo keys each, so cut the range where the
+    # running work (a triangle) reaches equal shares
+    if causal:
+        cuts = [lo + int(round((N - lo) * np.sqrt(t / (4 * n)))) for t in range(4 * n + 1)]
+    else:
+        cuts = [int(round(N * t / (4 * n))) for t in range(4 * n + 1)]
+    ranges = [(a, b) for a, b in zip(cuts[:-1], cuts[1:]) if b > a]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=n) as ex:
+        parts = list(ex.map(lambda r: oracle.dkdv_cols(qh, kh, vh, doh, scale, causal, cols, row_block, rows=r),
+                            ranges))
+    dk = np.zeros((len(cols), qh.shape[1]))
+    dv = np.zeros_like(dk)
+    for pk, pv in parts:
+        dk += pk
+        dv += pv
+    return dk, dv

@@ -321,6 +321,16 @@ def test_row_blocking_and_samplers(causal):
         dk, dv = oracle.dkdv_cols(q[0, h], k[0, h], v[0, h], do[0, h], scale, causal, rows, row_block=13)
         np.testing.assert_allclose(dk, ref["dk"][0, h, rows], rtol=1e-12, atol=1e-12)
         np.testing.assert_allclose(dv, ref["dv"][0, h, rows], rtol=1e-12, atol=1e-12)
+        # Shares of disjoint query-row ranges covering [0, N) add up to the
+        # whole gradient; a range before every sampled key's first visible
+        # row (causal) contributes nothing.
+        cuts = [0, 5, 31, 32, 60, N]
+        parts = [oracle.dkdv_cols(q[0, h], k[0, h], v[0, h], do[0, h], scale, causal, rows, row_block=7,
+                                  rows=(a, b)) for a, b in zip(cuts[:-1], cuts[1:])]
+        np.testing.assert_allclose(sum(p[0] for p in parts), ref["dk"][0, h, rows], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(sum(p[1] for p in parts), ref["dv"][0, h, rows], rtol=1e-12, atol=1e-12)
+        first = oracle.dkdv_cols(q[0, h], k[0, h], v[0, h], do[0, h], scale, causal, rows[1:], rows=(0, 1))
+        assert (np.all(first[0] == 0) and np.all(first[1] == 0)) if causal else np.any(first[1] != 0)
 
 
 # --------------------------------------------------------------------------

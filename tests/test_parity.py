@@ -8,16 +8,14 @@ sampled rows of O, L, dQ and sampled key rows of dK, dV, which the oracle
 evaluates one by one, plus invariants that hold at any size.
 """
 
-import math
-
 import numpy as np
 import pytest
 import torch
 
 import oracle
 from exact_io_aware_30_amd import workloads as wl
-from parity_utils import (TOL_G, TOL_L, TOL_O, assert_fwd, assert_grad, check_finite, err_abs, run_gpu,
-                          say, to64)
+from parity_utils import (TOL_G, TOL_L, TOL_O, assert_fwd, assert_grad, check_finite, dkdv_cols_split, err_abs,
+                          run_gpu, say, to64)
 
 pytestmark = pytest.mark.gpu
 
@@ -48,16 +46,26 @@ def test_workload_full(name):
         assert_grad(w.dtype, g, out[g], ref[g], name)
 
 
-def _sample(N, rng, extra):
+def _rows_every_block(N, rng, block):
+    """The edge rows of the tiles, plus one random row in every ``block`` rows."""
     base = [0, 1, 31, 32, 63, 64, 127, 128, 129, N // 2 - 1, N // 2, N - 2, N - 1]
-    return np.unique(np.clip(np.concatenate([base, rng.integers(0, N, extra)]), 0, N - 1))
+    per = np.arange(0, N, block) + rng.integers(0, block, (N + block - 1) // block)
+    return np.unique(np.clip(np.concatenate([base, per]), 0, N - 1))
 
 
-@pytest.mark.parametrize("name,heads,col_floor", [
-    ("long", [(0, 0), (1, 15), (0, 9)], 0),
-    ("batch1_64k", [(0, 0), (0, 5)], 49152),
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,heads", [
+    ("long", [(0, 0), (1, 15), (0, 9)]),
+    ("batch1_64k", [(0, 0), (0, 5)]),
 ])
-def test_workload_sampled(name, heads, col_floor):
+def test_workload_sampled(name, heads):
+    """The two large workloads on sampled outputs of whole heads: O, L and dQ
+    of the tile-edge rows plus one random row in every 256-row forward block
+    (every forward workgroup's rows are checked), dK and dV of keys 0, 1,
+    127, 128, N - 1 plus one random key in every 32-key group (every wave of
+    every dK/dV workgroup, the first key block's long accumulation loops
+    included).  The oracle walks all query rows for the columns, split over
+    host threads."""
     w = wl.WORKLOADS[name]
     say(f"[parity] {w.describe()} (sampled)")
     q, k, v, do = wl.make_inputs(w)
@@ -66,26 +74,30 @@ def test_workload_sampled(name, heads, col_floor):
     rng = np.random.default_rng(7)
     for (b, h) in heads:
         qh, kh, vh, doh = (_np(x[b, h]) for x in (q, k, v, do))
-        rows = _sample(w.N, rng, 8)
+        rows = _rows_every_block(w.N, rng, 256)
         o_ref, L_ref = oracle.forward_rows(qh, kh, vh, w.scale, w.causal, rows)
         assert_fwd(w.dtype, out["o"][b, h, rows], o_ref, out["lse"][b, h, rows], L_ref, f"{name} head {b},{h}")
         dq_ref = oracle.dq_rows(qh, kh, vh, doh, w.scale, w.causal, rows)
-        cols = np.unique(np.concatenate([[col_floor, col_floor + 1, col_floor + 127, col_floor + 128, w.N - 1],
-                                         rng.integers(col_floor, w.N, 6)]))
-        dk_ref, dv_ref = oracle.dkdv_cols(qh, kh, vh, doh, w.scale, w.causal, cols, row_block=1024)
+        cols = np.unique(np.concatenate([[0, 1, 127, 128, w.N - 1],
+                                         np.arange(0, w.N, 32) + rng.integers(0, 32, w.N // 32)]))
+        dk_ref, dv_ref = dkdv_cols_split(qh, kh, vh, doh, w.scale, w.causal, cols)
+        say(f"  head {b},{h}: {rows.size} rows, {cols.size} key columns")
         # Relative errors are normalised by the largest reference value over
         # the sampled rows of this head.
         assert_grad(w.dtype, "dq", out["dq"][b, h, rows], dq_ref, f"{name} head {b},{h}")
         assert_grad(w.dtype, "dk", out["dk"][b, h, cols], dk_ref, f"{name} head {b},{h}")
         assert_grad(w.dtype, "dv", out["dv"][b, h, cols], dv_ref, f"{name} head {b},{h}")
-    # Invariants at full size (secondary diagnostics): sum_j dK_j = 0 and
-    # sum_j dV_j = sum_i dO_i for every head, within accumulated rounding.
+        # The first key block on its own: its workgroup runs the longest
+        # query loop (every row of the head under the causal mask).
+        first = cols < 128
+        assert_grad(w.dtype, "dk", out["dk"][b, h, cols[first]], dk_ref[first], f"{name} head {b},{h} keys < 128")
+        assert_grad(w.dtype, "dv", out["dv"][b, h, cols[first]], dv_ref[first], f"{name} head {b},{h} keys < 128")
+    # Whole-tensor sums, printed as a diagnostic only (not a parity bar):
+    # sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i hold exactly for the true
+    # gradient; on the GPU they carry the accumulated rounding of N rows.
     dk_sum = np.abs(out["dk"].sum(axis=2)).max()
     dv_gap = np.abs(out["dv"].sum(axis=2) - _np(do).sum(axis=2)).max()
-    bound_k = 0.05 * np.abs(out["dk"]).max() * math.sqrt(w.N)
-    bound_v = 0.05 * np.abs(out["dv"]).max() * math.sqrt(w.N)
-    say(f"  invariants: |sum dK| {dk_sum:.3e} (<= {bound_k:.3e}), |sum dV - sum dO| {dv_gap:.3e} (<= {bound_v:.3e})")
-    assert dk_sum <= bound_k and dv_gap <= bound_v
+    say(f"  diagnostic: max |sum_j dK_j| {dk_sum:.3e}, max |sum_j dV_j - sum_i dO_i| {dv_gap:.3e}")
 
 
 # --------------------------------------------------------------------------
