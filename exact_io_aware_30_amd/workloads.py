@@ -84,7 +84,7 @@ def make_inputs(w: Workload, device="cpu"):
 
 RISE_TILE = 64      # keys per block of the staircase below
 RISE_STEP = 12.0    # base-2 units the scores rise at each step block
-RISE_QCOORD = 8.0   # value of every query's last coordinate
+RISE_QCOORD = 32.0  # value of every query's last coordinate
 
 
 def rise_steps(n: int):
@@ -103,7 +103,10 @@ def make_rising_inputs(w: Workload, device="cpu"):
     key block j // RISE_TILE; round to the dtype.  The last coordinate then
     adds about RISE_STEP * s(j) base-2 units to every score of key j, on top
     of the N(0, 1) part of the other d - 1 coordinates (keys of block 0 add
-    nothing)."""
+    nothing).  The shift sits mostly on the query side (keys' last
+    coordinate at most 12): the backward forms D from the rounded O, and
+    dQ = scale dS K then carries D's rounding times the keys' shared
+    component, which a large key coordinate would magnify."""
     q, k, v, do = make_inputs(w)
     q, k = q.float(), k.float()
     c = w.scale * math.log2(math.e)
