@@ -51,6 +51,7 @@ _SIG = {
                      _p],
     "fa_bwd_varlen_ws": [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _i, _i, _p,
                          ctypes.c_size_t, _p],
+    "fa_bwd_ex_scratch": [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _i, _i, _p],
     "fa_bwd_workspace_size": [_i, _i, _i, _i, _i],
     "fa_bwd_varlen_workspace_size": [_i, _i, _i, _i, _i, _i],
     "fa_status_string": [_i],
@@ -290,6 +291,23 @@ def fa_bwd_ex_ws(q, k, v, do, lse, delta, dq, dk, dv, scale: float, window, work
     _check(_lib.fa_bwd_ex_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
                              delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, N, d,
                              float(scale), int(wl), int(wr), _DT[q.dtype], wp, wb, _stream(q)), "fa_bwd_ex_ws")
+
+
+# Bytes of the library's static scratch array (FA_SCRATCH_BYTES).
+SCRATCH_BYTES = 256 << 20
+
+
+def fa_bwd_ex_scratch(q, k, v, do, lse, delta, dq, dk, dv, scale: float, window) -> None:
+    """fa_bwd_ex_ws with the head-split partials in the library's static
+    scratch array instead of a workspace: nothing is allocated."""
+    B, H, N, d = _bhnd(q, "q")
+    Hkv = _kv(q, ((k, "k"), (v, "v"), (dk, "dk"), (dv, "dv")))
+    _same(q, (do, "do"), (dq, "dq"))
+    _rows(q, (lse, "lse"), (delta, "delta"))
+    wl, wr = window
+    _check(_lib.fa_bwd_ex_scratch(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                                  delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, N, d,
+                                  float(scale), int(wl), int(wr), _DT[q.dtype], _stream(q)), "fa_bwd_ex_scratch")
 
 
 def attention_forward(q, k, v, scale: float, causal: bool, window=None):

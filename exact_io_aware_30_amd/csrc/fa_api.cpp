@@ -11,6 +11,8 @@
 
 #include "fa_launch.h"
 
+static_assert(FA_SCRATCH_BYTES == fa::kScratchBytes, "the header's scratch size is the array's");
+
 namespace {
 
 // One head slice is addressed with 32-bit byte offsets; the margin keeps the
@@ -306,6 +308,32 @@ int fa_bwd_ex_ws(const void* q, const void* k, const void* v, const void* dO, co
   return hip_status(fa::launch_bwd_dq(a, st));
 }
 
+int fa_bwd_ex_scratch(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                      const float* delta, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d,
+                      float scale, int window_left, int window_right, fa_dtype dt, void* stream) {
+  int rc = check_bwd(q, k, v, dO, lse, delta, dq, dk, dv, B, H, Hkv, N, d, scale, window_left, window_right, dt,
+                     true, true);
+  if (rc) return rc;
+  // The split the rule asks for, as fa_bwd_ex_ws runs it with
+  // fa_bwd_workspace_size bytes; rejected before anything is looked up or
+  // launched when its partials exceed the static array.
+  const long long R = static_cast<long long>(B) * Hkv * N;
+  const int gs = head_splits(B, Hkv, H / Hkv, N);
+  const long long used = split_bytes(gs, R, d);
+  if (used > static_cast<long long>(fa::kScratchBytes)) return FA_ERR_SCRATCH;
+  fa::BwdArgs a =
+      bwd_args(q, k, v, dO, lse, delta, dq, dk, dv, B, H, Hkv, N, d, scale, window_left, window_right, dt);
+  if (gs > 1) {
+    void* base = nullptr;
+    if ((rc = hip_status(fa::scratch_region(&base)))) return rc;
+    a.part = static_cast<float*>(base);
+    a.splits = gs;
+  }
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((rc = hip_status(fa::launch_bwd_dkdv(a, st)))) return rc;
+  return hip_status(fa::launch_bwd_dq(a, st));
+}
+
 int fa_bwd_ex(const void* q, const void* k, const void* v, const void* dO, const float* lse, const float* delta,
               void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d, float scale, int window_left,
               int window_right, fa_dtype dt, void* stream) {
@@ -388,6 +416,9 @@ const char* fa_status_string(int status) {
     case FA_ERR_ALIGNMENT: return "a pointer is not 16-byte aligned";
     case FA_ERR_HIP: return "the HIP runtime refused a kernel launch";
     case FA_ERR_ALIAS: return "an output overlaps an input or another output";
+    case FA_ERR_SCRATCH:
+      return "the call needs more head-split scratch than the library's static array holds (pass a workspace to "
+             "fa_bwd_ex_ws instead)";
     default: return "unknown status";
   }
 }

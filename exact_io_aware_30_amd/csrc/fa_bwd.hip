@@ -12,7 +12,15 @@
 #include "fa_launch.h"
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
+
+// Device memory of the backward entry point that allocates nothing: the
+// head-split float32 partial sums live here instead of in a caller
+// workspace.  Every device the library runs on holds its own copy from the
+// time the code object is loaded until the process ends; every call on a
+// device shares it (see fa::scratch_region).
+static __device__ __align__(256) unsigned char scratch[fa::kScratchBytes];
 
 // Tile configuration (compile-time; defaults chosen by measurement).
 #ifndef FA_BWD_STAGES
@@ -879,6 +887,35 @@ __global__ __launch_bounds__(64 * kBwdWaves, 2) void dq_kernel(const void* __res
                                    lane);
   }
   store_rows<T, D>(rdq, qrow, dqa, scale, lane);
+}
+
+// ---------------------------------------------------------------------------
+// The static scratch array's device address on the current device, looked
+// up once per device (with that device current) and kept: in host code the
+// array's name is not a device address, so kernels only ever receive the
+// address returned here.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_addr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t scratch_region(void** base) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    scratch_addr[dev] = p;
+  }
+  *base = scratch_addr[dev];
+  return hipSuccess;
 }
 
 // ---------------------------------------------------------------------------

@@ -45,6 +45,15 @@ struct BwdArgs {
   int splits = 1;
 };
 
+// Bytes of the static scratch array that holds the head-split partial sums
+// for the backward entry point that allocates nothing: 2 * 2048 * 128 rows
+// of d = 128 float32 values, the partials of a split that brings the dK/dV
+// grid to its 2048-workgroup target at d = 128.
+constexpr size_t kScratchBytes = size_t(256) << 20;
+// Device address of the scratch array on the current device (looked up on
+// the first call per device, then cached).
+hipError_t scratch_region(void** base);
+
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st);
 hipError_t launch_preprocess(const PreArgs& a, hipStream_t st);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t st);

@@ -56,7 +56,8 @@ enum {
   FA_ERR_UNSUPPORTED = -2, /* head dim not in {32,64,128}, or sizes beyond the limits above */
   FA_ERR_ALIGNMENT = -3,   /* a pointer is not 16-byte aligned */
   FA_ERR_HIP = -4,         /* the HIP runtime refused a launch */
-  FA_ERR_ALIAS = -5        /* an output overlaps an input or another output */
+  FA_ERR_ALIAS = -5,       /* an output overlaps an input or another output */
+  FA_ERR_SCRATCH = -6      /* fa_bwd_ex_scratch: the split needs more than FA_SCRATCH_BYTES */
 };
 
 /*
@@ -252,6 +253,30 @@ int fa_bwd_varlen_ws(const void* q, const void* k, const void* v,
 size_t fa_bwd_workspace_size(int B, int H, int Hkv, int N, int d);
 size_t fa_bwd_varlen_workspace_size(int B, int max_seqlen, int T, int H,
                                     int Hkv, int d);
+
+/*
+ * fa_bwd_ex_scratch -- fa_bwd_ex_ws without a caller workspace, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  The head-split partial
+ * sums go to a static device array of FA_SCRATCH_BYTES that the library
+ * holds on every device it runs on until the process ends; no call
+ * allocates or frees anything.  Arguments, operation and results are those
+ * of fa_bwd_ex_ws given fa_bwd_workspace_size(B, H, Hkv, N, d) bytes (the
+ * same split, the same bits); when that size exceeds FA_SCRATCH_BYTES the
+ * call returns FA_ERR_SCRATCH before launching anything.  The array needs
+ * no clearing (nothing in it is read before a call writes it), but every
+ * call on a device uses the same array: calls that overlap in time on one
+ * device (different streams, or host threads without ordering) race on it
+ * and must be ordered by the caller, for example on one stream.  The first
+ * call on a device looks the array's address up with that device current;
+ * a failure there returns FA_ERR_HIP.
+ */
+#define FA_SCRATCH_BYTES (256u << 20)
+int fa_bwd_ex_scratch(const void* q, const void* k, const void* v,
+                      const void* dO, const float* lse, const float* delta,
+                      void* dq, void* dk, void* dv, int B, int H, int Hkv,
+                      int N, int d, float scale, int window_left,
+                      int window_right, fa_dtype dt, void* stream);
 
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* fa_status_string(int status);

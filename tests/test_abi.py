@@ -20,7 +20,7 @@ HEADER = os.path.join(ROOT, "include", "fa.h")
 from exact_io_aware_30_amd import binding  # noqa: E402
 
 lib = binding._lib
-OK, INVALID, UNSUPPORTED, ALIGN, HIPERR, ALIAS = 0, -1, -2, -3, -4, -5
+OK, INVALID, UNSUPPORTED, ALIGN, HIPERR, ALIAS, SCRATCH = 0, -1, -2, -3, -4, -5, -6
 
 
 def declared_functions():
@@ -35,7 +35,7 @@ def test_header_functions_are_exported():
                             "fa_fwd_gqa", "fa_bwd_gqa", "fa_bwd_dkdv_gqa", "fa_bwd_dq_gqa",
                             "fa_fwd_ex", "fa_bwd_ex", "fa_bwd_dkdv_ex", "fa_bwd_dq_ex",
                             "fa_fwd_varlen", "fa_bwd_varlen",
-                            "fa_bwd_ex_ws", "fa_bwd_varlen_ws", "fa_bwd_workspace_size",
+                            "fa_bwd_ex_ws", "fa_bwd_varlen_ws", "fa_bwd_workspace_size", "fa_bwd_ex_scratch",
                             "fa_bwd_varlen_workspace_size",
                             "fa_status_string", "fa_version"])
     out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True, text=True).stdout
@@ -47,7 +47,7 @@ def test_header_functions_are_exported():
 
 
 def test_status_strings_and_version():
-    for code in (OK, INVALID, UNSUPPORTED, ALIGN, HIPERR, ALIAS):
+    for code in (OK, INVALID, UNSUPPORTED, ALIGN, HIPERR, ALIAS, SCRATCH):
         s = binding.fa_status_string(code)
         assert s and s != "unknown status"
     assert binding.fa_status_string(12345) == "unknown status"
@@ -254,6 +254,28 @@ def test_workspace_forms_reject(p):
     assert vneed == 2 * 8 * 64 * 32 * 4
     assert lib.fa_bwd_varlen_ws(*p[:9], p[10], 2, 32, 64, 8, 1, 32, 0.125, -1, 0, 1, None, 16, None) == INVALID
     assert lib.fa_bwd_varlen_ws(*p[:9], p[10], 2, 32, 64, 8, 1, 32, 0.125, -1, 0, 1, p[3], vneed, None) == ALIAS
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="fake pointers: run where no GPU is visible")
+def test_scratch_form_rejects():
+    """fa_bwd_ex_scratch checks like fa_bwd_ex_ws, then refuses a split whose
+    partials exceed the static array, before any HIP call (fake, disjoint
+    pointers: nothing may be launched)."""
+    f = lib.fa_bwd_ex_scratch
+    fake = [0x10000000 * (i + 1) for i in range(9)]
+    args = lambda B, H, Hkv, N, d: (*fake, B, H, Hkv, N, d, 0.125, -1, 0, 1, None)  # noqa: E731
+    # 16 query heads on one key/value head, 200 key blocks: the rule splits
+    # 16 ways, 2 * 16 * 25600 * 128 * 4 bytes = 400 MiB > 256 MiB
+    assert binding.fa_bwd_workspace_size(1, 16, 1, 25600, 128) == 2 * 16 * 25600 * 128 * 4
+    assert f(*args(1, 16, 1, 25600, 128)) == SCRATCH
+    assert binding.SCRATCH_BYTES == 256 << 20
+    assert "static array" in binding.fa_status_string(SCRATCH)
+    # the checks of the workspace form come first
+    assert f(*args(1, 16, 3, 25600, 128)) == INVALID
+    assert f(*args(1, 16, 1, 25600, 48)) == UNSUPPORTED
+    a = list(args(1, 16, 1, 25600, 128))
+    a[6] = a[0]  # dq over q
+    assert f(*a) == ALIAS
 
 
 def test_workspace_size_rule():
