@@ -316,12 +316,13 @@ struct DmaTile {
     }
   }
   // Enqueue the tile whose first row is row0 (the row offset is added per
-  // lane so that the out-of-range check sees the full offset).
+  // lane so that the out-of-range check sees the full offset).  With an even
+  // split the per-wave test is false at compile time: no branches.
   __device__ __forceinline__ void issue(Rsrc src, lds_char* tile, int row0, int w) const {
     const uint32_t base = (uint32_t)(row0 * D * 2);
 #pragma unroll
     for (int i = 0; i < PER; ++i)
-      if (i * NW + w < NI) dma16(src, tile + (i * NW + w) * 1024, base + off[i]);
+      if (NI % NW == 0 || i * NW + w < NI) dma16(src, tile + (i * NW + w) * 1024, base + off[i]);
   }
 };
 

@@ -318,30 +318,34 @@ __device__ __forceinline__ void pipe_wait(int t, int nt) {
 // scheduling fences between the groups so that the compiler keeps this
 // order (a wave issues VALU work while its own MFMAs execute).
 template <class T, int D, bool MASK, int IDX>
-__device__ __forceinline__ void fwd_pipe_step(lds_char* lds, int t, int nt, int ntw, int tb,
+__device__ __forceinline__ void fwd_pipe_step(lds_char* lds, lds_char* ldsd, int t, int nt, int ntw, int tb,
                                               const DmaTile<FwdCfg<D>::kBN, D, FwdCfg<D>::kWaves>& dma, Rsrc rk, Rsrc rv,
-                                              const u32x4* qf, const uint32_t* koff, const uint32_t* voff,
+                                              const u32x4* qf, uint32_t* koff, uint32_t* voff,
                                               f32x16* acc, f32x16* s_cur, f32x16* s_nxt, float& mref, float& l,
                                               int wq0, int qrow, int N, Win win, float c, int w, int lane) {
   constexpr int S = kPipeStages, BN = FwdCfg<D>::kBN, TILE = BN * D * 2, NB = D / 32, NKK = D / 16, NA = FwdCfg<D>::kNA;
   pipe_wait<2 * DmaTile<FwdCfg<D>::kBN, D, FwdCfg<D>::kWaves>::PER>(t, nt);
-  if (t + S - 1 < nt) fwd_pipe_issue<D, (IDX + S - 1) % S>(lds, tb + t + S - 1, dma, rk, rv, w);
+  if (t + S - 1 < nt) fwd_pipe_issue<D, (IDX + S - 1) % S>(ldsd, tb + t + S - 1, dma, rk, rv, w);
   __builtin_amdgcn_sched_barrier(0);
   if (t >= ntw) return;  // no key from tile t on is visible to any query of the wave
-  // Tile bases made opaque per step, so that the compiler does not hoist a
-  // full set of per-buffer, per-lane addresses out of the loop.
-  uint32_t vb = (uint32_t)(uintptr_t)lds + (S + IDX) * TILE, kb = (uint32_t)(uintptr_t)lds + ((IDX + 1) % S) * TILE;
-  asm volatile("" : "+v"(vb), "+v"(kb));
-  // Operand addresses of this step: one add per per-lane offset, the row
-  // blocks as immediates (32 rows of K are 64D bytes, 16 rows of V 32D).
+  // The per-lane operand addresses (absolute: K's are relative to ring
+  // buffer 0, V's to V buffer 0) are made opaque in place each step (no
+  // instruction is emitted), so that the compiler does not hoist a full set
+  // of per-buffer addresses out of the loop; the buffer and row-block terms
+  // are then immediates folded into the read instructions' offsets, with
+  // no address arithmetic left in the step.
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) asm volatile("" : "+v"(koff[kk]));
+#pragma unroll
+  for (int x = 0; x < 2 * NB; ++x) asm volatile("" : "+v"(voff[x]));
   const lds_char* kp[NKK];
   const lds_char* vp[NB][2];
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) kp[kk] = (const lds_char*)(uintptr_t)(kb + koff[kk]);
+  for (int kk = 0; kk < NKK; ++kk) kp[kk] = (const lds_char*)(uintptr_t)koff[kk] + ((IDX + 1) % S) * TILE;
 #pragma unroll
   for (int b = 0; b < NB; ++b)
 #pragma unroll
-    for (int x = 0; x < 2; ++x) vp[b][x] = (const lds_char*)(uintptr_t)(vb + voff[2 * b + x]);
+    for (int x = 0; x < 2; ++x) vp[b][x] = (const lds_char*)(uintptr_t)voff[2 * b + x] + IDX * TILE;
 
   // Run 1: S^T(t+1) = K(t+1) Q^T, MFMA i = (kk = i / NA, a = i % NA), and
   // p = 2^(S(t) c - mref) and packing of tile t (with kSumInPv off, also its
@@ -437,6 +441,10 @@ __global__ __launch_bounds__(64 * FwdCfg<D>::kWaves, 2) void fwd_pipe_kernel(con
   uint32_t lds_base = (uint32_t)(uintptr_t)(lds_char*)smem;
   asm volatile("" : "+v"(lds_base));
   lds_char* const lds = (lds_char*)(uintptr_t)lds_base;
+  // DMA destinations from the array's own address, which the compiler keeps
+  // in scalar registers: M0 is then set without a v_readfirstlane (a vector
+  // to scalar dependency in every copy).
+  lds_char* const ldsd = (lds_char*)smem;
 
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, known uniform
@@ -465,7 +473,7 @@ __global__ __launch_bounds__(64 * FwdCfg<D>::kWaves, 2) void fwd_pipe_kernel(con
   const int ntw = MASK ? min(nt, (win.key_hi(wq0 + 31, N) + BN - 1) / BN - tb) : nt;
   Dma dma;
   dma.init(w, lane);
-  fwd_pipe_issue<D, 0>(lds, tb, dma, rk, rv, w);
+  fwd_pipe_issue<D, 0>(ldsd, tb, dma, rk, rv, w);
 
   const int qrow = wq0 + (lane & 31);  // this lane's query
   u32x4 qf[NKK];
@@ -473,15 +481,15 @@ __global__ __launch_bounds__(64 * FwdCfg<D>::kWaves, 2) void fwd_pipe_kernel(con
   for (int kk = 0; kk < NKK; ++kk) qf[kk] = bload16(rq, (uint32_t)((qrow * D + 16 * kk + 8 * h) * 2));
   uint32_t koff[NKK], voff[2 * NB];
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) koff[kk] = rows_offset<D>(kk, lane);
+  for (int kk = 0; kk < NKK; ++kk) koff[kk] = lds_base + rows_offset<D>(kk, lane);
 #pragma unroll
-  for (int x = 0; x < 2 * NB; ++x) voff[x] = cols_offset<D>(32 * (x / 2), x % 2, lane);
+  for (int x = 0; x < 2 * NB; ++x) voff[x] = lds_base + S * TILE + cols_offset<D>(32 * (x / 2), x % 2, lane);
   // Q has landed (and with it tile 0) before the ring starts: no load the
   // compiler tracks may be pending inside the loop.
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) land(qf[kk]);
-  if (nt > 1) fwd_pipe_issue<D, 1>(lds, tb + 1, dma, rk, rv, w);
-  if (nt > 2) fwd_pipe_issue<D, 2>(lds, tb + 2, dma, rk, rv, w);
+  if (nt > 1) fwd_pipe_issue<D, 1>(ldsd, tb + 1, dma, rk, rv, w);
+  if (nt > 2) fwd_pipe_issue<D, 2>(ldsd, tb + 2, dma, rk, rv, w);
   // Tile 0 landed (waited above); tiles 1 and 2 may be in flight.
   dma_wait_barrier<63>();
 
@@ -498,16 +506,16 @@ __global__ __launch_bounds__(64 * FwdCfg<D>::kWaves, 2) void fwd_pipe_kernel(con
   fwd_rescale<NB>(fwd_rowmax<FwdCfg<D>::kNA>(sa, c), acc, mref, l);
 
   for (int t = 0; t < nt; t += 4) {
-    fwd_pipe_step<T, D, MASK, 0>(lds, t, nt, ntw, tb, dma, rk, rv, qf, koff, voff, acc, sa, sb, mref, l, wq0, qrow, N, win, c, w,
+    fwd_pipe_step<T, D, MASK, 0>(lds, ldsd, t, nt, ntw, tb, dma, rk, rv, qf, koff, voff, acc, sa, sb, mref, l, wq0, qrow, N, win, c, w,
                                   lane);
     if (t + 1 < nt)
-      fwd_pipe_step<T, D, MASK, 1>(lds, t + 1, nt, ntw, tb, dma, rk, rv, qf, koff, voff, acc, sb, sa, mref, l, wq0, qrow, N, win,
+      fwd_pipe_step<T, D, MASK, 1>(lds, ldsd, t + 1, nt, ntw, tb, dma, rk, rv, qf, koff, voff, acc, sb, sa, mref, l, wq0, qrow, N, win,
                                     c, w, lane);
     if (t + 2 < nt)
-      fwd_pipe_step<T, D, MASK, 2>(lds, t + 2, nt, ntw, tb, dma, rk, rv, qf, koff, voff, acc, sa, sb, mref, l, wq0, qrow, N, win,
+      fwd_pipe_step<T, D, MASK, 2>(lds, ldsd, t + 2, nt, ntw, tb, dma, rk, rv, qf, koff, voff, acc, sa, sb, mref, l, wq0, qrow, N, win,
                                     c, w, lane);
     if (t + 3 < nt)
-      fwd_pipe_step<T, D, MASK, 3>(lds, t + 3, nt, ntw, tb, dma, rk, rv, qf, koff, voff, acc, sb, sa, mref, l, wq0, qrow, N, win,
+      fwd_pipe_step<T, D, MASK, 3>(lds, ldsd, t + 3, nt, ntw, tb, dma, rk, rv, qf, koff, voff, acc, sb, sa, mref, l, wq0, qrow, N, win,
                                     c, w, lane);
   }
 
