@@ -98,7 +98,7 @@ int smaller_divisor(int G, int gs) {
 // query heads per key/value head: the smallest divisor of G that brings the
 // grid to the target, G at most.
 int head_splits(int B, int Hkv, int G, int n) {
-  const long long base = static_cast<long long>((n + kDkdvKeys - 1) / kDkdvKeys) * B * Hkv;
+  const long long base = (static_cast<long long>(n) + kDkdvKeys - 1) / kDkdvKeys * B * Hkv;
   int gs = 1;
   while (gs < G && base * gs < FA_DKDV_SPLIT_TARGET) {
     int next = gs + 1;
@@ -233,13 +233,14 @@ int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* dO, c
 }
 
 size_t fa_bwd_workspace_size(int B, int H, int Hkv, int N, int d) {
-  if (B < 1 || H < 1 || N < 1 || check_heads(H, Hkv) || (d != 32 && d != 64 && d != 128)) return 0;
+  // 0 for any size the backward entry points refuse
+  if (check_common(B, H, N, d, FA_BF16) || check_heads(H, Hkv)) return 0;
   return static_cast<size_t>(split_bytes(head_splits(B, Hkv, H / Hkv, N), static_cast<long long>(B) * Hkv * N, d));
 }
 
 size_t fa_bwd_varlen_workspace_size(int B, int max_seqlen, int T, int H, int Hkv, int d) {
-  if (B < 1 || max_seqlen < 1 || T < 1 || H < 1 || check_heads(H, Hkv) || (d != 32 && d != 64 && d != 128))
-    return 0;
+  // 0 for any size the packed backward refuses
+  if (T < 1 || check_common(B, H, max_seqlen, d, FA_BF16) || check_heads(H, Hkv)) return 0;
   return static_cast<size_t>(
       split_bytes(head_splits(B, Hkv, H / Hkv, max_seqlen), static_cast<long long>(Hkv) * T, d));
 }
