@@ -57,6 +57,16 @@ struct FwdCfg {
 #endif
 };
 
+// Short sequences (N <= kShortSeq, the longest sequence when packed) use
+// the plain kernel with 4 waves (128 query rows) and a 2-deep ring at every
+// head dimension: causal grids of short sequences are a few blocks per head
+// with very uneven work, and the smaller blocks pack the compute units
+// better.  Measured (bf16 causal, same box): 10-13% faster at d = 64 for
+// [8,16,1024] and [4,16,2048], 12% and 4% at d = 128 for [8,16,1024] and
+// [4,16,2048]; at N = 4096 (d = 128) and 65536 (d = 64) the default shapes
+// are 5% and 3% faster, hence the cut.
+constexpr int kShortSeq = 2048, kShortWaves = 4, kShortStages = 2;
+
 // Rescale threshold in base-2 units: the reference maximum used for the
 // exponentials is moved only when a row's maximum exceeds it by more than
 // this, so p = 2^(S c - ref) stays below 2^8 and most tiles skip the
@@ -163,8 +173,8 @@ __device__ __forceinline__ void fwd_tile(const lds_char* kt, const lds_char* vt,
 }
 
 // DMA of key tile t (K then V) into ring buffer IDX.
-template <int D, int IDX>
-__device__ __forceinline__ void fwd_issue(lds_char* lds, int t, const DmaTile<FwdCfg<D>::kBN, D, FwdCfg<D>::kWaves>& dma, Rsrc rk,
+template <int D, int IDX, int NW>
+__device__ __forceinline__ void fwd_issue(lds_char* lds, int t, const DmaTile<FwdCfg<D>::kBN, D, NW>& dma, Rsrc rk,
                                           Rsrc rv, int w) {
   constexpr int TILE = FwdCfg<D>::kBN * D * 2;
   lds_char* b = lds + IDX * 2 * TILE;
@@ -176,13 +186,13 @@ __device__ __forceinline__ void fwd_issue(lds_char* lds, int t, const DmaTile<Fw
 // index, so that every LDS operand address is a register plus an immediate):
 // wait and barrier, DMA of tile t + S - 1 into the buffer tile t - 1 used,
 // then the math.
-template <class T, int D, bool MASK, int IDX>
-__device__ __forceinline__ void fwd_step(lds_char* lds, int t, int nt, int tb, const DmaTile<FwdCfg<D>::kBN, D, FwdCfg<D>::kWaves>& dma,
+template <class T, int D, bool MASK, int IDX, int NW, int S>
+__device__ __forceinline__ void fwd_step(lds_char* lds, int t, int nt, int tb, const DmaTile<FwdCfg<D>::kBN, D, NW>& dma,
                                          Rsrc rk, Rsrc rv, const u32x4* qf, f32x16* acc, float& mref, float& l,
                                          int wq0, int qrow, int N, Win win, float c, int w, int lane) {
-  constexpr int S = FwdCfg<D>::kStages, BN = FwdCfg<D>::kBN, TILE = BN * D * 2;
-  ring_wait<S, 2 * DmaTile<FwdCfg<D>::kBN, D, FwdCfg<D>::kWaves>::PER>(t, nt);
-  if (t + S - 1 < nt) fwd_issue<D, (IDX + S - 1) % S>(lds, tb + t + S - 1, dma, rk, rv, w);
+  constexpr int BN = FwdCfg<D>::kBN, TILE = BN * D * 2;
+  ring_wait<S, 2 * DmaTile<FwdCfg<D>::kBN, D, NW>::PER>(t, nt);
+  if (t + S - 1 < nt) fwd_issue<D, (IDX + S - 1) % S, NW>(lds, tb + t + S - 1, dma, rk, rv, w);
   __builtin_amdgcn_sched_barrier(0);
   const int j0 = (tb + t) * BN;
   // No key of the tile is visible to any query of the wave.
@@ -524,8 +534,8 @@ __global__ __launch_bounds__(64 * FwdCfg<D>::kWaves, 2) void fwd_pipe_kernel(con
   if (h == 0 && qrow < N) lsep[(size_t)qr0 + qrow] = (mref + log2_fast(lt)) * kLn2;
 }
 
-template <class T, int D, int MODE>
-__global__ __launch_bounds__(64 * FwdCfg<D>::kWaves, 2) void fwd_kernel(const void* __restrict__ qp,
+template <class T, int D, int MODE, int NW, int S>
+__global__ __launch_bounds__(64 * NW, 2) void fwd_kernel(const void* __restrict__ qp,
                                                                 const void* __restrict__ kp,
                                                                 const void* __restrict__ vp, void* __restrict__ op,
                                                                 float* __restrict__ lsep, Geom geo, int BH, int nqb,
@@ -534,7 +544,7 @@ __global__ __launch_bounds__(64 * FwdCfg<D>::kWaves, 2) void fwd_kernel(const vo
   // compile-time constant so that every window test folds; 2: any window.
   constexpr bool MASK = MODE != 0;
   const Win win = MODE == 1 ? Win{-1, 0} : win_in;
-  constexpr int NW = FwdCfg<D>::kWaves, S = FwdCfg<D>::kStages, BM = 32 * NW, BN = FwdCfg<D>::kBN, NKK = D / 16, NB = D / 32;
+  constexpr int BM = 32 * NW, BN = FwdCfg<D>::kBN, NKK = D / 16, NB = D / 32;
   constexpr int TILE = BN * D * 2, BUF = 2 * TILE;
   using Dma = DmaTile<BN, D, NW>;
   __shared__ __attribute__((aligned(16))) char smem[S * BUF];
@@ -563,7 +573,7 @@ __global__ __launch_bounds__(64 * FwdCfg<D>::kWaves, 2) void fwd_kernel(const vo
   const int tb = kbeg / BN, nt = (kend + BN - 1) / BN - tb;
   Dma dma;
   dma.init(w, lane);
-  fwd_issue<D, 0>(lds, tb, dma, rk, rv, w);
+  fwd_issue<D, 0, NW>(lds, tb, dma, rk, rv, w);
 
   const int qrow = q0 + 32 * w + (lane & 31);  // this lane's query
   u32x4 qf[NKK];
@@ -573,8 +583,8 @@ __global__ __launch_bounds__(64 * FwdCfg<D>::kWaves, 2) void fwd_kernel(const vo
   // compiler tracks may be pending inside the loop.
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) land(qf[kk]);
-  if (S > 2 && nt > 1) fwd_issue<D, 1 % S>(lds, tb + 1, dma, rk, rv, w);
-  if (S > 3 && nt > 2) fwd_issue<D, 2 % S>(lds, tb + 2, dma, rk, rv, w);
+  if (S > 2 && nt > 1) fwd_issue<D, 1 % S, NW>(lds, tb + 1, dma, rk, rv, w);
+  if (S > 3 && nt > 2) fwd_issue<D, 2 % S, NW>(lds, tb + 2, dma, rk, rv, w);
 
   f32x16 acc[NB];
 #pragma unroll
@@ -583,15 +593,17 @@ __global__ __launch_bounds__(64 * FwdCfg<D>::kWaves, 2) void fwd_kernel(const vo
   const int wq0 = q0 + 32 * w;      // first query of this wave
 
   for (int t = 0; t < nt; t += S) {
-    fwd_step<T, D, MASK, 0>(lds, t, nt, tb, dma, rk, rv, qf, acc, mref, l, wq0, qrow, N, win, c, w, lane);
+    fwd_step<T, D, MASK, 0, NW, S>(lds, t, nt, tb, dma, rk, rv, qf, acc, mref, l, wq0, qrow, N, win, c, w, lane);
     if (t + 1 < nt)
-      fwd_step<T, D, MASK, 1>(lds, t + 1, nt, tb, dma, rk, rv, qf, acc, mref, l, wq0, qrow, N, win, c, w, lane);
+      fwd_step<T, D, MASK, 1, NW, S>(lds, t + 1, nt, tb, dma, rk, rv, qf, acc, mref, l, wq0, qrow, N, win, c, w, lane);
     if constexpr (S > 2)
       if (t + 2 < nt)
-        fwd_step<T, D, MASK, 2 % S>(lds, t + 2, nt, tb, dma, rk, rv, qf, acc, mref, l, wq0, qrow, N, win, c, w, lane);
+        fwd_step<T, D, MASK, 2 % S, NW, S>(lds, t + 2, nt, tb, dma, rk, rv, qf, acc, mref, l, wq0, qrow, N, win, c, w,
+                                           lane);
     if constexpr (S > 3)
       if (t + 3 < nt)
-        fwd_step<T, D, MASK, 3 % S>(lds, t + 3, nt, tb, dma, rk, rv, qf, acc, mref, l, wq0, qrow, N, win, c, w, lane);
+        fwd_step<T, D, MASK, 3 % S, NW, S>(lds, t + 3, nt, tb, dma, rk, rv, qf, acc, mref, l, wq0, qrow, N, win, c, w,
+                                           lane);
   }
 
   const float lt = sum_with_partner(l);
@@ -599,19 +611,32 @@ __global__ __launch_bounds__(64 * FwdCfg<D>::kWaves, 2) void fwd_kernel(const vo
   if (h == 0 && qrow < N) lsep[(size_t)qr0 + qrow] = (mref + log2_fast(lt)) * kLn2;
 }
 
+// The plain kernel with NW waves and an S-deep ring.
+template <class T, int D, int MODE, int NW, int S>
+static void launch_fwd_plain(const FwdArgs& a, const Geom& geo, const Win& win, hipStream_t st) {
+  const int BH = a.B * a.H, BM = 32 * NW;
+  const int nqb = (a.N + BM - 1) / BM;  // a.N: the longest sequence when packed
+  hipLaunchKernelGGL((fwd_kernel<T, D, MODE, NW, S>), dim3(nqb * BH), dim3(64 * NW), 0, st, a.q, a.k, a.v, a.o, a.lse,
+                     geo, BH, nqb, win, a.scale * kLog2e);
+}
+
 template <class T, int D, int MODE>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   const int BH = a.B * a.H;
-  const int BM = 32 * FwdCfg<D>::kWaves;
-  const int nqb = (a.N + BM - 1) / BM;  // a.N: the longest sequence when packed
   const Win win{a.wl, a.wr};
   const Geom geo{a.N, a.H, a.H / a.Hkv, a.cu, a.T};
-  if constexpr (kFwdPipelined<D>)
+  constexpr bool kShortIsDefault = !kFwdPipelined<D> && FwdCfg<D>::kWaves == kShortWaves &&
+                                   FwdCfg<D>::kStages == kShortStages;
+  if (!kShortIsDefault && a.N <= kShortSeq) {
+    launch_fwd_plain<T, D, MODE, kShortWaves, kShortStages>(a, geo, win, st);
+  } else if constexpr (kFwdPipelined<D>) {
+    const int BM = 32 * FwdCfg<D>::kWaves;
+    const int nqb = (a.N + BM - 1) / BM;
     hipLaunchKernelGGL((fwd_pipe_kernel<T, D, MODE>), dim3(nqb * BH), dim3(64 * FwdCfg<D>::kWaves), 0, st, a.q, a.k, a.v,
                        a.o, a.lse, geo, BH, nqb, win, a.scale * kLog2e);
-  else
-    hipLaunchKernelGGL((fwd_kernel<T, D, MODE>), dim3(nqb * BH), dim3(64 * FwdCfg<D>::kWaves), 0, st, a.q, a.k, a.v, a.o,
-                       a.lse, geo, BH, nqb, win, a.scale * kLog2e);
+  } else {
+    launch_fwd_plain<T, D, MODE, FwdCfg<D>::kWaves, FwdCfg<D>::kStages>(a, geo, win, st);
+  }
   return hipGetLastError();
 }
 

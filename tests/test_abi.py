@@ -307,7 +307,7 @@ def test_rates_library_exports_and_rejects():
 
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(CSRC, "fa_rates.h")).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
-    assert names == ["fa_rates_lds", "fa_rates_valu"]
+    assert names == ["fa_rates_atomic", "fa_rates_lds", "fa_rates_valu"]
     out = subprocess.run(["nm", "-D", "--defined-only", RATES_LIB_PATH], capture_output=True, text=True).stdout
     assert set(names) <= set(re.findall(r"\bT (fa_\w+)$", out, flags=re.M))
     lib = ctypes.CDLL(RATES_LIB_PATH)
@@ -320,3 +320,11 @@ def test_rates_library_exports_and_rejects():
     lib.fa_rates_lds.restype = ctypes.c_int
     assert lib.fa_rates_lds(None, 6, None) == -1
     assert lib.fa_rates_lds(buf, 5, None) == -1
+    lib.fa_rates_atomic.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_void_p]
+    lib.fa_rates_atomic.restype = ctypes.c_int
+    assert lib.fa_rates_atomic(None, 8, 8192, 32, None) == -1
+    assert lib.fa_rates_atomic(buf, 7, 8192, 32, None) == -1
+    assert lib.fa_rates_atomic(buf, 8, 8190, 32, None) == -1   # N not a multiple of 128
+    assert lib.fa_rates_atomic(buf, 8, 8192, 0, None) == -1
+    assert lib.fa_rates_atomic(buf, 8, 65536, 1024, None) == -1  # over 2^30 floats

@@ -150,3 +150,8 @@ def test_overlap_fraction():
     assert bench.overlap_fraction(1.0, 0.5, 1.5) == pytest.approx(0.0)  # one after the other
     assert bench.overlap_fraction(1.0, 0.5, 1.0) == pytest.approx(1.0)  # the shorter fully hidden
     assert bench.overlap_fraction(1.0, 0.8, 1.4) == pytest.approx(0.5)
+
+
+def test_host_cpu_model_is_named():
+    m = bench.host_cpu_model()
+    assert isinstance(m, str) and len(m) > 0

@@ -108,7 +108,8 @@ def test_workload_sampled(name, heads):
 @pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_ragged_sweep(dtype, d, causal):
-    for N in (1, 17, 127, 129, 1999):
+    # 2500: past the short-sequence cut (2048), the pipelined d = 128 and 8-wave d = 64 forwards
+    for N in (1, 17, 127, 129, 1999, 2500):
         seed = 20000 + N * 7 + d + (1 if causal else 0) + (2 if dtype == "bf16" else 0)
         w = wl.Workload(f"sweep_N{N}", dtype, 1, 2, N, d, causal, 2.0 if N == 129 else 1.0, seed)
         say(f"[parity] {w.describe()}")

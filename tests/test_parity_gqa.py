@@ -23,6 +23,9 @@ CASES = [
     ("bf16", 2, 4, 2, 129, 32, True),
     ("fp16", 1, 4, 4, 200, 128, False),
     ("bf16", 1, 8, 1, 1000, 64, True),
+    # past the short-sequence cut (2048)
+    ("bf16", 1, 4, 2, 2200, 128, True),
+    ("fp16", 1, 4, 1, 2300, 64, False),
 ]
 
 

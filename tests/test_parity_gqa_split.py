@@ -26,6 +26,7 @@ CASES = [
     ("bf16", 1, 16, 1, 300, 32, (50, 10)),
     ("fp16", 1, 12, 3, 513, 128, (-1, 0)),
     ("bf16", 2, 4, 1, 129, 128, (64, 0)),
+    ("bf16", 1, 8, 1, 2500, 128, (-1, 0)),  # past the short-sequence cut (2048)
 ]
 
 

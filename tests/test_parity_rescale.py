@@ -10,10 +10,12 @@ built to climb: make_rising_inputs adds a staircase to the scores along the
 key axis (steps of 12 base-2 units at key blocks 1, 2, the middle one and
 the last one).  The host checks on the very inputs the GPU gets that the
 move rule fires after the first tile in every row that sees a whole step
-block, and several times in rows that see every step; then the HIP path is
+block, at least twice in rows that see every step (three times or more in
+nine rows out of ten); then the HIP path is
 compared with the oracle element by element at the parity tolerances, for
-the pipelined forward (d = 128) and the plain one (d = 64, 32), fp16 and
-bf16, causal and full.
+every forward form (the short-sequence 4-wave kernel at N = 1500; at
+N = 2500 the pipelined kernel at d = 128 and the 8-wave plain one at d = 64),
+fp16 and bf16, causal and full.
 """
 
 import math
@@ -26,16 +28,21 @@ import oracle
 from exact_io_aware_30_amd import workloads as wl
 from parity_utils import assert_fwd, assert_grad, check_finite, run_gpu, say
 
-N_RISE = 1500   # 24 key tiles of 64: the reference moves at tiles 1, 2, 12, 23
+# 1500: 24 key tiles of 64, the reference moves at tiles 1, 2, 12, 23 (the
+# short-sequence forward); 2500: 40 tiles, moves at 1, 2, 20, 39 (the long
+# forwards: at d = 128 the pipelined kernel, whose four unrolled steps each
+# see a move).
+N_RISE = (1500, 2500)
 TILE = 64       # the forward's key tile at every head dimension
 SLACK = 8.0     # base-2 units a tile's row maximum must exceed the reference by
 
-CASES = [(dt, d, causal) for dt in ("fp16", "bf16") for d in (32, 64, 128) for causal in (False, True)]
+CASES = [(n, dt, d, causal) for n in N_RISE for dt in ("fp16", "bf16") for d in (32, 64, 128)
+         for causal in (False, True)]
 
 
-def _workload(dt, d, causal):
-    return wl.Workload(f"rising_{dt}_d{d}_{'causal' if causal else 'full'}", dt, 1, 2, N_RISE, d, causal, 1.0,
-                       7100 + d + (1 if causal else 0) + (2 if dt == "bf16" else 0))
+def _workload(n, dt, d, causal):
+    return wl.Workload(f"rising_{dt}_d{d}_{'causal' if causal else 'full'}_N{n}", dt, 1, 2, n, d, causal, 1.0,
+                       7100 + n + d + (1 if causal else 0) + (2 if dt == "bf16" else 0))
 
 
 def move_counts(qh, kh, scale, causal):
@@ -61,7 +68,8 @@ def move_counts(qh, kh, scale, causal):
 def check_rising(q, k, w):
     """Assert the move rule fires as designed on every head of (q, k)."""
     steps = wl.rise_steps(w.N)
-    assert steps == [1, 2, 12, 23], steps
+    nt = (w.N + TILE - 1) // TILE
+    assert steps == [1, 2, nt // 2, nt - 1], steps
     rows = np.arange(w.N)
     # rows that see all of key block 1, and rows that see all of every step
     # block (the last block is the ragged tail: rows that see its first key)
@@ -73,22 +81,23 @@ def check_rising(q, k, w):
             moves, rise = move_counts(qh, kh, w.scale, w.causal)
             assert np.all(moves[see_one] >= 1), f"head {b},{h}: a row never moves after its first tile"
             assert np.all(rise[see_one] > SLACK)
-            assert np.all(moves[see_all] >= 3), f"head {b},{h}: a row moves fewer than 3 times"
+            assert np.all(moves[see_all] >= 2), f"head {b},{h}: a row moves fewer than 2 times"
+            assert np.mean(moves[see_all] >= 3) >= 0.9, f"head {b},{h}: under 90% of rows move 3 times"
             assert see_all.sum() > 0 and see_one.sum() > w.N // 2
 
 
-@pytest.mark.parametrize("dt,d,causal", CASES)
-def test_rising_inputs_move_the_reference(dt, d, causal):
+@pytest.mark.parametrize("n,dt,d,causal", CASES)
+def test_rising_inputs_move_the_reference(n, dt, d, causal):
     """Host logic: the planted inputs fire the move rule (no GPU)."""
-    w = _workload(dt, d, causal)
+    w = _workload(n, dt, d, causal)
     q, k, _, _ = wl.make_rising_inputs(w)
     check_rising(q, k, w)
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("dt,d,causal", CASES)
-def test_parity_running_max_moves(dt, d, causal):
-    w = _workload(dt, d, causal)
+@pytest.mark.parametrize("n,dt,d,causal", CASES)
+def test_parity_running_max_moves(n, dt, d, causal):
+    w = _workload(n, dt, d, causal)
     say(f"[parity] {w.describe()} rising scores (reference moves after tile 0)")
     q, k, v, do = wl.make_rising_inputs(w)
     check_rising(q, k, w)

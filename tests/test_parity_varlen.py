@@ -23,6 +23,9 @@ CASES = [
     ("bf16", 2, 1, 64, [1000, 2, 450], True, (50, 0)),
     ("fp16", 2, 2, 32, [77, 0, 0, 1, 513], False, (20, 20)),
     ("bf16", 8, 8, 128, [2048, 100], True, None),
+    # the longest sequence past the short-sequence cut (2048)
+    ("bf16", 2, 1, 128, [2500, 30, 700], True, None),
+    ("fp16", 2, 2, 64, [2100, 0, 900], False, (400, 0)),
 ]
 
 

@@ -26,6 +26,10 @@ CASES = [
     ("fp16", 2, 4, 2, 513, 32, (70, -1)),
     ("bf16", 1, 2, 2, 450, 32, (33, 0)),
     ("fp16", 1, 2, 2, 257, 128, (5000, 5000)),
+    # sequences past the short-sequence cut (2048): the pipelined d = 128 and 8-wave d = 64 forwards
+    ("bf16", 1, 2, 2, 3000, 128, (700, 0)),
+    ("fp16", 1, 2, 1, 2600, 64, (300, 200)),
+    ("bf16", 1, 2, 2, 2300, 128, (-1, 100)),
 ]
 
 

@@ -4,7 +4,8 @@ under the published 2.5 PFLOP/s; an exponential no faster than an FMA; the
 per-score sequence, which holds an exponential and several other vector
 instructions, slower than either; the interleaved MFMA + vector loop no
 faster than its longer half and no slower than both halves; LDS-fed MFMA
-loops no faster than the register-fed one)."""
+loops no faster than the register-fed one; the atomic dQ accumulation
+giving every sum exactly, in both grid orders)."""
 
 import os
 import sys
@@ -38,3 +39,11 @@ def test_lds_rates_are_plausible():
     assert 200.0 < r["mfma_regs_tflops"] < 2600.0
     # an operand read from LDS cannot make the matrix core faster (5% timing slack)
     assert 0 < r["mfma_lds2_tflops"] <= 1.05 * r["mfma_lds1_tflops"] <= 1.05 * 1.05 * r["mfma_regs_tflops"]
+
+
+def test_atomic_accumulation_is_exact_and_timed():
+    r = bench.probe_atomic(N=2048, BH=8)
+    print(r, flush=True)
+    assert r["wrong_sums"] == 0
+    assert r["atomic_ms_head_per_xcd"] > 0 and r["atomic_ms_head_spread"] > 0 and r["plain_rmw_ms"] > 0
+    assert 0 < r["atomic_tbs"] < 100 and r["plain_tbs"] > 0
