@@ -106,6 +106,18 @@ def traffic_from_summary(kernel: str):
     return float(m.group(1)) if m else None
 
 
+def host_cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, heads: int = 24):
     """The oracle, as it stands, on the first `heads` of the B*H heads."""
     import numpy as np
@@ -129,7 +141,7 @@ def cpu_baseline(w, heads: int = 24):
     return {"value": fb / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"the first {heads} of {w.B * w.H} heads of {w.describe()}: fwd+bwd, {dt:.1f} s wall, "
                       f"numpy fp64",
-            "seconds": round(dt, 3)}
+            "seconds": round(dt, 3), "cpu_model": host_cpu_model()}
 
 
 def _inputs(w, dev):
@@ -271,6 +283,26 @@ def probe_lds():
             "mfma_regs_tflops": out[3], "compute_units": int(out[4]), "lds_read_ms": out[5]}
 
 
+def probe_atomic(N: int = 8192, BH: int = 32):
+    """The atomic-dQ accumulation measured alone by libfa_rates.so (float32
+    atomic adds of 32 x 128 tiles, one workgroup per 128-key block and head,
+    causal, d = 128), beside the same traffic as plain read-add-write."""
+    import ctypes
+
+    import torch
+
+    lib = ctypes.CDLL(RATES_LIBRARY)
+    lib.fa_rates_atomic.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_void_p]
+    lib.fa_rates_atomic.restype = ctypes.c_int
+    out = (ctypes.c_double * 8)()
+    rc = lib.fa_rates_atomic(out, 8, N, BH, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    if rc != 0:
+        raise RuntimeError(f"fa_rates_atomic failed (status {rc})")
+    return {"N": N, "BH": BH, "bytes": out[0], "atomic_ms_head_per_xcd": out[1], "atomic_ms_head_spread": out[2],
+            "plain_rmw_ms": out[3], "atomic_tbs": out[4], "wrong_sums": int(out[5] + out[6]), "plain_tbs": out[7]}
+
+
 def overlap_fraction(t_mfma: float, t_valu: float, t_both: float) -> float:
     """Share of the shorter half's time hidden under the longer one when both
     run interleaved: 0 = executed one after the other, 1 = fully hidden."""
@@ -312,8 +344,15 @@ def ceilings(rows=()):
     print(f"LDS: ds_read_b128 alone {lds['lds_read_tbs']:.1f} TB/s over {lds['compute_units']} CUs; dense bf16 MFMA "
           f"{lds['mfma_regs_tflops']:.0f} TFLOP/s with operands in registers, {lds['mfma_lds1_tflops']:.0f} with one "
           f"1 KiB LDS operand per MFMA, {lds['mfma_lds2_tflops']:.0f} with two")
+    at = probe_atomic()
+    print(f"atomic dQ accumulation alone (bf16 [{at['BH']} heads, N={at['N']}, d=128] causal, 128-key blocks): "
+          f"{at['bytes'] / 1e9:.2f} GB of float32 atomic adds in {at['atomic_ms_head_per_xcd']:.3f} ms "
+          f"({at['atomic_tbs']:.2f} TB/s; {at['atomic_ms_head_spread']:.3f} ms with a head's blocks spread over "
+          f"the XCDs; {at['wrong_sums']} wrong sums), against {at['plain_rmw_ms']:.3f} ms for the same traffic "
+          f"as plain read-add-write")
     emit({"probe_rates": {k: (round(v, 3) if isinstance(v, float) else v) for k, v in rates.items()},
           "probe_lds": {k: (round(v, 3) if isinstance(v, float) else v) for k, v in lds.items()},
+          "probe_atomic": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in at.items()},
           "forward_ceilings": out})
 
 

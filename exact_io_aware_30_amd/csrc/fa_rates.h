@@ -58,6 +58,29 @@ int fa_rates_valu(double* out, int n, void* stream);
  */
 int fa_rates_lds(double* out, int n, void* stream);
 
+/*
+ * fa_rates_atomic -- the cost of accumulating dQ with atomics inside the
+ * dK/dV kernel, the alternative to a separate dQ kernel that recomputes S
+ * and dP (the pages leave open how dQ is accumulated: "flash-attn-triton"
+ * docs, "Where things live").  Runs the accumulation alone, in the pattern
+ * that form would issue for BH heads of N rows at d = 128 under the causal
+ * mask: one workgroup per (128-key block, head) adds a 32 x 128 float32 tile
+ * for every 32-row query tile its block sees, with hardware float32 atomic
+ * adds; then checks every sum (each row counted once per block that sees
+ * it).  Best of three, timed with HIP events on `stream` (synchronised):
+ *   out[0]  bytes of float32 added
+ *   out[1]  ms, head index fastest in the grid (a head's blocks on one XCD)
+ *   out[2]  ms, key block fastest (a head's blocks spread over every XCD)
+ *   out[3]  ms of the same traffic as plain read-add-write (not atomic)
+ *   out[4]  TB/s of atomic adds in the first ordering
+ *   out[5], out[6]  wrong sums in the two orderings (0 expected)
+ *   out[7]  TB/s of the plain reference
+ * Needs N a multiple of 128, BH * N * 128 <= 2^30, n >= 8; allocates and
+ * frees a BH * N * 128 float buffer and a host copy.  Returns 0, -1 for a
+ * bad argument, -4 for a HIP or host allocation error.
+ */
+int fa_rates_atomic(double* out, int n, int N, int BH, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

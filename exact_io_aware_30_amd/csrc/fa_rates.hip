@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdlib>
 
 namespace {
 
@@ -237,7 +238,116 @@ hipError_t time_lds(float* out, int grid, int iters, hipStream_t st, float* best
   return err;
 }
 
+// ---------------------------------------------------------------------------
+// fp32 atomic adds in the pattern a backward that accumulated dQ with
+// atomics inside the dK/dV kernel would issue: one workgroup of 256 lanes
+// per (128-key block, head), walking the 32-row query tiles its block sees
+// under the causal mask and adding a 32 x 128 float32 tile (16 values per
+// lane) into acc[head][row][128] for each.  ORDER 0: head index fastest in
+// the grid (a head's blocks share an XCD under round-robin dispatch); 1: key
+// block fastest (a head's blocks spread over every XCD); 2: the same
+// traffic as plain load-add-store (wrong sums: the memory-only reference).
+// ---------------------------------------------------------------------------
+template <int ORDER>
+__global__ __launch_bounds__(256) void atomic_tile_kernel(float* acc, int N, int BH, int nkb) {
+  const int x = blockIdx.x;
+  const int kb = ORDER == 1 ? x % nkb : x / BH, bh = ORDER == 1 ? x / nkb : x % BH;
+  float* head = acc + (size_t)bh * N * 128;
+  const int nt = N / 32, tid = threadIdx.x;
+  for (int t = kb * 4; t < nt; ++t) {
+    float* tile = head + (size_t)t * 32 * 128;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float* p = tile + i * 256 + tid;
+      if constexpr (ORDER <= 1)
+        unsafeAtomicAdd(p, 1.0f);
+      else
+        *p += 1.0f;
+    }
+  }
+}
+
+template <int ORDER>
+hipError_t time_atomic(float* acc, int N, int BH, hipStream_t st, float* best_ms) {
+  hipEvent_t e0, e1;
+  hipError_t err = hipEventCreate(&e0);
+  if (err != hipSuccess) return err;
+  if ((err = hipEventCreate(&e1)) != hipSuccess) {
+    (void)hipEventDestroy(e0);
+    return err;
+  }
+  const int nkb = N / 128;
+  float best = 1e30f;
+  for (int rep = 0; rep < 3 && err == hipSuccess; ++rep) {
+    err = hipMemsetAsync(acc, 0, (size_t)BH * N * 128 * sizeof(float), st);
+    if (err == hipSuccess) err = hipEventRecord(e0, st);
+    if (err == hipSuccess) {
+      hipLaunchKernelGGL((atomic_tile_kernel<ORDER>), dim3(nkb * BH), dim3(256), 0, st, acc, N, BH, nkb);
+      err = hipGetLastError();
+    }
+    if (err == hipSuccess) err = hipEventRecord(e1, st);
+    if (err == hipSuccess) err = hipEventSynchronize(e1);
+    float ms = 0.f;
+    if (err == hipSuccess) err = hipEventElapsedTime(&ms, e0, e1);
+    if (err == hipSuccess) best = std::min(best, ms);
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  *best_ms = best;
+  return err;
+}
+
+// Rows whose count differs from the number of key blocks that see them
+// (row r is seen by blocks 0 .. r / 128).
+long count_wrong(const float* h, int N, int BH) {
+  long bad = 0;
+  for (long i = 0; i < (long)BH * N * 128; ++i) {
+    const long row = (i / 128) % N;
+    if (h[i] != (float)(row / 128 + 1)) ++bad;
+  }
+  return bad;
+}
+
 }  // namespace
+
+extern "C" int fa_rates_atomic(double* out, int n, int N, int BH, void* stream) {
+  if (!out || n < 8 || N < 128 || N % 128 != 0 || BH < 1 || (long)BH * N * 128 > (1L << 30)) return -1;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const size_t count = (size_t)BH * N * 128;
+  float* acc = nullptr;
+  if (hipMalloc(&acc, count * sizeof(float)) != hipSuccess) return -4;
+  float* host = static_cast<float*>(malloc(count * sizeof(float)));
+  if (!host) {
+    (void)hipFree(acc);
+    return -4;
+  }
+  float ms[3] = {0, 0, 0};
+  long bad[2] = {0, 0};
+  hipError_t err = time_atomic<0>(acc, N, BH, st, &ms[0]);
+  if (err == hipSuccess) err = hipMemcpyAsync(host, acc, count * sizeof(float), hipMemcpyDeviceToHost, st);
+  if (err == hipSuccess) err = hipStreamSynchronize(st);
+  if (err == hipSuccess) bad[0] = count_wrong(host, N, BH);
+  if (err == hipSuccess) err = time_atomic<1>(acc, N, BH, st, &ms[1]);
+  if (err == hipSuccess) err = hipMemcpyAsync(host, acc, count * sizeof(float), hipMemcpyDeviceToHost, st);
+  if (err == hipSuccess) err = hipStreamSynchronize(st);
+  if (err == hipSuccess) bad[1] = count_wrong(host, N, BH);
+  if (err == hipSuccess) err = time_atomic<2>(acc, N, BH, st, &ms[2]);
+  free(host);
+  (void)hipFree(acc);
+  if (err != hipSuccess) return -4;
+  double tiles = 0;
+  for (int kb = 0; kb < N / 128; ++kb) tiles += N / 32 - 4 * kb;
+  const double bytes = tiles * BH * 4096.0 * 4.0;
+  out[0] = bytes;            // bytes of float32 added
+  out[1] = ms[0];            // atomics, a head's blocks on one XCD, ms
+  out[2] = ms[1];            // atomics, a head's blocks over every XCD, ms
+  out[3] = ms[2];            // the same traffic as plain read-add-write, ms
+  out[4] = bytes / (ms[0] * 1e-3) / 1e12;  // TB/s of atomic adds (first ordering)
+  out[5] = (double)bad[0];   // wrong sums, first ordering
+  out[6] = (double)bad[1];   // wrong sums, second ordering
+  out[7] = bytes / (ms[2] * 1e-3) / 1e12;  // TB/s of the plain reference
+  return 0;
+}
 
 extern "C" int fa_rates_lds(double* out, int n, void* stream) {
   if (!out || n < 6) return -1;
