@@ -975,11 +975,12 @@ static int resident_workgroups(const void* kernel, std::atomic<int>* cache) {
   int v = cache[dev].load(std::memory_order_relaxed);
   if (v == 0) {
     int cus = 0, per_cu = 0;
-    v = (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) == hipSuccess && cus > 0 &&
-         per_cu > 0)
-            ? cus * per_cu
-            : -1;  // 0 is "not looked up yet"
+    const bool ok = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+                    hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) == hipSuccess;
+    // A failed query must not surface as the launch's error (the caller
+    // reads hipGetLastError after the launch): clear it and walk down.
+    if (!ok) (void)hipGetLastError();
+    v = ok && cus > 0 && per_cu > 0 ? cus * per_cu : -1;  // 0 is "not looked up yet"
     cache[dev].store(v, std::memory_order_relaxed);
   }
   return v > 0 ? v : 0;
