@@ -66,6 +66,13 @@ struct FwdCfg {
 // [4,16,2048]; at N = 4096 (d = 128) and 65536 (d = 64) the default shapes
 // are 5% and 3% faster, hence the cut.
 constexpr int kShortSeq = 2048, kShortWaves = 4, kShortStages = 2;
+// Windows bounded on both sides and at most kNarrowWindow keys wide take the
+// same kernel at any N: a block visits the keys of its rows' windows, so
+// 128-row blocks visit fewer masked keys at the window's edges than 256-row
+// ones.  Measured (bf16 [2,16,8192,d], same box, outputs bit-identical):
+// windows (256, 0) 26% faster at d = 128 and 14% at d = 64, (512, 512) 12%,
+// (1024, 0) 14% and 6%, (2047, 0) 9% and 7%, (3071, 0) 4%, (4095, 0) 2-3%.
+constexpr long kNarrowWindow = 4096;
 
 // Rescale threshold in base-2 units: the reference maximum used for the
 // exponentials is moved only when a row's maximum exceeds it by more than
@@ -627,7 +634,8 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   const Geom geo{a.N, a.H, a.H / a.Hkv, a.cu, a.T};
   constexpr bool kShortIsDefault = !kFwdPipelined<D> && FwdCfg<D>::kWaves == kShortWaves &&
                                    FwdCfg<D>::kStages == kShortStages;
-  if (!kShortIsDefault && a.N <= kShortSeq) {
+  const bool narrow = MODE == 2 && a.wl >= 0 && a.wr >= 0 && static_cast<long>(a.wl) + a.wr + 1 <= kNarrowWindow;
+  if (!kShortIsDefault && (a.N <= kShortSeq || narrow)) {
     launch_fwd_plain<T, D, MODE, kShortWaves, kShortStages>(a, geo, win, st);
   } else if constexpr (kFwdPipelined<D>) {
     const int BM = 32 * FwdCfg<D>::kWaves;

@@ -26,10 +26,16 @@ CASES = [
     ("fp16", 2, 4, 2, 513, 32, (70, -1)),
     ("bf16", 1, 2, 2, 450, 32, (33, 0)),
     ("fp16", 1, 2, 2, 257, 128, (5000, 5000)),
-    # sequences past the short-sequence cut (2048): the pipelined d = 128 and 8-wave d = 64 forwards
+    # sequences past the short-sequence cut (2048).  Windows bounded on both
+    # sides and at most 4096 keys wide take the 4-wave forward at any N:
     ("bf16", 1, 2, 2, 3000, 128, (700, 0)),
     ("fp16", 1, 2, 1, 2600, 64, (300, 200)),
+    ("bf16", 1, 2, 2, 5000, 128, (2047, 2048)),
+    ("fp16", 1, 2, 1, 3300, 64, (1500, 0)),
+    # the others take the long-sequence forwards (pipelined at d = 128): a
+    # window unbounded on the left, and one key wider than 4096
     ("bf16", 1, 2, 2, 2300, 128, (-1, 100)),
+    ("fp16", 1, 2, 2, 4500, 128, (2048, 2048)),
 ]
 
 
